@@ -1,0 +1,134 @@
+/*
+ * fa_oracle.h — C-ABI of the fp64 CPU oracle (test infrastructure only).
+ *
+ * The oracle is a plain, slow, obviously-correct host implementation of what the
+ * fused attention forward pass computes.  It exists to check the GPU library
+ * (fa.h) and is built into its own shared library, libfa_oracle.so, from
+ * oracle/fa_oracle.c.  The GPU library never links it, and it shares no code,
+ * header or table with the GPU library: the dtype codes below are restated here
+ * with the same numeric values as fa.h because both describe the same buffers.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg use it.
+ *
+ * Definitions followed (pages as cited in the sources):
+ *   - standard three-step attention: S = scale * Q K^T, P = row-softmax(S), O = P V
+ *     ("05_flash_attention.py" course file, function standard_attention;
+ *      "Flash Attention" blog page, section "Why Flash Attention" and Algorithm 2
+ *      for the scale tau and the mask);
+ *   - causal visibility: key k is visible to query q iff k <= q, indices 0-based,
+ *     aligned at the top-left corner (course file, standard_attention's triu(1) mask);
+ *   - row logsumexp L = m + ln(l), natural log (course file, flash_attention_forward
+ *     and demo_online_softmax);
+ *   - online softmax and the (+) merge on (m, d) and (m, d, o~)
+ *     ("Flash Attention" blog page, sections "Online Softmax" and parallelisation).
+ *
+ * Conventions common to every function:
+ *   - all pointers are HOST pointers; the caller owns every buffer;
+ *   - the functions are synchronous, re-entrant and thread-safe (they keep no
+ *     global state; scratch memory is malloc'd per call and freed before return);
+ *   - return value: 0 on success, FA_ORACLE_EINVAL (1) on an invalid argument,
+ *     FA_ORACLE_ENOMEM (4) if a scratch allocation fails; outputs are then untouched
+ *     or partially written;
+ *   - tensors are contiguous: q and o are [B,H,Nq,d], k and v are [B,H,Nk,d],
+ *     lse is [B,H,Nq], d fastest;
+ *   - arithmetic is IEEE fp64 with plain left-to-right summation.
+ */
+#ifndef FA_ORACLE_H
+#define FA_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element type of q, k, v (and o for fa_fwd_ref); same codes as fa.h */
+enum { FA_ORACLE_F32 = 0, FA_ORACLE_F16 = 1, FA_ORACLE_BF16 = 2 };
+
+enum { FA_ORACLE_OK = 0, FA_ORACLE_EINVAL = 1, FA_ORACLE_ENOMEM = 4 };
+
+/*
+ * One-dimensional online softmax over x[0..n) read in blocks of `block` values
+ * (course file, online_softmax_stats; blog page "Online Softmax").
+ * Per block b (nb = ceil(n/block) blocks), after reading it:
+ *   run_m[b]   running maximum m_b;
+ *   run_l[b]   running sum l_b = sum_{k read so far} exp(x_k - m_b);
+ *   carried[b] the previous sum carried over, l_{b-1} * exp(m_{b-1} - m_b) (0 for b = 0);
+ *   fresh[b]   the new block's own sum relative to the new maximum, sum exp(x_k - m_b).
+ * y[0..n) receives the final softmax exp(x_i - m_last) / l_last (second pass).
+ * Any trace pointer may be NULL.  n >= 1, block >= 1.  -inf entries are allowed as
+ * long as x holds at least one finite value.
+ */
+int fa_oracle_softmax_online(const double* x, int64_t n, int64_t block, double* y,
+                             double* run_m, double* run_l, double* carried, double* fresh);
+
+/*
+ * The (+) merge of two online-softmax states (blog page, the extended operator on
+ * (m, d, o~)).  A state is packed as [m, d, o~_0 .. o~_{dim-1}] (dim+2 doubles).
+ * out may alias a or b.  The empty state (m = -inf, d = 0, o~ = 0) is the identity.
+ */
+int fa_oracle_merge(int64_t dim, const double* a, const double* b, double* out);
+
+/*
+ * Part 1 — standard three-step attention for selected query rows of ONE head,
+ * on fp64 inputs: q [nq,d], k [nk,d], v [nk,d].  For each i < n_rows, row r = rows[i]:
+ * materialise s_k = scale * <q_r, k_k> for every key (-inf when causal and k > r),
+ * safe softmax (max, exp, sum, normalise), then o = sum_k p_k v_k.
+ * Writes o[i*d .. i*d+d) and lse[i] = m + ln(l).
+ */
+int fa_oracle_attention_f64(const double* q, const double* k, const double* v,
+                            int64_t nq, int64_t nk, int64_t d, int causal, double scale,
+                            int64_t n_rows, const int64_t* rows, double* o, double* lse);
+
+/*
+ * Part 2 — scalar online (m, d, o~) accumulator, same contract as part 1.
+ * key_block <= 0: keys are consumed one at a time (blog page recurrence);
+ * key_block  > 0: each contiguous block of key_block keys is first reduced to its own
+ * state by the scalar recurrence, then folded into the running state with the (+) merge.
+ * Masked keys are skipped.  If max_raised is not NULL, max_raised[i] counts how often
+ * the running maximum of row i increased after the first visible key.
+ */
+int fa_oracle_online_f64(const double* q, const double* k, const double* v,
+                         int64_t nq, int64_t nk, int64_t d, int causal, double scale,
+                         int64_t key_block, int64_t n_rows, const int64_t* rows,
+                         double* o, double* lse, int64_t* max_raised);
+
+/*
+ * Part 1 on the raw input buffers the GPU receives: q, k, v hold `dtype` elements
+ * (bf16/fp16 bit patterns or fp32), widened exactly to fp64.  The n_sel selected rows
+ * are (sel_bh[i], sel_row[i]) with sel_bh = b*H + h.  Outputs: o64 [n_sel, d] and
+ * lse64 [n_sel].  `scale` is the fp32 value passed to the GPU, widened exactly.
+ * Rows belonging to the same head should be adjacent (K and V of a head are widened
+ * once per run of equal sel_bh).  Requires B, H, Nq, Nk, d >= 1.
+ */
+int fa_ref_rows_f64(const void* q, const void* k, const void* v,
+                    int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                    int causal, float scale, int dtype,
+                    int64_t n_sel, const int64_t* sel_bh, const int64_t* sel_row,
+                    double* o64, double* lse64);
+
+/* Part 2 on raw input buffers; same contract as fa_ref_rows_f64 plus key_block. */
+int fa_ref_online_f64(const void* q, const void* k, const void* v,
+                      int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                      int causal, float scale, int dtype,
+                      int64_t n_sel, const int64_t* sel_bh, const int64_t* sel_row,
+                      int64_t key_block, double* o64, double* lse64, int64_t* max_raised);
+
+/*
+ * Whole-tensor host counterpart of fa_fwd: every row through part 1, then o is
+ * rounded from fp64 to `dtype` with round-to-nearest-even (directly, no double
+ * rounding) and lse to fp32.  Synchronous; o and lse are host buffers.
+ */
+int fa_fwd_ref(const void* q, const void* k, const void* v, void* o, float* lse,
+               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+               int causal, float scale, int dtype);
+
+/* fp64 -> dtype rounding used by fa_fwd_ref (round to nearest, ties to even),
+ * exposed so that it can be pinned against independent conversions. */
+int fa_oracle_round(const double* x, int64_t n, int dtype, void* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_ORACLE_H */

@@ -1,0 +1,522 @@
+/*
+ * fa_oracle.c — fp64 CPU oracle for the fused attention forward pass.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg may load this code.  The GPU library shares nothing with it.
+ *
+ * It is deliberately plain: loops in the order the definitions are written, fp64,
+ * left-to-right sums, no blocking, no fusion, no reordering.  Build flags keep
+ * IEEE semantics (no fast-math, no FMA contraction).
+ *
+ * What it follows (the pages are named by their titles / addresses):
+ *   [A] "05_flash_attention.py" (CS336 lecture-5 course file, semidirectx.com):
+ *       standard_attention (scale, causal triu mask, softmax, @V),
+ *       flash_attention_forward (returned L = m + log l), online_softmax_stats.
+ *   [B] "Flash Attention" (blog.cyberangel.work): sections "Online Softmax"
+ *       (safe softmax, the online recurrence and its invariant), the parallelisation
+ *       section (the (+) operator on (m, d) and on (m, d, o~)), Algorithm 2 (tau, mask).
+ *   [C] "手写 Flash Attention：从算法原理到高性能实现" (bjdmk.com.cn), section 2.2:
+ *       the worked two-block example that the tests pin.
+ *
+ * Readings where the pages are silent are listed beside the code that takes them.
+ */
+#include "../include/fa_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------- */
+/* exact widening of the stored element types to fp64                        */
+/* ------------------------------------------------------------------------- */
+
+static double widen_bf16(uint16_t bits)
+{
+    /* bf16 is the upper half of an IEEE binary32 */
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double widen_f16(uint16_t bits)
+{
+    /* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits */
+    int sign = bits >> 15;
+    int expo = (bits >> 10) & 0x1f;
+    int frac = bits & 0x3ff;
+    double mag;
+    if (expo == 0)
+        mag = ldexp((double)frac, -24); /* subnormal: frac * 2^-24 */
+    else if (expo == 31)
+        mag = frac ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(frac | 0x400), expo - 25);
+    return sign ? -mag : mag;
+}
+
+static double widen_one(const void* base, int64_t idx, int dtype)
+{
+    if (dtype == FA_ORACLE_F32) {
+        float f;
+        memcpy(&f, (const char*)base + 4 * idx, 4);
+        return (double)f;
+    }
+    uint16_t h;
+    memcpy(&h, (const char*)base + 2 * idx, 2);
+    return dtype == FA_ORACLE_BF16 ? widen_bf16(h) : widen_f16(h);
+}
+
+static void widen_span(const void* base, int64_t first, int64_t count, int dtype, double* out)
+{
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = widen_one(base, first + i, dtype);
+}
+
+/* ------------------------------------------------------------------------- */
+/* one-dimensional online softmax with per-block trace  [B] "Online Softmax",  */
+/* [A] online_softmax_stats                                                  */
+/* ------------------------------------------------------------------------- */
+
+int fa_oracle_softmax_online(const double* x, int64_t n, int64_t block, double* y,
+                             double* run_m, double* run_l, double* carried, double* fresh)
+{
+    if (!x || n < 1 || block < 1)
+        return FA_ORACLE_EINVAL;
+
+    double m = -INFINITY; /* running maximum, starts at -inf */
+    double l = 0.0;       /* running sum relative to m, starts at 0 */
+    int64_t b = 0;
+    for (int64_t start = 0; start < n; start += block, ++b) {
+        int64_t end = start + block < n ? start + block : n;
+
+        /* new maximum over the old one and the block */
+        double m_new = m;
+        for (int64_t i = start; i < end; ++i)
+            if (x[i] > m_new)
+                m_new = x[i];
+
+        /* rebase the old sum to the new maximum; while nothing finite has been
+         * read yet (m = m_new = -inf) there is nothing to carry */
+        double carry = (l == 0.0) ? 0.0 : l * exp(m - m_new);
+
+        /* the block's own contribution relative to the new maximum */
+        double add = 0.0;
+        if (m_new != -INFINITY)
+            for (int64_t i = start; i < end; ++i)
+                add += exp(x[i] - m_new);
+
+        l = carry + add;
+        m = m_new;
+        if (run_m) run_m[b] = m;
+        if (run_l) run_l[b] = l;
+        if (carried) carried[b] = carry;
+        if (fresh) fresh[b] = add;
+    }
+    if (m == -INFINITY)
+        return FA_ORACLE_EINVAL; /* no finite value: softmax undefined */
+
+    /* second pass: normalise with the final statistics */
+    if (y)
+        for (int64_t i = 0; i < n; ++i)
+            y[i] = exp(x[i] - m) / l;
+    return FA_ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* the (+) merge on (m, d, o~)  [B] parallelisation section                  */
+/* ------------------------------------------------------------------------- */
+
+int fa_oracle_merge(int64_t dim, const double* a, const double* b, double* out)
+{
+    if (!a || !b || !out || dim < 0)
+        return FA_ORACLE_EINVAL;
+    double ma = a[0], mb = b[0];
+    /* The empty state (-inf, 0, 0) is the identity.  The pages leave
+     * (-inf) - (-inf) undefined; returning the other operand is the reading that
+     * makes the -inf initial state degenerate to plain softmax, as [A] and [C] say. */
+    if (ma == -INFINITY || mb == -INFINITY) {
+        const double* keep = (ma == -INFINITY) ? b : a;
+        if (keep != out)
+            memmove(out, keep, (size_t)(dim + 2) * sizeof(double));
+        return FA_ORACLE_OK;
+    }
+    double m = ma > mb ? ma : mb;
+    double ca = exp(ma - m);
+    double cb = exp(mb - m);
+    double d = a[1] * ca + b[1] * cb;
+    for (int64_t t = 0; t < dim; ++t)
+        out[2 + t] = a[2 + t] * ca + b[2 + t] * cb;
+    out[0] = m;
+    out[1] = d;
+    return FA_ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Part 1: standard three-step attention, one row  [A] standard_attention     */
+/* ------------------------------------------------------------------------- */
+
+/* score of query row r against key kk: scale * sum_t q[t] k[t], or -inf if masked */
+static double score(const double* q_row, const double* k_row, int64_t d, double scale,
+                    int causal, int64_t r, int64_t kk)
+{
+    if (causal && kk > r)
+        return -INFINITY;
+    double dot = 0.0;
+    for (int64_t t = 0; t < d; ++t)
+        dot += q_row[t] * k_row[t];
+    return scale * dot;
+}
+
+/* s is caller scratch of nk doubles */
+static void three_step_row(const double* q_row, const double* k, const double* v, int64_t nk,
+                           int64_t d, int causal, double scale, int64_t r, double* s,
+                           double* o_row, double* lse)
+{
+    /* step 1: materialise the score row S[r, :] */
+    for (int64_t kk = 0; kk < nk; ++kk)
+        s[kk] = score(q_row, k + kk * d, d, scale, causal, r, kk);
+
+    /* step 2: safe softmax — maximum, shifted exponentials, sum, normalise */
+    double m = -INFINITY;
+    for (int64_t kk = 0; kk < nk; ++kk)
+        if (s[kk] > m)
+            m = s[kk];
+    double l = 0.0;
+    for (int64_t kk = 0; kk < nk; ++kk) {
+        s[kk] = exp(s[kk] - m); /* masked keys: exp(-inf) = 0 */
+        l += s[kk];
+    }
+    for (int64_t kk = 0; kk < nk; ++kk)
+        s[kk] = s[kk] / l; /* P[r, :] */
+
+    /* step 3: O[r, :] = P[r, :] V */
+    for (int64_t t = 0; t < d; ++t)
+        o_row[t] = 0.0;
+    for (int64_t kk = 0; kk < nk; ++kk)
+        for (int64_t t = 0; t < d; ++t)
+            o_row[t] += s[kk] * v[kk * d + t];
+
+    /* logsumexp of the scaled, masked scores */
+    *lse = m + log(l);
+}
+
+int fa_oracle_attention_f64(const double* q, const double* k, const double* v,
+                            int64_t nq, int64_t nk, int64_t d, int causal, double scale,
+                            int64_t n_rows, const int64_t* rows, double* o, double* lse)
+{
+    if (!q || !k || !v || !o || !lse || nq < 1 || nk < 1 || d < 1 || n_rows < 0 ||
+        (n_rows > 0 && !rows))
+        return FA_ORACLE_EINVAL;
+    for (int64_t i = 0; i < n_rows; ++i)
+        if (rows[i] < 0 || rows[i] >= nq)
+            return FA_ORACLE_EINVAL;
+    double* s = (double*)malloc((size_t)nk * sizeof(double));
+    if (!s)
+        return FA_ORACLE_ENOMEM;
+    for (int64_t i = 0; i < n_rows; ++i)
+        three_step_row(q + rows[i] * d, k, v, nk, d, causal, scale, rows[i], s, o + i * d,
+                       lse + i);
+    free(s);
+    return FA_ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Part 2: scalar online (m, d, o~) accumulator  [B] "Online Softmax" and the  */
+/* o~ extension; [A] flash_attention_forward for the returned L               */
+/* ------------------------------------------------------------------------- */
+
+/* State layout [m, d, o~_0..o~_{dim-1}], as for fa_oracle_merge. */
+
+/* fold one visible key with score x and value row vrow into the state */
+static void online_step(double* st, int64_t dim, double x, const double* vrow, int64_t* raised,
+                        int first)
+{
+    double m_old = st[0];
+    double m_new = x > m_old ? x : m_old;
+    if (!first && m_new > m_old && raised)
+        ++*raised;
+    double c = first ? 0.0 : exp(m_old - m_new); /* rescale factor of the old state */
+    double e = exp(x - m_new);                     /* weight of the new key */
+    st[1] = st[1] * c + e;
+    for (int64_t t = 0; t < dim; ++t)
+        st[2 + t] = st[2 + t] * c + e * vrow[t];
+    st[0] = m_new;
+}
+
+static void online_row(const double* q_row, const double* k, const double* v, int64_t nk,
+                       int64_t d, int causal, double scale, int64_t r, int64_t key_block,
+                       double* run, double* blk, double* o_row, double* lse, int64_t* raised)
+{
+    run[0] = -INFINITY;
+    run[1] = 0.0;
+    for (int64_t t = 0; t < d; ++t)
+        run[2 + t] = 0.0;
+    int64_t nraised = 0;
+    int seen = 0; /* has the running state absorbed a visible key yet? */
+
+    if (key_block <= 0) {
+        for (int64_t kk = 0; kk < nk; ++kk) {
+            double x = score(q_row, k + kk * d, d, scale, causal, r, kk);
+            if (x == -INFINITY)
+                continue; /* masked key: skipped */
+            online_step(run, d, x, v + kk * d, &nraised, !seen);
+            seen = 1;
+        }
+    } else {
+        for (int64_t k0 = 0; k0 < nk; k0 += key_block) {
+            int64_t k1 = k0 + key_block < nk ? k0 + key_block : nk;
+            /* reduce the block to its own state, starting from the empty state */
+            blk[0] = -INFINITY;
+            blk[1] = 0.0;
+            for (int64_t t = 0; t < d; ++t)
+                blk[2 + t] = 0.0;
+            int blk_seen = 0;
+            for (int64_t kk = k0; kk < k1; ++kk) {
+                double x = score(q_row, k + kk * d, d, scale, causal, r, kk);
+                if (x == -INFINITY)
+                    continue;
+                online_step(blk, d, x, v + kk * d, NULL, !blk_seen);
+                blk_seen = 1;
+            }
+            if (!blk_seen)
+                continue; /* a fully masked block contributes the identity */
+            if (seen && blk[0] > run[0])
+                ++nraised;
+            fa_oracle_merge(d, run, blk, run);
+            seen = 1;
+        }
+    }
+    /* final normalisation and logsumexp */
+    for (int64_t t = 0; t < d; ++t)
+        o_row[t] = run[2 + t] / run[1];
+    *lse = run[0] + log(run[1]);
+    if (raised)
+        *raised = nraised;
+}
+
+int fa_oracle_online_f64(const double* q, const double* k, const double* v,
+                         int64_t nq, int64_t nk, int64_t d, int causal, double scale,
+                         int64_t key_block, int64_t n_rows, const int64_t* rows,
+                         double* o, double* lse, int64_t* max_raised)
+{
+    if (!q || !k || !v || !o || !lse || nq < 1 || nk < 1 || d < 1 || n_rows < 0 ||
+        (n_rows > 0 && !rows))
+        return FA_ORACLE_EINVAL;
+    for (int64_t i = 0; i < n_rows; ++i)
+        if (rows[i] < 0 || rows[i] >= nq)
+            return FA_ORACLE_EINVAL;
+    double* run = (double*)malloc((size_t)(2 * (d + 2)) * sizeof(double));
+    if (!run)
+        return FA_ORACLE_ENOMEM;
+    double* blk = run + (d + 2);
+    for (int64_t i = 0; i < n_rows; ++i)
+        online_row(q + rows[i] * d, k, v, nk, d, causal, scale, rows[i], key_block, run, blk,
+                   o + i * d, lse + i, max_raised ? max_raised + i : NULL);
+    free(run);
+    return FA_ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* raw-buffer entry points                                                   */
+/* ------------------------------------------------------------------------- */
+
+static int check_raw(const void* q, const void* k, const void* v, int64_t B, int64_t H,
+                     int64_t Nq, int64_t Nk, int64_t d, int dtype)
+{
+    if (!q || !k || !v)
+        return FA_ORACLE_EINVAL;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1)
+        return FA_ORACLE_EINVAL;
+    if (dtype != FA_ORACLE_F32 && dtype != FA_ORACLE_F16 && dtype != FA_ORACLE_BF16)
+        return FA_ORACLE_EINVAL;
+    return FA_ORACLE_OK;
+}
+
+/* shared driver of fa_ref_rows_f64 / fa_ref_online_f64: widens K and V once per run
+ * of equal sel_bh, widens each selected query row, then runs part 1 or part 2 on it */
+static int ref_rows(const void* q, const void* k, const void* v, int64_t B, int64_t H,
+                    int64_t Nq, int64_t Nk, int64_t d, int causal, float scale, int dtype,
+                    int64_t n_sel, const int64_t* sel_bh, const int64_t* sel_row,
+                    int use_online, int64_t key_block, double* o64, double* lse64,
+                    int64_t* max_raised)
+{
+    int rc = check_raw(q, k, v, B, H, Nq, Nk, d, dtype);
+    if (rc)
+        return rc;
+    if (n_sel < 0 || (n_sel > 0 && (!sel_bh || !sel_row || !o64 || !lse64)))
+        return FA_ORACLE_EINVAL;
+    for (int64_t i = 0; i < n_sel; ++i)
+        if (sel_bh[i] < 0 || sel_bh[i] >= B * H || sel_row[i] < 0 || sel_row[i] >= Nq)
+            return FA_ORACLE_EINVAL;
+
+    double* kh = (double*)malloc((size_t)(Nk * d) * sizeof(double));
+    double* vh = (double*)malloc((size_t)(Nk * d) * sizeof(double));
+    double* qr = (double*)malloc((size_t)d * sizeof(double));
+    double* s = (double*)malloc((size_t)Nk * sizeof(double));
+    double* st = (double*)malloc((size_t)(2 * (d + 2)) * sizeof(double));
+    if (!kh || !vh || !qr || !s || !st) {
+        free(kh);
+        free(vh);
+        free(qr);
+        free(s);
+        free(st);
+        return FA_ORACLE_ENOMEM;
+    }
+    const double sc = (double)scale; /* the fp32 argument, widened exactly */
+    int64_t cur = -1;
+    for (int64_t i = 0; i < n_sel; ++i) {
+        int64_t bh = sel_bh[i], r = sel_row[i];
+        if (bh != cur) {
+            widen_span(k, bh * Nk * d, Nk * d, dtype, kh);
+            widen_span(v, bh * Nk * d, Nk * d, dtype, vh);
+            cur = bh;
+        }
+        widen_span(q, (bh * Nq + r) * d, d, dtype, qr);
+        if (use_online)
+            online_row(qr, kh, vh, Nk, d, causal, sc, r, key_block, st, st + (d + 2),
+                       o64 + i * d, lse64 + i, max_raised ? max_raised + i : NULL);
+        else
+            three_step_row(qr, kh, vh, Nk, d, causal, sc, r, s, o64 + i * d, lse64 + i);
+    }
+    free(kh);
+    free(vh);
+    free(qr);
+    free(s);
+    free(st);
+    return FA_ORACLE_OK;
+}
+
+int fa_ref_rows_f64(const void* q, const void* k, const void* v, int64_t B, int64_t H,
+                    int64_t Nq, int64_t Nk, int64_t d, int causal, float scale, int dtype,
+                    int64_t n_sel, const int64_t* sel_bh, const int64_t* sel_row, double* o64,
+                    double* lse64)
+{
+    return ref_rows(q, k, v, B, H, Nq, Nk, d, causal, scale, dtype, n_sel, sel_bh, sel_row, 0, 0,
+                    o64, lse64, NULL);
+}
+
+int fa_ref_online_f64(const void* q, const void* k, const void* v, int64_t B, int64_t H,
+                      int64_t Nq, int64_t Nk, int64_t d, int causal, float scale, int dtype,
+                      int64_t n_sel, const int64_t* sel_bh, const int64_t* sel_row,
+                      int64_t key_block, double* o64, double* lse64, int64_t* max_raised)
+{
+    return ref_rows(q, k, v, B, H, Nq, Nk, d, causal, scale, dtype, n_sel, sel_bh, sel_row, 1,
+                    key_block, o64, lse64, max_raised);
+}
+
+/* ------------------------------------------------------------------------- */
+/* fp64 -> storage format, round to nearest, ties to even (no double rounding) */
+/* ------------------------------------------------------------------------- */
+
+/* Round x to a binary format with p significand bits (implicit bit included),
+ * minimum normal exponent emin and maximum exponent emax. */
+static double round_format(double x, int p, int emin, int emax)
+{
+    if (x != x || x == 0.0 || isinf(x))
+        return x;
+    int e2;
+    frexp(x, &e2);      /* |x| = f * 2^e2, f in [0.5, 1): exponent of x is e2 - 1 */
+    int ex = e2 - 1;
+    if (ex < emin)
+        ex = emin;      /* subnormal range: fixed quantum */
+    double quantum = ldexp(1.0, ex - p + 1);
+    double r = rint(x / quantum) * quantum; /* rint rounds half to even */
+    double maxfin = ldexp(2.0 - ldexp(1.0, 1 - p), emax);
+    if (fabs(r) > maxfin)
+        return copysign(INFINITY, x);
+    return r;
+}
+
+static uint16_t encode_f16(double r)
+{
+    /* r is exactly representable in binary16 (or +-inf / nan) */
+    uint16_t sign = signbit(r) ? 0x8000 : 0;
+    if (r != r)
+        return 0x7e00;
+    double a = fabs(r);
+    if (isinf(a))
+        return sign | 0x7c00;
+    if (a == 0.0)
+        return sign;
+    if (a < ldexp(1.0, -14))
+        return sign | (uint16_t)(a / ldexp(1.0, -24)); /* subnormal */
+    int e2;
+    frexp(a, &e2);
+    int ex = e2 - 1;
+    uint16_t frac = (uint16_t)(a / ldexp(1.0, ex - 10) - 1024.0);
+    return sign | (uint16_t)((ex + 15) << 10) | frac;
+}
+
+static void store_rounded(double x, int dtype, void* out, int64_t idx)
+{
+    if (dtype == FA_ORACLE_F32) {
+        float f = (float)round_format(x, 24, -126, 127);
+        memcpy((char*)out + 4 * idx, &f, 4);
+    } else if (dtype == FA_ORACLE_BF16) {
+        uint16_t h;
+        if (x != x) {
+            h = 0x7fc0;
+        } else {
+            float f = (float)round_format(x, 8, -126, 127); /* exact in binary32 */
+            uint32_t u;
+            memcpy(&u, &f, 4);
+            h = (uint16_t)(u >> 16);
+        }
+        memcpy((char*)out + 2 * idx, &h, 2);
+    } else {
+        uint16_t h = encode_f16(round_format(x, 11, -14, 15));
+        memcpy((char*)out + 2 * idx, &h, 2);
+    }
+}
+
+int fa_oracle_round(const double* x, int64_t n, int dtype, void* out)
+{
+    if (!x || !out || n < 0)
+        return FA_ORACLE_EINVAL;
+    if (dtype != FA_ORACLE_F32 && dtype != FA_ORACLE_F16 && dtype != FA_ORACLE_BF16)
+        return FA_ORACLE_EINVAL;
+    for (int64_t i = 0; i < n; ++i)
+        store_rounded(x[i], dtype, out, i);
+    return FA_ORACLE_OK;
+}
+
+int fa_fwd_ref(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+               int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal, float scale, int dtype)
+{
+    int rc = check_raw(q, k, v, B, H, Nq, Nk, d, dtype);
+    if (rc)
+        return rc;
+    if (!o || !lse)
+        return FA_ORACLE_EINVAL;
+    double* o64 = (double*)malloc((size_t)(Nq * d) * sizeof(double));
+    double* l64 = (double*)malloc((size_t)Nq * sizeof(double));
+    int64_t* bh = (int64_t*)malloc((size_t)Nq * sizeof(int64_t));
+    int64_t* row = (int64_t*)malloc((size_t)Nq * sizeof(int64_t));
+    if (!o64 || !l64 || !bh || !row) {
+        free(o64);
+        free(l64);
+        free(bh);
+        free(row);
+        return FA_ORACLE_ENOMEM;
+    }
+    for (int64_t h = 0; h < B * H && rc == FA_ORACLE_OK; ++h) {
+        for (int64_t r = 0; r < Nq; ++r) {
+            bh[r] = h;
+            row[r] = r;
+        }
+        rc = fa_ref_rows_f64(q, k, v, B, H, Nq, Nk, d, causal, scale, dtype, Nq, bh, row, o64,
+                             l64);
+        if (rc)
+            break;
+        for (int64_t i = 0; i < Nq * d; ++i)
+            store_rounded(o64[i], dtype, o, h * Nq * d + i);
+        for (int64_t r = 0; r < Nq; ++r)
+            lse[h * Nq + r] = (float)l64[r];
+    }
+    free(o64);
+    free(l64);
+    free(bh);
+    free(row);
+    return rc;
+}

@@ -1,0 +1,126 @@
+"""Mutation tests: the pins have teeth (CPU only).
+
+Each case plants one plausible mistake in a private copy of the oracle's C
+source — compiled into a temporary library, never touching the real one — and
+checks that at least one pin of the battery below rejects it.  The first cases
+are the blog/article's own troubleshooting entry (a rescale factor forgotten in
+the running sum — "手写"/CUTLASS article section 3.3 and its section 6.3 table);
+the rest are a dropped scale, an inverted mask, a wrong index, a wrong sign.
+"""
+import json
+import math
+import os
+import shutil
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+SRC = os.path.join(os.path.dirname(oracle.__file__), "fa_oracle.c")
+
+MUTANTS = {
+    "softmax_sum_not_rebased": ("double carry = (l == 0.0) ? 0.0 : l * exp(m - m_new);",
+                                "double carry = (l == 0.0) ? 0.0 : l;"),
+    "online_rescale_dropped": ("double c = first ? 0.0 : exp(m_old - m_new);",
+                               "double c = first ? 0.0 : 1.0;"),
+    "online_output_not_rescaled": ("st[2 + t] = st[2 + t] * c + e * vrow[t];",
+                                   "st[2 + t] = st[2 + t] + e * vrow[t];"),
+    "merge_sum_not_rebased": ("double d = a[1] * ca + b[1] * cb;",
+                              "double d = a[1] + b[1] * cb;"),
+    "merge_wrong_sign": ("double cb = exp(mb - m);", "double cb = exp(m - mb);"),
+    "scale_dropped": ("return scale * dot;", "return dot;"),
+    "mask_inverted": ("if (causal && kk > r)", "if (causal && kk < r)"),
+    "mask_off_by_one": ("if (causal && kk > r)", "if (causal && kk >= r)"),
+    "value_index_transposed": ("o_row[t] += s[kk] * v[kk * d + t];",
+                               "o_row[t] += s[kk] * v[kk * d + (d - 1 - t)];"),
+    "lse_wrong_sign": ("*lse = m + log(l);", "*lse = m - log(l);"),
+    "online_lse_wrong_sign": ("*lse = run[0] + log(run[1]);", "*lse = run[0] - log(run[1]);"),
+}
+
+
+def _pins(L):
+    """Run the pin battery against library L; return the names of the pins that fail."""
+    failed = []
+
+    def check(name, fn):
+        try:
+            fn()
+        except (AssertionError, oracle.OracleError, FloatingPointError, ValueError):
+            failed.append(name)
+
+    def worked_example():
+        g = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+        y, tr = oracle.softmax_online(g["scores"], g["block"], L=L)
+        z = math.fsum(math.exp(v - 5.0) for v in g["scores"])
+        assert abs(tr["run_l"][1] - g["printed"]["total_sum"]) < 6e-4
+        np.testing.assert_allclose(y, [math.exp(v - 5.0) / z for v in g["scores"]], rtol=1e-14)
+
+    def torch_sdpa():
+        import torch
+        rng = np.random.default_rng(3)
+        for causal in (False, True):
+            q, k, v = (rng.standard_normal((24, 8)) for _ in range(3))
+            o, _ = oracle.attention_f64(q, k, v, causal, 0.4, L=L)
+            mask = torch.from_numpy(np.tril(np.ones((24, 24), bool))) if causal else None
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                *(torch.from_numpy(a)[None] for a in (q, k, v)), attn_mask=mask, scale=0.4)[0]
+            np.testing.assert_allclose(o, ref.numpy(), rtol=1e-12, atol=1e-13)
+
+    def lse_scipy():
+        from scipy.special import logsumexp
+        rng = np.random.default_rng(4)
+        q, k, v = (rng.standard_normal((20, 8)) for _ in range(3))
+        _, lse = oracle.attention_f64(q, k, v, False, 0.4, L=L)
+        np.testing.assert_allclose(lse, logsumexp(0.4 * q @ k.T, axis=1), rtol=1e-13)
+
+    def part2_vs_part1():
+        rng = np.random.default_rng(5)
+        q, k = rng.standard_normal((30, 16)) * 3, rng.standard_normal((30, 16)) * 3
+        v = rng.standard_normal((30, 16))
+        for causal in (False, True):
+            o1, l1 = oracle.attention_f64(q, k, v, causal, 0.25, L=L)
+            for kb in (0, 5):
+                o2, l2, _ = oracle.online_f64(q, k, v, causal, 0.25, kb, L=L)
+                np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-12)
+                np.testing.assert_allclose(l2, l1, rtol=1e-12, atol=1e-12)
+
+    def merge_closed_form():
+        a = np.array([0.3, 2.5, 1.0, -2.0])
+        b = np.array([-1.2, 0.7, 0.5, 4.0])
+        ab = oracle.merge(a, b, L=L)
+        m = 0.3
+        ca, cb = 1.0, math.exp(-1.5)
+        np.testing.assert_allclose(ab, [m, 2.5 * ca + 0.7 * cb, 1.0 * ca + 0.5 * cb,
+                                        -2.0 * ca + 4.0 * cb], rtol=1e-15)
+
+    for name, fn in [("worked_example", worked_example), ("torch_sdpa", torch_sdpa),
+                     ("lse_scipy", lse_scipy), ("part2_vs_part1", part2_vs_part1),
+                     ("merge_closed_form", merge_closed_form)]:
+        check(name, fn)
+    return failed
+
+
+def test_unmutated_oracle_passes_battery(oracle_lib):
+    assert _pins(oracle_lib) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    before, after = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(before) >= 1, f"mutation site for {name} not found"
+    mutated = src.replace(before, after)
+    cdir = tmp_path / "oracle"
+    cdir.mkdir()
+    (cdir / "fa_oracle.c").write_text(mutated)
+    inc = tmp_path / "include"
+    inc.mkdir()
+    shutil.copy(os.path.join(os.path.dirname(SRC), "..", "include", "fa_oracle.h"), inc)
+    so = str(tmp_path / "libmutant.so")
+    oracle.build(so, str(cdir / "fa_oracle.c"))
+    L = oracle.load(so)
+    with np.errstate(all="ignore"):
+        failed = _pins(L)
+    assert failed, f"mutant {name} passed every pin"
