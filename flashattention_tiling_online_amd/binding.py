@@ -1,0 +1,106 @@
+"""Thin ctypes binding of libfa.so (include/fa.h): argument marshalling only.
+
+Every step of the attention forward runs in the library's gfx950 kernels; torch
+is used for device memory and the current HIP stream.  If the library has not
+been built the first call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfa.so")
+
+FA_DTYPE_F32, FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1, 2
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH = 0, 1, 2, 3
+
+# symbols include/fa.h declares
+EXPORTS = ("fa_fwd", "fa_status_str", "fa_tile_rows")
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__(f"fa_fwd failed: {fa_status_str(status)} ({status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build the HIP library first "
+                "(python -m flashattention_tiling_online_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        i64 = ctypes.c_int64
+        L.fa_fwd.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_void_p, i64, i64, i64, i64, i64,
+                                                      ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                                      ctypes.c_void_p]
+        L.fa_fwd.restype = ctypes.c_int
+        L.fa_status_str.argtypes = [ctypes.c_int]
+        L.fa_status_str.restype = ctypes.c_char_p
+        L.fa_tile_rows.argtypes = [ctypes.c_int, i64, ctypes.c_int]
+        L.fa_tile_rows.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def fa_status_str(status: int) -> str:
+    return lib().fa_status_str(int(status)).decode()
+
+
+def fa_tile_rows(dtype: int, d: int, causal: bool) -> int:
+    return lib().fa_tile_rows(int(dtype), int(d), int(bool(causal)))
+
+
+def fa_fwd_raw(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int, Nk: int,
+               d: int, causal: int, scale: float, dtype: int, stream: int) -> int:
+    """Direct call with integer device pointers; returns the fa_status_t code."""
+    return lib().fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, int(causal), float(scale),
+                        int(dtype), stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: FA_DTYPE_F32, torch.float16: FA_DTYPE_F16,
+             torch.bfloat16: FA_DTYPE_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def fa_fwd(q, k, v, causal: bool = False, scale: float | None = None, o=None, lse=None,
+           stream=None):
+    """O, L = attention forward of torch tensors q [B,H,Nq,d], k, v [B,H,Nk,d] on the GPU.
+
+    o and lse are allocated (torch) when not given.  The kernel is enqueued on
+    ``stream`` (default: torch's current stream) and the call returns at once.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-D GPU tensor [B,H,N,d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != (B, H, Nk, d):
+        raise ValueError("k and v must be [B,H,Nk,d] with q's B, H and d")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share a dtype")
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H,
+                    Nq, Nk, d, int(bool(causal)), scale, code, stream.cuda_stream)
+    if st != FA_OK:
+        raise FAError(st)
+    return o, lse

@@ -1,0 +1,35 @@
+"""Build libfa.so (the gfx950 HIP kernels and their C-ABI) in-tree with hipcc."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "fa_abi.hip")
+OUT = os.path.join(PKG, "libfa.so")
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-Wall",
+    # keep the compiler from emitting packed-fp32 VALU instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def build(out: str = OUT, extra=()) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = out + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-o", tmp, SRC]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)  # atomic: a reader never sees a half-written library
+    return out
+
+
+if __name__ == "__main__":
+    print(build(*(sys.argv[1:2] or [])))

@@ -1,0 +1,48 @@
+// fa_common.hpp — device-side helpers shared by the gfx950 attention kernels.
+//
+// Work decomposition: one workgroup per (batch*head, query tile), as in the
+// course page "05_flash_attention.py" (flash_attention_forward: each query block
+// is owned by one thread block and its state stays on chip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.693147180559945309417f;
+
+// Number of XCDs (accelerator complex dies) on gfx950.  Consecutive workgroup ids
+// are dispatched round-robin over them, and each has its own L2.
+constexpr int kXcds = 8;
+
+// Map the hardware workgroup id to a logical tile id so that the logical ids an
+// XCD receives are contiguous.  Logical ids are ordered head-major, so the query
+// tiles of one head — which all stream the same K and V — share one XCD's L2.
+// A bijection on [0, n) for any n.
+__device__ __forceinline__ int xcd_remap(int wg, int n)
+{
+    const int per = n / kXcds;
+    const int rem = n % kXcds;
+    const int x = wg % kXcds;     // XCD this workgroup lands on
+    const int j = wg / kXcds;     // its rank among that XCD's workgroups
+    return x * per + (x < rem ? x : rem) + j;
+}
+
+// -inf as a float constant usable in device code
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Exchange with the lane 32 positions away (the other half of a wave64).
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+
+}  // namespace fa

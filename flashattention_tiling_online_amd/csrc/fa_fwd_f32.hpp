@@ -1,0 +1,189 @@
+// fa_fwd_f32.hpp — fused attention forward for fp32 inputs on gfx950.
+//
+// Same recurrence and work decomposition as the bf16/fp16 kernel (the course page
+// "05_flash_attention.py", flash_attention_forward; the blog page "Flash
+// Attention" for the rescale of the unnormalised accumulator), but every operand
+// stays fp32: both contractions use v_mfma_f32_32x32x2_f32, and P is fed to the
+// second one without rounding.  This path exists for fp32 callers who need
+// single-precision accuracy; it is simple rather than fast (single-buffered
+// LDS, two barriers per tile).
+//
+// Register layouts mirror the bf16 kernel: S^T = K Q^T and O^T = V^T P^T, so each
+// lane owns one query.  With k = 2 per MFMA, lane half hh supplies one k index:
+//   S:  A = K[key = 32kb + lane%32][d = 2c + hh],   B = Q[my_q][2c + hh]
+//   PV: A = V[key(kb, t, hh)][d = 32db + lane%32],  B = P[my_q][key(kb, t, hh)]
+// with key(kb, t, hh) = 32kb + 8(t/4) + 4hh + t%4 the key of accumulator register t.
+// LDS strides: K rows D+2 floats (64 lanes hit 64 distinct banks), V rows D+8
+// floats (the two wave halves read rows 4 apart, 32 banks apart).
+#pragma once
+
+#include "fa_common.hpp"
+
+namespace fa {
+
+template <int D>
+struct TileF32 {
+    static constexpr int BR = 128;
+    static constexpr int BC = 64;
+    static constexpr int NT = 256;
+    static constexpr int KS = D + 2;
+    static constexpr int VS = D + 8;
+    static constexpr int CH = BC * D / 4 / NT;  // float4 chunks per thread per tensor
+    static constexpr int DB = D / 32;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256)
+void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                       const float* __restrict__ V, float* __restrict__ O,
+                       float* __restrict__ LSE, int Nq, int Nk, int n_qtiles, float c2)
+{
+    using P = TileF32<D>;
+    __shared__ __attribute__((aligned(16))) float Ks[P::BC * P::KS];
+    __shared__ __attribute__((aligned(16))) float Vs[P::BC * P::VS];
+
+    const int logical = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+    const int bh = logical / n_qtiles;
+    int qt = logical - bh * n_qtiles;
+    if (CAUSAL)
+        qt = n_qtiles - 1 - qt;
+    const int q0 = qt * P::BR;
+
+    const int tid = (int)threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int ql = lane & 31;
+    const int hh = lane >> 5;
+    const int qw0 = q0 + wave * 32;
+    const int my_q = qw0 + ql;
+
+    const float* Qh = Q + (size_t)bh * Nq * D;
+    const float* Kh = K + (size_t)bh * Nk * D;
+    const float* Vh = V + (size_t)bh * Nk * D;
+
+    float qf[D / 2];
+#pragma unroll
+    for (int c = 0; c < D / 2; ++c)
+        qf[c] = my_q < Nq ? Qh[(size_t)my_q * D + 2 * c + hh] : 0.f;
+
+    int nkt = (Nk + P::BC - 1) / P::BC;
+    if (CAUSAL) {
+        const int qlast = min(q0 + P::BR, Nq) - 1;
+        nkt = min(nkt, qlast / P::BC + 1);
+    }
+    const bool wave_active = qw0 < Nq;
+    const int qw_last = min(qw0 + 31, Nq - 1);
+
+    f32x16 o[P::DB];
+#pragma unroll
+    for (int db = 0; db < P::DB; ++db)
+        o[db] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    float m2 = neg_inf();
+    float l = 0.f;
+
+    for (int j = 0; j < nkt; ++j) {
+        const int key0 = j * P::BC;
+        __syncthreads();  // previous tile fully consumed
+#pragma unroll
+        for (int i = 0; i < P::CH; ++i) {
+            const int f = i * P::NT + tid;
+            const int key = f / (D / 4);
+            const int d4 = f % (D / 4);
+            const int gk = key0 + key;
+            f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+            if (gk < Nk) {
+                kv = *reinterpret_cast<const f32x4*>(Kh + (size_t)gk * D + 4 * d4);
+                vv = *reinterpret_cast<const f32x4*>(Vh + (size_t)gk * D + 4 * d4);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                Ks[key * P::KS + 4 * d4 + e] = kv[e];
+            *reinterpret_cast<f32x4*>(Vs + key * P::VS + 4 * d4) = vv;
+        }
+        __syncthreads();
+
+        if (!wave_active || (CAUSAL && key0 > qw_last))
+            continue;
+
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+            for (int c = 0; c < D / 2; ++c)
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[(32 * kb + ql) * P::KS + 2 * c + hh],
+                                                             qf[c], s[kb], 0, 0, 0);
+        }
+
+        const bool need_mask = (key0 + P::BC > Nk) || (CAUSAL && key0 + P::BC - 1 > qw0);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    if (key >= Nk || (CAUSAL && key > my_q))
+                        s[kb][r] = neg_inf();
+                }
+        }
+
+        float mx = s[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                mx = fmaxf(mx, s[kb][r]);
+        mx = fmaxf(mx, swap_halves(mx));
+        const float m_new = fmaxf(m2, mx * c2);
+        const bool none = (m_new == neg_inf());
+        const float alpha = none ? 1.f : exp2_fast(m2 - m_new);
+        const float mneg = none ? 0.f : -m_new;
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = exp2_fast(fmaf(s[kb][r], c2, mneg));
+                s[kb][r] = p;
+                rs += p;
+            }
+        l = l * alpha + rs;
+        m2 = m_new;
+#pragma unroll
+        for (int db = 0; db < P::DB; ++db)
+            o[db] *= alpha;
+
+#pragma unroll
+        for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    const int key = 32 * kb + 8 * (t >> 2) + 4 * hh + (t & 3);
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[key * P::VS + 32 * db + ql],
+                                                                 s[kb][t], o[db], 0, 0, 0);
+                }
+    }
+
+    if (!wave_active)
+        return;
+    const float lt = l + swap_halves(l);
+    if (my_q < Nq) {
+        const float inv = 1.0f / lt;
+        float* orow = O + ((size_t)bh * Nq + my_q) * D;
+#pragma unroll
+        for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                f32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = o[db][4 * a + e] * inv;
+                *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * a + 4 * hh) = w;
+            }
+        if (hh == 0)
+            LSE[(size_t)bh * Nq + my_q] = (m2 + log2_fast(lt)) * kLn2;
+    }
+}
+
+}  // namespace fa

@@ -9,10 +9,10 @@ the host-side, version-pinned equivalent):
 
 * every (tensor, b, h) slice [N, d] has its own stream:
   ``numpy.random.Generator(PCG64(SeedSequence([seed, tensor_id, b, h])))``,
-  ``standard_normal((N, d))`` in fp64, times sigma — so any head can be
-  regenerated alone;
-* the fp64 draw is rounded to the storage dtype with round-to-nearest-even,
-  directly from fp64 (no double rounding through fp32);
+  ``standard_normal((N, d), dtype=float32)`` times sigma in fp32 — so any head
+  can be regenerated alone;
+* the fp32 draw is rounded once to the storage dtype with round-to-nearest-even
+  (bf16: on the raw bits; fp16: numpy's conversion; fp32: as drawn);
 * bf16 is carried as ``uint16`` bit patterns, fp16 as ``float16``, fp32 as
   ``float32``.
 
@@ -22,6 +22,8 @@ shapes, dtypes, causal flags and value laws.
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import numpy as np
@@ -82,11 +84,37 @@ WORKLOADS = {
 SAMPLE_SEED = 9001
 
 
+def _bf16_bits_fast(x: np.ndarray):
+    """fp64 -> bf16 nearest-even on the raw bits: keep 7 of the 52 fraction bits,
+    adding half an ulp minus one plus the kept lsb (ties to even), then rebias the
+    exponent from 1023 to 127.  Returns (bits, ok) where ok marks the elements whose
+    result is a normal bf16 number; the others need the general path."""
+    u = x.view(np.uint64)
+    r = (u + np.uint64((1 << 44) - 1) + ((u >> np.uint64(45)) & np.uint64(1))) >> np.uint64(45)
+    sign = (r >> np.uint64(18)) & np.uint64(1)
+    e = ((r >> np.uint64(7)) & np.uint64(0x7FF)).astype(np.int64) - 1023 + 127
+    frac = r & np.uint64(0x7F)
+    ok = (e >= 1) & (e <= 254) & np.isfinite(x)
+    bits = (sign << np.uint64(15)) | (np.clip(e, 0, 255).astype(np.uint64) << np.uint64(7)) | frac
+    return bits.astype(np.uint16), ok
+
+
 def round_fp64(x: np.ndarray, dtype: str) -> np.ndarray:
     """Round fp64 values to the storage dtype, nearest-even, with no double rounding."""
-    x = np.asarray(x, dtype=np.float64)
+    x = np.ascontiguousarray(x, dtype=np.float64)
     if dtype == "f32":
         return x.astype(np.float32)  # a single IEEE rounding, nearest-even
+    if dtype == "bf16":
+        bits, ok = _bf16_bits_fast(x)
+        if ok.all():
+            return bits
+        bits[~ok] = _round_general(x[~ok], dtype)
+        return bits
+    return _round_general(x, dtype)
+
+
+def _round_general(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Scaling-based rounding that also covers zeros, subnormals, overflow and NaN."""
     if dtype == "f16":
         p, emin, emax = 11, -14, 15
     elif dtype == "bf16":
@@ -109,10 +137,35 @@ def round_fp64(x: np.ndarray, dtype: str) -> np.ndarray:
 
 def head_values(seed: int, tensor: str, b: int, h: int, n: int, d: int,
                 sigma: float) -> np.ndarray:
-    """fp64 draw for one (tensor, b, h) slice."""
+    """fp32 draw for one (tensor, b, h) slice."""
     ss = np.random.SeedSequence([int(seed), TENSOR_IDS[tensor], int(b), int(h)])
     rng = np.random.Generator(np.random.PCG64(ss))
-    return rng.standard_normal((n, d)) * sigma
+    x = rng.standard_normal((n, d), dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    return x
+
+
+def round_fp32(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round fp32 values to the storage dtype, nearest-even (in place for bf16)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "f32":
+        return x
+    if dtype == "f16":
+        return x.astype(np.float16)
+    # bf16: add 0x7fff plus the lsb that is kept, then drop the low 16 bits; a carry
+    # into the exponent is the correct rounding, and overflow lands on +-inf
+    nan = np.isnan(x)
+    u = x.view(np.uint32)
+    lsb = u >> np.uint32(16)
+    lsb &= np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u >>= np.uint32(16)
+    out = u.astype(np.uint16)
+    if nan.any():
+        out[nan] = 0x7FC0
+    return out
 
 
 def make_tensor(w: Workload, tensor: str) -> np.ndarray:
@@ -120,9 +173,18 @@ def make_tensor(w: Workload, tensor: str) -> np.ndarray:
     n = w.Nq if tensor == "q" else w.Nk
     sigma = {"q": w.sigma_q, "k": w.sigma_k, "v": w.sigma_v}[tensor]
     out = np.empty((w.B, w.H, n, w.d), dtype=STORAGE[w.dtype])
-    for b in range(w.B):
-        for h in range(w.H):
-            out[b, h] = round_fp64(head_values(w.seed, tensor, b, h, n, w.d, sigma), w.dtype)
+
+    def fill(bh):
+        b, h = divmod(bh, w.H)
+        out[b, h] = round_fp32(head_values(w.seed, tensor, b, h, n, w.d, sigma), w.dtype)
+
+    heads = range(w.B * w.H)
+    if w.B * w.H * n * w.d < (1 << 22):
+        for bh in heads:
+            fill(bh)
+    else:  # each head has its own stream, so heads can be drawn in parallel
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, heads))
     return out
 
 

@@ -1,0 +1,102 @@
+/*
+ * fa.h — C-ABI of the MI355X (gfx950) fused attention forward library, libfa.so.
+ *
+ * One entry point computes, for every batch b and head h,
+ *
+ *     S = scale * Q[b,h] K[b,h]^T            (Nq x Nk, never written to memory)
+ *     S[q,k] = -inf where causal and k > q   (key k visible to query q iff k <= q)
+ *     O[b,h] = softmax_rows(S) V[b,h]
+ *     L[b,h,q] = ln sum_k exp(S[q,k])        (the row logsumexp, natural log)
+ *
+ * tiled over query row-blocks and key/value column-blocks with the online-softmax
+ * (m, l, O~) recurrence, so that the score matrix stays on chip.  Definitions:
+ *   - the operation and the returned L = m + log l: the "05_flash_attention.py"
+ *     course page (semidirectx.com, CS336 lecture 5), standard_attention and
+ *     flash_attention_forward;
+ *   - the scale tau applied to Q K^T and the mask: the "Flash Attention" blog page
+ *     (blog.cyberangel.work), Algorithm 2;
+ *   - the causal rule (k visible to q iff k <= q, top-left aligned): the course
+ *     page's triu(1) mask and its causal block skip.
+ *
+ * The library allocates nothing, keeps no state between calls and never prints.
+ * Every call is re-entrant.  Link with -lfa (it depends on the HIP runtime only).
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o.  lse is always fp32. */
+typedef enum {
+    FA_DTYPE_F32 = 0,  /* IEEE binary32 */
+    FA_DTYPE_F16 = 1,  /* IEEE binary16 */
+    FA_DTYPE_BF16 = 2  /* bfloat16 (upper half of binary32) */
+} fa_dtype_t;
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative size, Nk = 0 with queries,
+                               non-positive or non-finite scale, unknown dtype, size limit */
+    FA_ERR_UNSUPPORTED = 2, /* head size d outside {64, 128} */
+    FA_ERR_LAUNCH = 3       /* the HIP runtime rejected the kernel launch */
+} fa_status_t;
+
+/* hipStream_t without the HIP headers: pass the stream handle (0 = default stream). */
+typedef void* fa_stream_t;
+
+/*
+ * fa_fwd — fused attention forward on the GPU.
+ *
+ * Arguments (all pointers are DEVICE pointers owned by the caller):
+ *   q    [B, H, Nq, d]  element type `dtype`, contiguous, d fastest
+ *   k    [B, H, Nk, d]  same
+ *   v    [B, H, Nk, d]  same
+ *   o    [B, H, Nq, d]  output, element type `dtype`; rounded from fp32 to nearest-even
+ *   lse  [B, H, Nq]     output, fp32, natural-log row logsumexp of the scaled, masked scores
+ *   B, H, Nq, Nk        batch, heads, query and key/value lengths (any values >= 0 that
+ *                       fit the limits below; not restricted to tile multiples)
+ *   d                   head size: 64 or 128
+ *   causal              0: every key visible; 1: key k visible to query q iff k <= q
+ *                       (0-based, top-left aligned also when Nq != Nk)
+ *   scale               multiplies Q K^T before the softmax (usually 1/sqrt(d));
+ *                       must be finite and > 0
+ *   dtype               element type of q, k, v and o
+ *   stream              HIP stream the kernel is enqueued on
+ *
+ * Alignment: q, k, v and o must be 16-byte aligned, lse 4-byte aligned.  The output
+ * buffers must not overlap the inputs.
+ *
+ * Behaviour:
+ *   - returns before the kernel completes (asynchronous on `stream`);
+ *   - B*H*Nq == 0: nothing to compute, returns FA_OK without touching the GPU or
+ *     any buffer (the pointers may then be NULL; dtype, d, causal and scale are still
+ *     validated);
+ *   - Nk == 0 with queries present: FA_ERR_INVALID_ARG (softmax over no keys);
+ *   - every argument error is reported before any HIP call;
+ *   - NaN or Inf in the inputs propagate to the affected rows;
+ *   - limits: Nq*d and Nk*d below 2^31 (per-head offsets are 32-bit), B*H below 2^31,
+ *     and ceil(Nq / fa_tile_rows(...)) * B * H below 2^31 (the 1-D grid); otherwise
+ *     FA_ERR_INVALID_ARG.
+ * Results are deterministic: the same inputs give bitwise-identical outputs.
+ */
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                   float scale, fa_dtype_t dtype, fa_stream_t stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* fa_status_str(fa_status_t status);
+
+/* Query-tile height (rows per workgroup) the library uses for (dtype, d, causal);
+ * 0 if the combination is unsupported.  Lets a caller size sample checks and
+ * compute the grid the library launches: ceil(Nq / rows) * B * H workgroups. */
+int fa_tile_rows(fa_dtype_t dtype, int64_t d, int causal);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

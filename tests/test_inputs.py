@@ -10,7 +10,7 @@ def test_deterministic_and_per_head_independent():
     b = inputs.make_tensor(w, "k")
     np.testing.assert_array_equal(a, b)
     # any head regenerates alone
-    one = inputs.round_fp64(inputs.head_values(12, "k", 1, 2, 17, 8, 1.0), "bf16")
+    one = inputs.round_fp32(inputs.head_values(12, "k", 1, 2, 17, 8, 1.0), "bf16")
     np.testing.assert_array_equal(a[1, 2], one)
     # different tensors / heads / seeds differ
     assert not np.array_equal(a, inputs.make_tensor(w, "v"))
@@ -49,3 +49,18 @@ def test_sample_rows():
     w2 = inputs.custom("t", 1, 2, 10, 10, 8, "bf16", False, seed=1)
     bh3, rows3 = inputs.sample_rows(w2, 5, 100)
     assert bh3.size == 20 and set(rows3.tolist()) == set(range(10))
+
+
+def test_round_fp32_to_bf16_matches_fp64_path():
+    """The in-place bit rounding equals the general fp64 rounding on fp32 inputs,
+    including ties, carries into the exponent, overflow and subnormals."""
+    rng = np.random.default_rng(9)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 3,
+                        (rng.standard_normal(1000) * 1e-39).astype(np.float32),
+                        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 3.3895314e38, -3.4e38, 0.0, -0.0,
+                                  np.inf, -np.inf], dtype=np.float32)])
+    got = inputs.round_fp32(x.copy(), "bf16")
+    want = inputs.round_fp64(x.astype(np.float64), "bf16")
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(inputs.round_fp32(x, "f16"),
+                                  inputs.round_fp64(x.astype(np.float64), "f16"))
