@@ -1,0 +1,217 @@
+"""Benchmark of the fused attention forward (fa_fwd) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one fa_fwd call over the whole workload (every head, every query
+tile: Q K^T, mask, online softmax, P V, epilogue).  Inputs are generated on the
+host from their seeds and copied to HBM before the timed region.  The timed
+region is bracketed by torch.cuda.synchronize() and measured with HIP events
+recorded on the stream the kernel is launched on (torch's current stream).
+
+Prints ONE JSON line on stdout.  Besides the throughput it carries:
+  roofline      the kernel against MI355X's dense bf16/fp16 MFMA peak
+                (2516.6 TFLOP/s = 256 CUs x 4096 flop/clk x 2.4 GHz): achieved =
+                counted flops per launch / average launch time; traffic = HBM bytes
+                per launch from the committed rocprofv3 counter summary in
+                profiles/, reported only while the kernel sources still hash to
+                the value recorded there (else null);
+  cpu_baseline  the fp64 oracle timed on this host's cores on a bounded, seeded
+                row sample of the same workload (time-budgeted; the sample is
+                described in the line).
+
+Counted flops follow the method's definition: 4*B*H*Nq*Nk*d, halved when causal.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (bf16, d=128, N=4K/8K/32K) + % of MFMA peak, 1 GPU"
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+HBM_PEAK_GBS = 8000.0
+CSRC = os.path.join(ROOT, "flashattention_tiling_online_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per launch from profiles/hbm_traffic_<workload>.txt, if still current."""
+    path = os.path.join(PROFILES, f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            a, b = line.split("=", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("kernel_sources_sha256_16") != kernel_source_hash():
+        log(f"[bench] {path} was taken on other kernel sources: traffic reported as null")
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def to_device(a, dtype, dev):
+    import numpy as np
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(a).to(dev)
+
+
+def cpu_baseline(w, q, k, v, budget_s: float):
+    """The oracle (part 1, fp64, all host threads) on a seeded row sample, for about
+    budget_s seconds of wall time; returns the dict for the JSON line."""
+    import numpy as np
+
+    import oracle
+    from flashattention_tiling_online_amd import inputs
+
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    bh, rows = inputs.sample_rows(w, w.B * w.H, w.Nq)  # every row, in a seeded order
+    perm = np.random.Generator(np.random.PCG64(inputs.SAMPLE_SEED)).permutation(bh.size)
+    bh, rows = bh[perm], rows[perm]
+    chunk = max(cores * 64, 256)
+    done = 0
+    flops = 0.0
+    t0 = time.perf_counter()
+    while done < bh.size and time.perf_counter() - t0 < budget_s:
+        sel = slice(done, min(done + chunk, bh.size))
+        order = np.lexsort((rows[sel], bh[sel]))  # rows of one head adjacent
+        b_, r_ = bh[sel][order], rows[sel][order]
+        oracle.ref_rows_f64(q, k, v, w.causal, w.scale, w.dtype, b_, r_, threads=cores)
+        vis = np.minimum(r_ + 1, w.Nk) if w.causal else np.full(r_.size, w.Nk)
+        flops += float((4.0 * w.d * vis).sum())
+        done = sel.stop
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": (f"{done} of the {bh.size} rows of {w.name} (all heads), taken in a "
+                       f"seeded random order until the {budget_s:g} s budget ran out; fp64 "
+                       f"three-step oracle on {cores} threads; rate = 4*d*visible_keys per "
+                       f"row summed over those rows / wall time")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="self_8k_causal")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="oracle seconds (wall)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run 3 plain device copies of MIB MiB "
+                         "(reference dispatches for scaling HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import flashattention_tiling_online_amd as fa
+    from flashattention_tiling_online_amd import inputs
+
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "dispatches": 3}), flush=True)
+        return 0
+
+    w = inputs.WORKLOADS[args.workload]
+    log(f"[bench] {w.describe()}: generating inputs")
+    q, k, v = inputs.make_qkv(w)
+    tq, tk, tv = (to_device(a, w.dtype, dev) for a in (q, k, v))
+    o = torch.empty_like(tq)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.fa_fwd(tq, tk, tv, causal=w.causal, scale=w.scale, o=o, lse=lse, stream=stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(end) / args.steps
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {ms:.4f} ms/step ({t_wall / args.steps * 1e3:.4f} ms wall), {tflops:.1f} TFLOP/s")
+
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = committed_traffic(w.name)
+    roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline (~{args.cpu_budget:.0f} s)")
+        cpu = cpu_baseline(w, q, k, v, args.cpu_budget)
+        log(f"[bench] cpu baseline: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} cores")
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "scale": "1/sqrt(d)",
+                   "inputs": f"N(0,{w.sigma_q:g}^2) Q, N(0,{w.sigma_k:g}^2) K, "
+                             f"N(0,{w.sigma_v:g}^2) V, seeded"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernel_sources_sha256_16": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
