@@ -12,24 +12,33 @@
 // (course page, causal branch of flash_attention_forward).
 //
 // gfx950 mapping (designed for CDNA4, not taken from the pages' NVIDIA design):
-//   * workgroup = 4 wave64s = 128 query rows; wave w owns rows [32w, 32w+32);
-//     2 workgroups per CU, so each SIMD interleaves two waves;
+//   * wave w owns query rows [32w, 32w+32) of its workgroup's tile; for d = 128 a
+//     workgroup is 8 waves (256 rows) and fills a CU alone, for d = 64 it is 4 waves
+//     (128 rows) and two share a CU: either way each SIMD interleaves two waves, and
+//     each staged K/V tile serves as many query rows as fit;
 //   * both contractions on v_mfma_f32_32x32x16_{bf16,f16}; S is computed
 //     transposed, S^T = K Q^T, so each lane owns ONE query (lane % 32) and 16 of
 //     the 32 keys of a 32-key block: the row max needs one exchange between the
 //     wave halves, the row sum none until the epilogue;
 //   * O is accumulated transposed, O^T = V^T P^T: alpha is a per-lane scalar and P
 //     is the MFMA B operand straight from the S registers (rounded to T);
-//   * K and V tiles go global -> LDS by DMA (buffer_load ... lds, 16 B per lane),
-//     with the buffer bound set to the head's remaining rows so that rows past Nk
-//     read as zero without a branch; LDS rows are XOR-swizzled on 16-byte chunks
-//     so that the K reads (ds_read_b128) and the V^T reads (ds_read_b64_tr_b16,
-//     which hands each lane 4 consecutive keys of one column) hit 64 distinct
-//     banks; the keys of V^T come out in exactly the order P has in registers;
+//   * K tiles go global -> LDS by DMA (buffer_load ... lds, 16 B per lane) into
+//     rows padded by 16 B, so that the K reads (ds_read_b128) of 16 consecutive
+//     rows hit 64 distinct banks and every operand address is one base register
+//     plus an immediate; a DMA block is 1 KB of consecutive LDS and lanes that land
+//     on padding are masked off;
+//   * V is transposed on its way to LDS: each thread loads a 4-key x 4-dim block
+//     into registers (one tile ahead), transposes it with 8 perms and writes V^T
+//     rows with ds_write_b64, keys already in the order P has in registers; the
+//     P.V operand is then a plain ds_read_b128 (LDS transpose reads deliver a
+//     third of the bytes per cycle on gfx950); thread -> block mapping and the
+//     144-byte V^T row stride make both the writes and the reads conflict-free;
+//   * every buffer access goes through a buffer resource bounded by the head's
+//     remaining rows, so rows past Nk read as zero without a branch;
 //   * software pipeline: while the softmax of tile j and the P.V MFMAs of tile j
 //     run, the S MFMAs of tile j+1 are issued; K and V have separate double
 //     buffers with the next loads issued one tile ahead; one barrier per tile;
-//   * exp is exp2 with scale*log2(e) folded into one FMA; the O rescale is skipped
+//   * exp is exp2 with scale*log2(e) folded into one FMA; the O~ rescale is skipped
 //     when no row max of the wave moved (alpha = 1 exactly); the row sum l is taken
 //     on the fp32 P before it is rounded for the MFMA (a sum of the rounded P would
 //     put up to 2^-9 relative error into l, and so into L, on rows with few keys).
@@ -39,10 +48,8 @@
 
 namespace fa {
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 template <typename T>
 struct Mfma16;
@@ -67,28 +74,39 @@ struct Mfma16<_Float16> {
 
 template <int D>
 struct Tile16 {
-    static constexpr int BR = 128;              // query rows per workgroup
-    static constexpr int BC = 64;               // keys per K/V tile
-    static constexpr int NT = 256;              // threads per workgroup
-    static constexpr int ROWB = D * 2;          // bytes per K/V row
-    static constexpr int TILE = BC * ROWB;      // bytes per K or V tile
-    static constexpr int LPW = TILE / 1024 / 4; // 1 KB DMA loads per wave per tile
-    static constexpr int DC = D / 16;           // 16-wide d chunks of the S contraction
-    static constexpr int DB = D / 32;           // 32-wide d blocks of O
-    static constexpr int LDS = 4 * TILE;        // K[2] and V[2]
-    static constexpr int K0 = 0, K1 = TILE, V0 = 2 * TILE, V1 = 3 * TILE;
-    static_assert(LPW >= 1, "tile too small for the DMA staging");
+    // d = 128: 8 waves (256 query rows) share each staged K/V tile, one workgroup
+    // per CU (2 waves per SIMD); d = 64: 4 waves (128 rows), two workgroups per CU,
+    // so that the small-d grids still cover the chip.
+    static constexpr int NW = D == 128 ? 8 : 4;  // waves per workgroup
+    static constexpr int BR = 32 * NW;           // query rows per workgroup
+    static constexpr int BC = 64;                // keys per K/V tile
+    static constexpr int NT = 64 * NW;           // threads per workgroup
+    static constexpr int ROWB = D * 2;           // bytes per K/V row in memory
+    static constexpr int KSTR = ROWB + 16;       // K row stride in LDS
+    static constexpr int VTSTR = 2 * BC + 16;    // V^T row stride in LDS (one row per dim)
+    static constexpr int KT = BC * KSTR;         // bytes of one K tile in LDS
+    static constexpr int VT = D * VTSTR;         // bytes of one V^T tile in LDS
+    static constexpr int KNB = KT / 1024;        // 1-KB DMA blocks per K tile
+    static constexpr int KPW = (KNB + NW - 1) / NW;  // K blocks per wave (at most)
+    static_assert(NT == 4 * D, "V staging: one 4-key x 4-dim block per thread");
+    static constexpr int DC = D / 16;            // 16-wide d chunks of the S contraction
+    static constexpr int DB = D / 32;            // 32-wide d blocks of O
+    static constexpr int LDS = 2 * KT + 2 * VT;  // K[2] and V^T[2]
+    static constexpr int K0 = 0, K1 = KT, V0 = 2 * KT, V1 = 2 * KT + VT;
+    static_assert(KT % 1024 == 0, "K tiles must be whole DMA blocks");
 };
 
-// XOR applied to the 16-byte chunk index of LDS row `row` (bijective on 16
-// consecutive rows; see the layout notes at the top of the file).
+// Byte offset, inside a tile of the [rows, D] matrix in memory, that lane `lane` of
+// the 1-KB DMA block `blk` fetches for an LDS tile with row stride `str`: the LDS
+// byte it lands on is blk*1024 + 16*lane.  -1 for lanes that land on row padding
+// (they are masked off and fetch nothing).
 template <int D>
-__device__ __forceinline__ int swz(int row)
+__device__ __forceinline__ int dma_src(int blk, int lane, int str)
 {
-    if constexpr (D == 128)
-        return ((row & 3) << 2) | ((row >> 2) & 3);
-    else
-        return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+    const int pos = blk * 1024 + 16 * lane;
+    const int row = pos / str;
+    const int ch = (pos - row * str) / 16;
+    return ch < (2 * D) / 16 ? row * (2 * D) + ch * 16 : -1;
 }
 
 // Word 3 of a gfx9 buffer resource for untyped (raw) loads: 32-bit data format.
@@ -104,23 +122,64 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const T* base, int r
                                              n * D * (int)sizeof(T), kRsrcWord3);
 }
 
-// DMA one K or V tile (rows [tile*BC, tile*BC + BC) of a head) into LDS: this wave's
-// LPW 1-KB blocks starting at `dst`; lane i of each block lands at dst + 1024*blk + 16*i.
-// A device function (not a lambda) so that the host pass never sees the builtin.
-template <int D, typename T>
+// DMA one K or V tile (rows [tile*BC, tile*BC + BC) of a head) into the LDS tile at
+// `dst`: this wave's blocks wave, wave+NW, ... (< NB); src[i] is the lane's source
+// offset for its i-th block (-1: padding, lane masked off).  A device function (not
+// a lambda) so that the host pass never sees the builtin.
+template <int D, int NB, int PW, typename T>
 __device__ __forceinline__ void stage_tile(const T* head, int tile, int nrows, char* dst,
-                                           const int* voff)
+                                           int wave, const int* src)
 {
-    using P = Tile16<D>;
-    const __amdgpu_buffer_rsrc_t r = rows_rsrc<D>(head, tile * P::BC, nrows);
+    const __amdgpu_buffer_rsrc_t r = rows_rsrc<D>(head, tile * Tile16<D>::BC, nrows);
 #pragma unroll
-    for (int i = 0; i < P::LPW; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * 1024), 16, voff[i], 0,
-                                                 0, 0);
+    for (int i = 0; i < PW; ++i) {
+        const int blk = wave + Tile16<D>::NW * i;
+        if (blk < NB && src[i] >= 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + blk * 1024), 16, src[i],
+                                                     0, 0, 0);
+    }
+}
+
+// V staging of one thread: the 4-key x 4-dim block (keys 4kg..4kg+3, dims
+// 4dq..4dq+3) of tile `tile`, loaded as four 8-byte rows (rows past nrows read 0).
+template <int D, typename T>
+__device__ __forceinline__ void load_v_block(const T* head, int tile, int nrows, int kg, int dq,
+                                             u32x2* r)
+{
+    const __amdgpu_buffer_rsrc_t rs = rows_rsrc<D>(head, tile * Tile16<D>::BC, nrows);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        r[m] = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, ((4 * kg + m) * D + 4 * dq) * 2, 0, 0));
+}
+
+// Transpose the block and write it as four V^T row segments (dim 4dq+e, 4 keys each)
+// at LDS byte `dst` + (4dq+e)*VTSTR + 2*slot, where the keys of 16-key chunk cc are
+// stored in the order the P registers hold them: slots 16cc + 8h + 0..3 hold keys
+// 16cc + 4h + 0..3 and slots 16cc + 8h + 4..7 hold keys 16cc + 8 + 4h + 0..3.
+template <int D>
+__device__ __forceinline__ void store_vt_block(char* dst, int kg, int dq, const u32x2* r)
+{
+    const int cc = kg >> 2, x = kg & 3;
+    const int slot = 16 * cc + 4 * (((x & 1) << 1) | (x >> 1));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t a0 = (e < 2) ? r[0].x : r[0].y, a1 = (e < 2) ? r[1].x : r[1].y;
+        const uint32_t a2 = (e < 2) ? r[2].x : r[2].y, a3 = (e < 2) ? r[3].x : r[3].y;
+        u32x2 w;
+        if (e & 1) {
+            w.x = (a0 >> 16) | (a1 & 0xffff0000u);
+            w.y = (a2 >> 16) | (a3 & 0xffff0000u);
+        } else {
+            w.x = (a0 & 0xffffu) | (a1 << 16);
+            w.y = (a2 & 0xffffu) | (a3 << 16);
+        }
+        *reinterpret_cast<u32x2*>(dst + (4 * dq + e) * Tile16<D>::VTSTR + 2 * slot) = w;
+    }
 }
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(Tile16<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                           const T* __restrict__ V, T* __restrict__ O, float* __restrict__ LSE,
                           int Nq, int Nk, int n_qtiles, float c2)
@@ -130,7 +189,6 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     using vec = typename M::vec;
     typedef T T4 __attribute__((ext_vector_type(4)));
     __shared__ __attribute__((aligned(1024))) char smem[P::LDS];
-    lds_char* const lds = (lds_char*)smem;
     const char* const sm = smem;
 
     // ---- which (batch*head, query tile) this workgroup owns
@@ -162,51 +220,40 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     if (CAUSAL && wave_active)
         n_w = min(nkt, min(qw0 + 31, Nq - 1) / P::BC + 1);
 
-    // ---- DMA staging: per-lane byte offsets inside a tile (fixed for the kernel)
-    int voff[P::LPW];
+    // ---- K staging by DMA: per-lane source offsets of this wave's blocks (fixed)
+    int ksrc[P::KPW];
 #pragma unroll
-    for (int i = 0; i < P::LPW; ++i) {
-        const int pos = (wave * P::LPW + i) * 1024 + lane * 16;
-        const int row = pos / P::ROWB;
-        const int pch = (pos % P::ROWB) / 16;
-        voff[i] = row * P::ROWB + ((pch ^ swz<D>(row)) * 16);
-    }
-    auto stage = [&](const T* head, int tile, int lds_off) {
-        stage_tile<D>(head, tile, Nk, smem + lds_off + wave * P::LPW * 1024, voff);
+    for (int i = 0; i < P::KPW; ++i)
+        ksrc[i] = dma_src<D>(wave + P::NW * i, lane, P::KSTR);
+    auto stage_k = [&](int tile, int lds_off) {
+        stage_tile<D, P::KNB, P::KPW>(Kh, tile, Nk, smem + lds_off, wave, ksrc);
     };
+    // ---- V staging through registers: this thread's 4-key x 4-dim block.  Within a
+    // 32-lane half-wave the blocks cover 4 consecutive dim-quads x 8 key groups, which
+    // makes the transposed ds_write_b64 conflict-free.
+    const int v_dq = (tid & 3) + 4 * (tid >> 6);
+    const int v_kg = ((tid >> 2) & 3) + 4 * (((tid >> 4) & 1) + 2 * ((tid >> 5) & 1));
+    u32x2 vreg[4];
 
-    // ---- operand addresses inside a K / V buffer
-    // K (A operand of S^T): lane reads K[32kb + ql][16c + 8hh .. +8]; kb adds 32 rows.
-    int kaddr[P::DC];
-#pragma unroll
-    for (int c = 0; c < P::DC; ++c)
-        kaddr[c] = ql * P::ROWB + (((2 * c + hh) ^ swz<D>(ql)) * 16);
-    // V^T (A operand of O^T) by transpose reads: for (db, r) the 16-lane group g
-    // reads rows 8r + 4h + j (j = 0..3) and columns 32db + 16(g%2) + 4a; 16-key
-    // chunk cc adds 16 rows.
-    int vaddr[P::DB][2];
-    {
-        const int g = lane >> 4, t = lane & 15;
-        const int j = t >> 2, a = t & 3;
-#pragma unroll
-        for (int db = 0; db < P::DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int row = 8 * r + 4 * (g >> 1) + j;
-                const int col = 32 * db + 16 * (g & 1) + 4 * a;
-                vaddr[db][r] = row * P::ROWB + (((col >> 3) ^ swz<D>(row)) * 16) + (col & 7) * 2;
-            }
-    }
+    // ---- operand addresses inside a K / V^T tile: one base each, the rest immediates
+    // K (A operand of S^T): lane reads K[32kb + ql][16c + 8hh .. +8] at
+    // kbase + 32c + 32kb*KSTR.
+    const int kbase = ql * P::KSTR + hh * 16;
+    // V^T (A operand of O^T): lane reads V^T[32db + ql][slots 16cc + 8hh .. +8] at
+    // vbase + 32db*VTSTR + 32cc.
+    const int vbase = ql * P::VTSTR + hh * 16;
 
     // ---- prologue: tiles 0 and 1 in flight, Q fragment into registers
     if (0 < nkt) {
-        stage(Kh, 0, P::K0);
-        stage(Vh, 0, P::V0);
+        stage_k(0, P::K0);
+        load_v_block<D>(Vh, 0, Nk, v_kg, v_dq, vreg);
     }
-    if (1 < nkt) {
-        stage(Kh, 1, P::K1);
-        stage(Vh, 1, P::V1);
-    }
+    if (1 < nkt)
+        stage_k(1, P::K1);
+    if (0 < nkt)
+        store_vt_block<D>(smem + P::V0, v_kg, v_dq, vreg);
+    if (1 < nkt)
+        load_v_block<D>(Vh, 1, Nk, v_kg, v_dq, vreg);  // written to LDS during step 0
     // Q (B operand of S^T = K Q^T): lane supplies Q[my_q][16c + 8hh .. +8]
     vec qf[P::DC];
 #pragma unroll
@@ -226,12 +273,12 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
         for (int c = 0; c < P::DC; ++c)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const vec a = *reinterpret_cast<const vec*>(sm + kb_off + kaddr[c] + kb * 32 * P::ROWB);
+                const vec a = *reinterpret_cast<const vec*>(sm + kb_off + kbase + 32 * c + kb * 32 * P::KSTR);
                 s[kb] = M::mma(a, qf[c], s[kb]);
             }
     };
 
-    // ---- running state: base-2 max, this half's partial sum, O^T accumulators
+    // ---- running state: base-2 reference max m2, this half's partial sum l, O^T
     f32x16 o[P::DB];
 #pragma unroll
     for (int db = 0; db < P::DB; ++db)
@@ -239,24 +286,33 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     float m2 = neg_inf();
     float l = 0.f;
 
-    // softmax of tile j (in s) and O^T += V_j^T P_j^T from the V buffer at vb_off
-    auto softmax_pv = [&](int j, f32x16* s, int vb_off) {
+    // mask tile j: keys key0 + 4hh + off (off = 32kb + 8(r/4) + r%4) past the end of
+    // the keys or (causal) after the query become -inf
+    auto mask_tile = [&](int j, f32x16* s) {
         const int key0 = j * P::BC;
-        const bool need_mask = (key0 + P::BC > Nk) || (CAUSAL && key0 + P::BC - 1 > qw0);
-        if (need_mask) {
-            // keys key0 + 4hh + off with off = 32kb + 8(r/4) + r%4 are visible iff off <= lim
-            const int last = CAUSAL ? min(Nk - 1, my_q) : Nk - 1;
-            const int lim = last - key0 - 4 * hh;
+        const int last = CAUSAL ? min(Nk - 1, my_q) : Nk - 1;
+        const int lim = last - key0 - 4 * hh;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
-                    if (off > lim)
-                        s[kb][r] = neg_inf();
-                }
-        }
-        // row max: 32 values in-lane, then the other wave half
+            for (int r = 0; r < 16; ++r) {
+                const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+                if (off > lim)
+                    s[kb][r] = neg_inf();
+            }
+    };
+    auto needs_mask = [&](int j) {
+        const int key0 = j * P::BC;
+        return (key0 + P::BC > Nk) || (CAUSAL && key0 + P::BC - 1 > qw0);
+    };
+
+    // Running-max update of the online softmax.  O~ and l are rescaled by
+    // alpha = 2^(m2 - m_new) only when some row of the wave raised its max (else
+    // alpha = 1 exactly and the 64 multiplies are skipped).  The reference is always
+    // the exact running max: the dominant key of a row then gets p = 1, which the
+    // rounding of P to bf16/fp16 keeps exact (a stale reference, even by a few
+    // units, measurably loses accuracy on rows dominated by one key).
+    auto update_max = [&](f32x16* s) {
         float mx = s[0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -265,15 +321,22 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                 mx = fmaxf(mx, s[kb][r]);
         mx = fmaxf(mx, swap_halves(mx));
         const float m_new = fmaxf(m2, mx * c2);  // c2 > 0: max commutes with the scale
-        // a row that has seen no visible key yet keeps alpha = 1 and p = 0
-        const bool none = (m_new == neg_inf());
-        const float alpha = none ? 1.f : exp2_fast(m2 - m_new);
-        const float mneg = none ? 0.f : -m_new;
+        if (__builtin_amdgcn_ballot_w64(m_new > m2) != 0) {
+            const float alpha = exp2_fast(m2 - m_new);  // 0 on the first tile (m2 = -inf)
+#pragma unroll
+            for (int db = 0; db < P::DB; ++db)
+                o[db] *= alpha;
+            l *= alpha;
+            m2 = m_new;
+        }
+    };
 
-        // P = 2^(s c2 - m_new) in fp32; the row sum is taken on these fp32 values
-        // (four independent chains), then P is rounded to T and packed in the MFMA
-        // B-operand order: chunk cc = 2kb + h holds registers 8h .. 8h+7 of block kb
-        vec pb[4];
+    // P = 2^(s c2 - m2) in fp32, summed into l (four independent chains), then
+    // rounded to T and packed in the MFMA B-operand order: chunk cc = 2kb + h holds
+    // registers 8h .. 8h+7 of block kb.  A row with no visible key so far (m2 = -inf)
+    // gets p = 0.
+    auto exp_sum_pack = [&](f32x16* s, vec* pb) {
+        const float mneg = (m2 == neg_inf()) ? 0.f : -m2;
         float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc)
@@ -283,55 +346,62 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                 rs[e & 3] += p;
                 pb[cc][e] = (T)p;
             }
-        l = l * alpha + ((rs[0] + rs[1]) + (rs[2] + rs[3]));
-        // rescale O~ only if some row of the wave raised its max (else alpha == 1)
-        if (__builtin_amdgcn_ballot_w64(m_new != m2) != 0) {
-#pragma unroll
-            for (int db = 0; db < P::DB; ++db)
-                o[db] *= alpha;
-        }
-        m2 = m_new;
+        l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    };
 
-        // O^T += V^T P^T; the two transpose reads give keys 8r + 4h + 0..3 of chunk cc
+    // O^T += V^T P^T from the V^T buffer at vb_off
+    auto pv = [&](const vec* pb, int vb_off) {
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
             for (int db = 0; db < P::DB; ++db) {
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4*)(lds + (vb_off + cc * 16 * P::ROWB + vaddr[db][0])));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4*)(lds + (vb_off + cc * 16 * P::ROWB + vaddr[db][1])));
-                const vec a = __builtin_bit_cast(vec, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                const vec a = *reinterpret_cast<const vec*>(sm + vb_off + vbase + 32 * db * P::VTSTR + 32 * cc);
                 o[db] = M::mma(a, pb[cc], o[db]);
             }
     };
 
-    __syncthreads();  // waits for this wave's DMA (vmcnt) and publishes tiles 0, 1
+    __syncthreads();  // waits for this wave's DMA (vmcnt), publishes K_0, K_1 and V_0
     f32x16 sa[2], sb[2];
     if (0 < n_w)
         scores(P::K0, sa);
     __syncthreads();  // every wave has read K_0
     if (2 < nkt)
-        stage(Kh, 2, P::K0);
+        stage_k(2, P::K0);
 
-    // one pipelined step: S of tile j+1 (from K buffer kn), softmax + P.V of tile j
-    // (from V buffer vc); then publish the loads issued one step ago and issue the
-    // next ones into the buffers this step has finished with
-    auto step = [&](int j, f32x16* s_cur, f32x16* s_nxt, int kn, int vc) {
-        if (j + 1 < n_w)
-            scores(kn, s_nxt);
-        if (j < n_w)
-            softmax_pv(j, s_cur, vc);
+    // One pipelined step: softmax + P.V of tile j (scores in s_cur, V^T buffer vc)
+    // and the S MFMAs of tile j+1 (K buffer kn, into s_nxt); then V_{j+1} (in
+    // registers since the last step) is written to the other V^T buffer vn, the
+    // barrier publishes it together with K_{j+2} (DMA issued one step ago), and the
+    // next loads go out: V_{j+2} into registers, K_{j+3} into kn.  In the common
+    // case (tile j unmasked, tile j+1 live) the S MFMAs, the exponentials and the
+    // P.V MFMAs form one basic block so that MFMA and VALU work interleave.
+    auto step = [&](int j, f32x16* s_cur, f32x16* s_nxt, int kn, int vc, int vn) {
+        if (j < n_w) {
+            if (needs_mask(j))
+                mask_tile(j, s_cur);
+            update_max(s_cur);
+            vec pb[4];
+            if (j + 1 < n_w) {
+                scores(kn, s_nxt);
+                exp_sum_pack(s_cur, pb);
+                pv(pb, vc);
+            } else {
+                exp_sum_pack(s_cur, pb);
+                pv(pb, vc);
+            }
+        }
+        if (j + 1 < nkt)
+            store_vt_block<D>(smem + vn, v_kg, v_dq, vreg);
         __syncthreads();
-        if (j + 3 < nkt)
-            stage(Kh, j + 3, kn);
         if (j + 2 < nkt)
-            stage(Vh, j + 2, vc);
+            load_v_block<D>(Vh, j + 2, Nk, v_kg, v_dq, vreg);
+        if (j + 3 < nkt)
+            stage_k(j + 3, kn);
     };
     for (int j = 0; j < nkt; j += 2) {
-        step(j, sa, sb, P::K1, P::V0);
+        step(j, sa, sb, P::K1, P::V0, P::V1);
         if (j + 1 < nkt)
-            step(j + 1, sb, sa, P::K0, P::V1);
+            step(j + 1, sb, sa, P::K0, P::V1, P::V0);
     }
 
     if (!wave_active)
