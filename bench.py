@@ -7,6 +7,9 @@ tile: Q K^T, mask, online softmax, P V, epilogue).  Inputs are generated on the
 host from their seeds and copied to HBM before the timed region.  The timed
 region is bracketed by torch.cuda.synchronize() and measured with HIP events
 recorded on the stream the kernel is launched on (torch's current stream).
+Before the W warmup steps, untimed steps run back to back for --settle seconds:
+from idle the GPU needs some tens of milliseconds of load to reach its steady
+clocks, and a few warmup steps of a sub-millisecond kernel do not cover that.
 
 Prints ONE JSON line on stdout.  Besides the throughput it carries:
   roofline      the kernel against MI355X's dense bf16/fp16 MFMA peak
@@ -116,8 +119,11 @@ def cpu_baseline(w, q, k, v, budget_s: float):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle", type=float, default=1.0, metavar="SECONDS",
+                    help="before the warmup steps, untimed steps for at least this long so "
+                         "the GPU clocks reach their steady state")
     ap.add_argument("--workload", default="self_8k_causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="oracle seconds (wall)")
@@ -159,7 +165,14 @@ def main() -> int:
     def step():
         fa.fa_fwd(tq, tk, tv, causal=w.causal, scale=w.scale, o=o, lse=lse, stream=stream)
 
-    log(f"[bench] warmup {args.warmup}")
+    settled = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle:
+        for _ in range(8):
+            step()
+        settled += 8
+        torch.cuda.synchronize()
+    log(f"[bench] settle {settled} steps, warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -195,6 +208,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settled,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",

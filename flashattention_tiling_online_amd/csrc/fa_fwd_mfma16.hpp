@@ -38,10 +38,11 @@
 //   * software pipeline: while the softmax of tile j and the P.V MFMAs of tile j
 //     run, the S MFMAs of tile j+1 are issued; K and V have separate double
 //     buffers with the next loads issued one tile ahead; one barrier per tile;
-//   * exp is exp2 with scale*log2(e) folded into one FMA; the O~ rescale is skipped
-//     when no row max of the wave moved (alpha = 1 exactly); the row sum l is taken
-//     on the fp32 P before it is rounded for the MFMA (a sum of the rounded P would
-//     put up to 2^-9 relative error into l, and so into L, on rows with few keys).
+//   * exp is exp2 with scale*log2(e) folded into one FMA; the running-max reference
+//     moves (with the O~ rescale) only when a row's max exceeds it by more than 2^8;
+//     L takes the fp32 row sum of P, O the row sum of the rounded P it was built
+//     from (see update_max);
+//   * waves that share a SIMD run each step in opposite orders (ping-pong).
 #pragma once
 
 #include "fa_common.hpp"
@@ -61,6 +62,13 @@ struct Mfma16<__bf16> {
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
+    // acc + (sum of the two elements of a packed pair), fp32 accumulate
+    static __device__ __forceinline__ float dot_ones(uint32_t pair, float acc)
+    {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+    }
 };
 
 template <>
@@ -69,6 +77,12 @@ struct Mfma16<_Float16> {
     static __device__ __forceinline__ f32x16 mma(vec a, vec b, f32x16 c)
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float dot_ones(uint32_t pair, float acc)
+    {
+        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
     }
 };
 
@@ -126,14 +140,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const T* base, int r
 // `dst`: this wave's blocks wave, wave+NW, ... (< NB); src[i] is the lane's source
 // offset for its i-th block (-1: padding, lane masked off).  A device function (not
 // a lambda) so that the host pass never sees the builtin.
-template <int D, int NB, int PW, typename T>
+template <int D, int NB, int PW, int NW, typename T>
 __device__ __forceinline__ void stage_tile(const T* head, int tile, int nrows, char* dst,
                                            int wave, const int* src)
 {
-    const __amdgpu_buffer_rsrc_t r = rows_rsrc<D>(head, tile * Tile16<D>::BC, nrows);
+    const __amdgpu_buffer_rsrc_t r = rows_rsrc<D>(head, tile * 64, nrows);
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
-        const int blk = wave + Tile16<D>::NW * i;
+        const int blk = wave + NW * i;
         if (blk < NB && src[i] >= 0)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + blk * 1024), 16, src[i],
                                                      0, 0, 0);
@@ -141,12 +155,13 @@ __device__ __forceinline__ void stage_tile(const T* head, int tile, int nrows, c
 }
 
 // V staging of one thread: the 4-key x 4-dim block (keys 4kg..4kg+3, dims
-// 4dq..4dq+3) of tile `tile`, loaded as four 8-byte rows (rows past nrows read 0).
+// 4dq..4dq+3) of 64-key tile `tile`, loaded as four 8-byte rows (rows past nrows
+// read 0).
 template <int D, typename T>
 __device__ __forceinline__ void load_v_block(const T* head, int tile, int nrows, int kg, int dq,
                                              u32x2* r)
 {
-    const __amdgpu_buffer_rsrc_t rs = rows_rsrc<D>(head, tile * Tile16<D>::BC, nrows);
+    const __amdgpu_buffer_rsrc_t rs = rows_rsrc<D>(head, tile * 64, nrows);
 #pragma unroll
     for (int m = 0; m < 4; ++m)
         r[m] = __builtin_bit_cast(
@@ -157,7 +172,7 @@ __device__ __forceinline__ void load_v_block(const T* head, int tile, int nrows,
 // at LDS byte `dst` + (4dq+e)*VTSTR + 2*slot, where the keys of 16-key chunk cc are
 // stored in the order the P registers hold them: slots 16cc + 8h + 0..3 hold keys
 // 16cc + 4h + 0..3 and slots 16cc + 8h + 4..7 hold keys 16cc + 8 + 4h + 0..3.
-template <int D>
+template <int VTSTR>
 __device__ __forceinline__ void store_vt_block(char* dst, int kg, int dq, const u32x2* r)
 {
     const int cc = kg >> 2, x = kg & 3;
@@ -174,7 +189,7 @@ __device__ __forceinline__ void store_vt_block(char* dst, int kg, int dq, const 
             w.x = (a0 & 0xffffu) | (a1 << 16);
             w.y = (a2 & 0xffffu) | (a3 << 16);
         }
-        *reinterpret_cast<u32x2*>(dst + (4 * dq + e) * Tile16<D>::VTSTR + 2 * slot) = w;
+        *reinterpret_cast<u32x2*>(dst + (4 * dq + e) * VTSTR + 2 * slot) = w;
     }
 }
 
@@ -226,7 +241,7 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     for (int i = 0; i < P::KPW; ++i)
         ksrc[i] = dma_src<D>(wave + P::NW * i, lane, P::KSTR);
     auto stage_k = [&](int tile, int lds_off) {
-        stage_tile<D, P::KNB, P::KPW>(Kh, tile, Nk, smem + lds_off, wave, ksrc);
+        stage_tile<D, P::KNB, P::KPW, P::NW>(Kh, tile, Nk, smem + lds_off, wave, ksrc);
     };
     // ---- V staging through registers: this thread's 4-key x 4-dim block.  Within a
     // 32-lane half-wave the blocks cover 4 consecutive dim-quads x 8 key groups, which
@@ -251,7 +266,7 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     if (1 < nkt)
         stage_k(1, P::K1);
     if (0 < nkt)
-        store_vt_block<D>(smem + P::V0, v_kg, v_dq, vreg);
+        store_vt_block<P::VTSTR>(smem + P::V0, v_kg, v_dq, vreg);
     if (1 < nkt)
         load_v_block<D>(Vh, 1, Nk, v_kg, v_dq, vreg);  // written to LDS during step 0
     // Q (B operand of S^T = K Q^T): lane supplies Q[my_q][16c + 8hh .. +8]
@@ -284,7 +299,8 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     for (int db = 0; db < P::DB; ++db)
         o[db] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     float m2 = neg_inf();
-    float l = 0.f;
+    float l = 0.f;   // this half's sum of the fp32 P (for L)
+    float lr = 0.f;  // this half's sum of the rounded P (for the normalisation of O)
 
     // mask tile j: keys key0 + 4hh + off (off = 32kb + 8(r/4) + r%4) past the end of
     // the keys or (causal) after the query become -inf
@@ -306,12 +322,13 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
         return (key0 + P::BC > Nk) || (CAUSAL && key0 + P::BC - 1 > qw0);
     };
 
-    // Running-max update of the online softmax.  O~ and l are rescaled by
-    // alpha = 2^(m2 - m_new) only when some row of the wave raised its max (else
-    // alpha = 1 exactly and the 64 multiplies are skipped).  The reference is always
-    // the exact running max: the dominant key of a row then gets p = 1, which the
-    // rounding of P to bf16/fp16 keeps exact (a stale reference, even by a few
-    // units, measurably loses accuracy on rows dominated by one key).
+    // Running-max update with a lazy reference: m2 (and with it O~, l, lr, rescaled
+    // by alpha = 2^(m2 - m_new)) only moves when some row of the wave sees its max
+    // exceed m2 by more than kSlack, so P <= 2^kSlack and the 64-multiply rescale is
+    // rare.  Any reference gives the same softmax: L = m2 + log2(sum P) uses the fp32
+    // sum, and O is divided by the sum of the SAME rounded P that went into the P.V
+    // MFMAs, which keeps a row dominated by one key exact whatever that key's P is.
+    constexpr float kSlack = 8.0f;
     auto update_max = [&](f32x16* s) {
         float mx = s[0][0];
 #pragma unroll
@@ -321,20 +338,21 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                 mx = fmaxf(mx, s[kb][r]);
         mx = fmaxf(mx, swap_halves(mx));
         const float m_new = fmaxf(m2, mx * c2);  // c2 > 0: max commutes with the scale
-        if (__builtin_amdgcn_ballot_w64(m_new > m2) != 0) {
+        if (__builtin_amdgcn_ballot_w64(m_new > m2 + kSlack) != 0) {
             const float alpha = exp2_fast(m2 - m_new);  // 0 on the first tile (m2 = -inf)
 #pragma unroll
             for (int db = 0; db < P::DB; ++db)
                 o[db] *= alpha;
             l *= alpha;
+            lr *= alpha;
             m2 = m_new;
         }
     };
 
-    // P = 2^(s c2 - m2) in fp32, summed into l (four independent chains), then
-    // rounded to T and packed in the MFMA B-operand order: chunk cc = 2kb + h holds
-    // registers 8h .. 8h+7 of block kb.  A row with no visible key so far (m2 = -inf)
-    // gets p = 0.
+    // P = 2^(s c2 - m2) in fp32, summed into l (four independent chains); rounded to
+    // T and packed in the MFMA B-operand order (chunk cc = 2kb + h holds registers
+    // 8h .. 8h+7 of block kb); the rounded values summed into lr with v_dot2.  A row
+    // with no visible key so far (m2 = -inf) gets p = 0.
     auto exp_sum_pack = [&](f32x16* s, vec* pb) {
         const float mneg = (m2 == neg_inf()) ? 0.f : -m2;
         float rs[4] = {0.f, 0.f, 0.f, 0.f};
@@ -347,6 +365,15 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                 pb[cc][e] = (T)p;
             }
         l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+        float rr[2] = {0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            const u32x4 w = __builtin_bit_cast(u32x4, pb[cc]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                rr[e & 1] = M::dot_ones(w[e], rr[e & 1]);
+        }
+        lr += rr[0] + rr[1];
     };
 
     // O^T += V^T P^T from the V^T buffer at vb_off
@@ -372,26 +399,20 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     // and the S MFMAs of tile j+1 (K buffer kn, into s_nxt); then V_{j+1} (in
     // registers since the last step) is written to the other V^T buffer vn, the
     // barrier publishes it together with K_{j+2} (DMA issued one step ago), and the
-    // next loads go out: V_{j+2} into registers, K_{j+3} into kn.  In the common
-    // case (tile j unmasked, tile j+1 live) the S MFMAs, the exponentials and the
-    // P.V MFMAs form one basic block so that MFMA and VALU work interleave.
+    // next loads go out: V_{j+2} into registers, K_{j+3} into kn.
     auto step = [&](int j, f32x16* s_cur, f32x16* s_nxt, int kn, int vc, int vn) {
         if (j < n_w) {
+            if (j + 1 < n_w)
+                scores(kn, s_nxt);
             if (needs_mask(j))
                 mask_tile(j, s_cur);
             update_max(s_cur);
             vec pb[4];
-            if (j + 1 < n_w) {
-                scores(kn, s_nxt);
-                exp_sum_pack(s_cur, pb);
-                pv(pb, vc);
-            } else {
-                exp_sum_pack(s_cur, pb);
-                pv(pb, vc);
-            }
+            exp_sum_pack(s_cur, pb);
+            pv(pb, vc);
         }
         if (j + 1 < nkt)
-            store_vt_block<D>(smem + vn, v_kg, v_dq, vreg);
+            store_vt_block<P::VTSTR>(smem + vn, v_kg, v_dq, vreg);
         __syncthreads();
         if (j + 2 < nkt)
             load_v_block<D>(Vh, j + 2, Nk, v_kg, v_dq, vreg);
@@ -409,8 +430,9 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 
     // ---- epilogue: O = O~ / l (rounded to T, nearest-even), L = ln2 * (m2 + log2 l)
     const float lt = l + swap_halves(l);
+    const float lrt = lr + swap_halves(lr);
     if (my_q < Nq) {
-        const float inv = 1.0f / lt;
+        const float inv = 1.0f / lrt;
         T* orow = O + ((size_t)bh * Nq + my_q) * D;
 #pragma unroll
         for (int db = 0; db < P::DB; ++db)
