@@ -75,6 +75,78 @@ def committed_traffic(workload: str):
         return None
 
 
+def read_sclk_mhz():
+    """Current shader clock of GPU 0 in MHz from rocm-smi (None if unavailable)."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for line in r.stdout.splitlines():
+        m = re.search(r"GPU\[0\].*sclk clock level:.*\((\d+)\s*Mhz\)", line)
+        if m:
+            return float(m.group(1))
+    return None
+
+
+def sclk_under(step_fn, seconds: float = 1.5):
+    """Median shader clock (MHz) sampled while step_fn runs back to back."""
+    import statistics
+    import threading
+
+    import torch
+    stop = threading.Event()
+
+    def spin():
+        while not stop.is_set():
+            for _ in range(16):
+                step_fn()
+            torch.cuda.synchronize()
+
+    th = threading.Thread(target=spin)
+    th.start()
+    samples = []
+    try:
+        time.sleep(0.5)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            v = read_sclk_mhz()
+            if v is None:
+                break
+            samples.append(v)
+    finally:
+        stop.set()
+        th.join()
+    return statistics.median(samples) if samples else None
+
+
+def gemm_ceiling(dev, settle_s: float):
+    """hipBLASLt bf16 GEMM (torch.mm, 8192^3) on N(0,1) data: the dense-MFMA rate this
+    GPU sustains on random operands, with its clock; context for the roofline."""
+    import torch
+    n = 8192
+    g = torch.Generator(device=dev).manual_seed(1234)
+    a = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    mm = lambda: torch.mm(a, b, out=c)  # noqa: E731
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        mm()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 50
+    e0.record()
+    for _ in range(reps):
+        mm()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"what": "torch.mm bf16 8192x8192x8192, N(0,1) operands (hipBLASLt)",
+            "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1), "sclk_mhz": sclk_under(mm, 1.0)}
+
+
 def to_device(a, dtype, dev):
     import numpy as np
     import torch
@@ -127,6 +199,8 @@ def main() -> int:
     ap.add_argument("--workload", default="self_8k_causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="oracle seconds (wall)")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip the sclk readings and the GEMM ceiling run")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 3 plain device copies of MIB MiB "
                          "(reference dispatches for scaling HBM byte counters)")
@@ -194,6 +268,21 @@ def main() -> int:
     traffic = committed_traffic(w.name)
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic}
+    if not args.no_clocks:
+        # the same rate against 256 CUs x 4096 flop/clk at the clock measured while
+        # this kernel runs, and the GEMM rate this GPU reaches on random data
+        sclk = sclk_under(step)
+        if sclk:
+            at = 256 * 4096 * sclk * 1e6 / 1e12 if w.dtype != "f32" else None
+            roofline["sclk_mhz"] = sclk
+            if at:
+                roofline["peak_at_sclk"] = round(at, 1)
+                roofline["frac_at_sclk"] = round(tflops / at, 4)
+        if w.dtype != "f32":
+            ceil = gemm_ceiling(dev, args.settle)
+            roofline["gemm_reference"] = ceil
+            log(f"[bench] sclk {sclk} MHz under fa_fwd; {ceil['what']}: {ceil['tflops']} TFLOP/s "
+                f"at {ceil['sclk_mhz']} MHz")
 
     cpu = None
     if not args.no_cpu_baseline:

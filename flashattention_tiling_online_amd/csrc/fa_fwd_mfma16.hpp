@@ -41,8 +41,7 @@
 //   * exp is exp2 with scale*log2(e) folded into one FMA; the running-max reference
 //     moves (with the O~ rescale) only when a row's max exceeds it by more than 2^8;
 //     L takes the fp32 row sum of P, O the row sum of the rounded P it was built
-//     from (see update_max);
-//   * waves that share a SIMD run each step in opposite orders (ping-pong).
+//     from (see update_max).
 #pragma once
 
 #include "fa_common.hpp"
@@ -302,8 +301,11 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     float l = 0.f;   // this half's sum of the fp32 P (for L)
     float lr = 0.f;  // this half's sum of the rounded P (for the normalisation of O)
 
-    // mask tile j: keys key0 + 4hh + off (off = 32kb + 8(r/4) + r%4) past the end of
-    // the keys or (causal) after the query become -inf
+    // Mask tile j: keys key0 + 4hh + off (off = 32kb + 8(r/4) + r%4) past the end of
+    // the keys or (causal) after the query become -inf.  Only a wave's last tile can
+    // need it: the wave's first query qw0 is a multiple of 32 and its last tile is
+    // the one holding key min(qw0 + 31, Nq - 1) (or the last key), so every earlier
+    // 64-key tile ends before qw0; the ragged end of the keys is the last tile.
     auto mask_tile = [&](int j, f32x16* s) {
         const int key0 = j * P::BC;
         const int last = CAUSAL ? min(Nk - 1, my_q) : Nk - 1;
@@ -323,22 +325,27 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     };
 
     // Running-max update with a lazy reference: m2 (and with it O~, l, lr, rescaled
-    // by alpha = 2^(m2 - m_new)) only moves when some row of the wave sees its max
-    // exceed m2 by more than kSlack, so P <= 2^kSlack and the 64-multiply rescale is
-    // rare.  Any reference gives the same softmax: L = m2 + log2(sum P) uses the fp32
-    // sum, and O is divided by the sum of the SAME rounded P that went into the P.V
-    // MFMAs, which keeps a row dominated by one key exact whatever that key's P is.
+    // by alpha = 2^(m2 - m_new)) only moves when some lane of the wave sees its half
+    // of a row exceed m2 by more than kSlack, so P <= 2^kSlack and the 64-multiply
+    // rescale is rare.  The halves' maxima are exchanged only then: m2 is the same in
+    // both halves of a row because it is only ever set from the whole row's max.
+    // Any reference gives the same softmax: L = m2 + log2(sum P) uses the fp32 sum,
+    // and O is divided by the sum of the SAME rounded P that went into the P.V MFMAs,
+    // which keeps a row dominated by one key exact whatever that key's P is.
     constexpr float kSlack = 8.0f;
-    auto update_max = [&](f32x16* s) {
+    auto half_max = [&](const f32x16* s) {
         float mx = s[0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 mx = fmaxf(mx, s[kb][r]);
-        mx = fmaxf(mx, swap_halves(mx));
-        const float m_new = fmaxf(m2, mx * c2);  // c2 > 0: max commutes with the scale
-        if (__builtin_amdgcn_ballot_w64(m_new > m2 + kSlack) != 0) {
+        return mx;
+    };
+    auto update_max = [&](float mx) {
+        const float mh = mx * c2;  // c2 > 0: max commutes with the scale
+        if (__builtin_amdgcn_ballot_w64(mh > m2 + kSlack) != 0) {
+            const float m_new = fmaxf(m2, fmaxf(mh, swap_halves(mh)));
             const float alpha = exp2_fast(m2 - m_new);  // 0 on the first tile (m2 = -inf)
 #pragma unroll
             for (int db = 0; db < P::DB; ++db)
@@ -389,24 +396,38 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 
     __syncthreads();  // waits for this wave's DMA (vmcnt), publishes K_0, K_1 and V_0
     f32x16 sa[2], sb[2];
-    if (0 < n_w)
+    float ma = 0.f, mb = 0.f;  // half-row maxima of the scores in sa / sb
+    if (0 < n_w) {
         scores(P::K0, sa);
+        ma = half_max(sa);
+    }
     __syncthreads();  // every wave has read K_0
     if (2 < nkt)
         stage_k(2, P::K0);
 
-    // One pipelined step: softmax + P.V of tile j (scores in s_cur, V^T buffer vc)
-    // and the S MFMAs of tile j+1 (K buffer kn, into s_nxt); then V_{j+1} (in
-    // registers since the last step) is written to the other V^T buffer vn, the
-    // barrier publishes it together with K_{j+2} (DMA issued one step ago), and the
-    // next loads go out: V_{j+2} into registers, K_{j+3} into kn.
-    auto step = [&](int j, f32x16* s_cur, f32x16* s_nxt, int kn, int vc, int vn) {
-        if (j < n_w) {
-            if (j + 1 < n_w)
-                scores(kn, s_nxt);
-            if (needs_mask(j))
+    // One pipelined step: the reference check for tile j (scores in s_cur, their
+    // half-row max in m_cur), then, as one branch-free block, the S MFMAs of tile j+1
+    // (K buffer kn, into s_nxt) and their max, together with the softmax and P.V
+    // MFMAs of tile j (V^T buffer vc); a wave's last tile is masked if it needs it
+    // and has no next tile.  Then V_{j+1} (in registers since the last step) is
+    // written to the other V^T buffer vn, the barrier publishes it together with
+    // K_{j+2} (DMA issued one step ago), and the next loads go out: V_{j+2} into
+    // registers, K_{j+3} into kn.
+    auto step = [&](int j, f32x16* s_cur, f32x16* s_nxt, float& m_cur, float& m_nxt, int kn,
+                    int vc, int vn) {
+        if (j + 1 < n_w) {
+            update_max(m_cur);
+            scores(kn, s_nxt);
+            vec pb[4];
+            exp_sum_pack(s_cur, pb);
+            pv(pb, vc);
+            m_nxt = half_max(s_nxt);
+        } else if (j < n_w) {
+            if (needs_mask(j)) {
                 mask_tile(j, s_cur);
-            update_max(s_cur);
+                m_cur = half_max(s_cur);
+            }
+            update_max(m_cur);
             vec pb[4];
             exp_sum_pack(s_cur, pb);
             pv(pb, vc);
@@ -420,9 +441,9 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
             stage_k(j + 3, kn);
     };
     for (int j = 0; j < nkt; j += 2) {
-        step(j, sa, sb, P::K1, P::V0, P::V1);
+        step(j, sa, sb, ma, mb, P::K1, P::V0, P::V1);
         if (j + 1 < nkt)
-            step(j + 1, sb, sa, P::K0, P::V1, P::V0);
+            step(j + 1, sb, sa, mb, ma, P::K0, P::V1, P::V0);
     }
 
     if (!wave_active)
