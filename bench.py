@@ -198,6 +198,9 @@ def main() -> int:
                          "the GPU clocks reach their steady state")
     ap.add_argument("--workload", default="self_8k_causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--splits", type=int, default=None, metavar="N",
+                    help="time fa_fwd_split with N key ranges (0: fa_split_hint's count) "
+                         "instead of fa_fwd; a step is then both kernels (ranges + merge)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="oracle seconds (wall)")
     ap.add_argument("--no-clocks", action="store_true",
                     help="skip the sclk readings and the GEMM ceiling run")
@@ -235,9 +238,20 @@ def main() -> int:
     o = torch.empty_like(tq)
     lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    splits = None
+    if args.splits is not None:
+        code = {"bf16": fa.FA_DTYPE_BF16, "f16": fa.FA_DTYPE_F16, "f32": fa.FA_DTYPE_F32}[w.dtype]
+        splits = args.splits or max(1, fa.fa_split_hint(w.B, w.H, w.Nq, w.Nk, w.d, w.causal, code))
+        ws = torch.empty(max(16, fa.fa_fwd_split_workspace(w.B, w.H, w.Nq, w.d, splits)),
+                         dtype=torch.uint8, device=dev)
+        log(f"[bench] fa_fwd_split with {splits} key ranges requested")
 
-    def step():
-        fa.fa_fwd(tq, tk, tv, causal=w.causal, scale=w.scale, o=o, lse=lse, stream=stream)
+        def step():
+            fa.fa_fwd_split(tq, tk, tv, causal=w.causal, scale=w.scale, n_splits=splits, o=o,
+                            lse=lse, workspace=ws, stream=stream)
+    else:
+        def step():
+            fa.fa_fwd(tq, tk, tv, causal=w.causal, scale=w.scale, o=o, lse=lse, stream=stream)
 
     settled = 0
     t_settle = time.perf_counter()
@@ -306,6 +320,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
                    "causal": w.causal, "scale": "1/sqrt(d)",
+                   "entry": "fa_fwd" if splits is None else f"fa_fwd_split(n_splits={splits})",
                    "inputs": f"N(0,{w.sigma_q:g}^2) Q, N(0,{w.sigma_k:g}^2) K, "
                              f"N(0,{w.sigma_v:g}^2) V, seeded"},
         "roofline": roofline,

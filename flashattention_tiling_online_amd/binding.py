@@ -17,14 +17,15 @@ FA_DTYPE_F32, FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH = 0, 1, 2, 3
 
 # symbols include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_status_str", "fa_tile_rows")
+EXPORTS = ("fa_fwd", "fa_fwd_split", "fa_fwd_split_workspace", "fa_merge", "fa_split_hint",
+           "fa_status_str", "fa_tile_rows")
 
 _lib = None
 
 
 class FAError(RuntimeError):
     def __init__(self, status: int):
-        super().__init__(f"fa_fwd failed: {fa_status_str(status)} ({status})")
+        super().__init__(f"libfa call failed: {fa_status_str(status)} ({status})")
         self.status = status
 
 
@@ -45,6 +46,16 @@ def lib() -> ctypes.CDLL:
         L.fa_status_str.restype = ctypes.c_char_p
         L.fa_tile_rows.argtypes = [ctypes.c_int, i64, ctypes.c_int]
         L.fa_tile_rows.restype = ctypes.c_int
+        L.fa_fwd_split.argtypes = L.fa_fwd.argtypes[:-1] + [ctypes.c_int, ctypes.c_void_p, i64,
+                                                            ctypes.c_void_p]
+        L.fa_fwd_split.restype = ctypes.c_int
+        L.fa_fwd_split_workspace.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+        L.fa_fwd_split_workspace.restype = i64
+        L.fa_merge.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, i64, i64, i64, i64,
+                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        L.fa_merge.restype = ctypes.c_int
+        L.fa_split_hint.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+        L.fa_split_hint.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -64,6 +75,29 @@ def fa_fwd_raw(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int
                         int(dtype), stream)
 
 
+def fa_fwd_split_raw(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int, Nk: int,
+                     d: int, causal: int, scale: float, dtype: int, n_splits: int,
+                     workspace: int, workspace_bytes: int, stream: int) -> int:
+    """Direct call of fa_fwd_split with integer device pointers; returns the status code."""
+    return lib().fa_fwd_split(q, k, v, o, lse, B, H, Nq, Nk, d, int(causal), float(scale),
+                              int(dtype), int(n_splits), workspace, int(workspace_bytes), stream)
+
+
+def fa_merge_raw(o_parts: int, lse_parts: int, n_parts: int, B: int, H: int, Nq: int, d: int,
+                 o: int, lse: int, dtype: int, stream: int) -> int:
+    """Direct call of fa_merge with integer device pointers; returns the status code."""
+    return lib().fa_merge(o_parts, lse_parts, int(n_parts), B, H, Nq, d, o, lse, int(dtype),
+                          stream)
+
+
+def fa_fwd_split_workspace(B: int, H: int, Nq: int, d: int, n_splits: int) -> int:
+    return lib().fa_fwd_split_workspace(B, H, Nq, d, int(n_splits))
+
+
+def fa_split_hint(B: int, H: int, Nq: int, Nk: int, d: int, causal: bool, dtype: int) -> int:
+    return lib().fa_split_hint(B, H, Nq, Nk, d, int(bool(causal)), int(dtype))
+
+
 def _dtype_code(t) -> int:
     import torch
     codes = {torch.float32: FA_DTYPE_F32, torch.float16: FA_DTYPE_F16,
@@ -71,6 +105,77 @@ def _dtype_code(t) -> int:
     if t.dtype not in codes:
         raise TypeError(f"unsupported dtype {t.dtype}")
     return codes[t.dtype]
+
+
+def _check_qkv(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-D GPU tensor [B,H,N,d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != (B, H, Nk, d):
+        raise ValueError("k and v must be [B,H,Nk,d] with q's B, H and d")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share a dtype")
+    return B, H, Nq, Nk, d
+
+
+def fa_fwd_split(q, k, v, causal: bool = False, scale: float | None = None, n_splits=None,
+                 o=None, lse=None, workspace=None, stream=None):
+    """fa_fwd computed over key ranges and merged (fa_fwd_split).
+
+    n_splits defaults to fa_split_hint(...).  The fp32 workspace for the partial
+    states is allocated with torch when not given (a uint8 GPU tensor of at least
+    fa_fwd_split_workspace(...) bytes may be passed instead).
+    """
+    import torch
+    B, H, Nq, Nk, d = _check_qkv(q, k, v)
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if n_splits is None:
+        n_splits = max(1, fa_split_hint(B, H, Nq, Nk, d, causal, code))
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    need = fa_fwd_split_workspace(B, H, Nq, d, n_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_fwd_split_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          B, H, Nq, Nk, d, int(bool(causal)), scale, code, n_splits,
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          stream.cuda_stream)
+    if st != FA_OK:
+        raise FAError(st)
+    return o, lse
+
+
+def fa_merge(o_parts, lse_parts, dtype=None, o=None, lse=None, stream=None):
+    """Fold partial states o_parts [P,B,H,Nq,d], lse_parts [P,B,H,Nq] (fp32 GPU tensors)
+    into (o [B,H,Nq,d] of ``dtype``, lse [B,H,Nq] fp32) with fa_merge."""
+    import torch
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise TypeError("o_parts and lse_parts must be float32")
+    if not (o_parts.is_cuda and lse_parts.is_cuda and o_parts.is_contiguous()
+            and lse_parts.is_contiguous() and o_parts.dim() == 5
+            and lse_parts.shape == o_parts.shape[:4]):
+        raise ValueError("o_parts must be [P,B,H,Nq,d] and lse_parts [P,B,H,Nq], contiguous GPU")
+    P, B, H, Nq, d = o_parts.shape
+    dtype = dtype or torch.bfloat16
+    if o is None:
+        o = torch.empty((B, H, Nq, d), dtype=dtype, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=o_parts.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(o_parts.device)
+    st = fa_merge_raw(o_parts.data_ptr(), lse_parts.data_ptr(), P, B, H, Nq, d, o.data_ptr(),
+                      lse.data_ptr(), _dtype_code(o), stream.cuda_stream)
+    if st != FA_OK:
+        raise FAError(st)
+    return o, lse
 
 
 def fa_fwd(q, k, v, causal: bool = False, scale: float | None = None, o=None, lse=None,
@@ -81,15 +186,7 @@ def fa_fwd(q, k, v, causal: bool = False, scale: float | None = None, o=None, ls
     ``stream`` (default: torch's current stream) and the call returns at once.
     """
     import torch
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
-            raise ValueError(f"{name} must be a contiguous 4-D GPU tensor [B,H,N,d]")
-    B, H, Nq, d = q.shape
-    Nk = k.shape[2]
-    if k.shape != (B, H, Nk, d) or v.shape != (B, H, Nk, d):
-        raise ValueError("k and v must be [B,H,Nk,d] with q's B, H and d")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise TypeError("q, k and v must share a dtype")
+    B, H, Nq, Nk, d = _check_qkv(q, k, v)
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)

@@ -11,8 +11,13 @@
 #include "../../include/fa.h"
 #include "fa_fwd_f32.hpp"
 #include "fa_fwd_mfma16.hpp"
+#include "fa_merge.hpp"
 
 namespace {
+
+constexpr int kKeyTile = 64;     // keys per tile in every kernel (the split granularity)
+constexpr int kMaxSplits = 256;  // most key ranges fa_fwd_split accepts
+constexpr int64_t kAlign = 256;  // alignment of the partial-L block in the workspace
 
 struct Launch {
     const void* fn;  // device function address
@@ -20,64 +25,101 @@ struct Launch {
     int threads;     // threads per workgroup
 };
 
-template <typename T, int D, bool C>
+template <typename T, int D, bool C, bool S>
 Launch mfma16()
 {
-    return Launch{reinterpret_cast<const void*>(&fa::fa_fwd_mfma16_kernel<T, D, C>),
+    return Launch{reinterpret_cast<const void*>(&fa::fa_fwd_mfma16_kernel<T, D, C, S>),
                   fa::Tile16<D>::BR, fa::Tile16<D>::NT};
 }
 
-template <int D, bool C>
+template <int D, bool C, bool S>
 Launch f32()
 {
-    return Launch{reinterpret_cast<const void*>(&fa::fa_fwd_f32_kernel<D, C>), fa::TileF32<D>::BR,
-                  fa::TileF32<D>::NT};
+    return Launch{reinterpret_cast<const void*>(&fa::fa_fwd_f32_kernel<D, C, S>),
+                  fa::TileF32<D>::BR, fa::TileF32<D>::NT};
 }
 
-bool pick(fa_dtype_t dtype, int64_t d, int causal, Launch* out)
+template <typename T, bool S>
+Launch mfma16_of(int64_t d, bool c)
+{
+    return d == 128 ? (c ? mfma16<T, 128, true, S>() : mfma16<T, 128, false, S>())
+                    : (c ? mfma16<T, 64, true, S>() : mfma16<T, 64, false, S>());
+}
+
+template <bool S>
+Launch f32_of(int64_t d, bool c)
+{
+    return d == 128 ? (c ? f32<128, true, S>() : f32<128, false, S>())
+                    : (c ? f32<64, true, S>() : f32<64, false, S>());
+}
+
+bool pick(fa_dtype_t dtype, int64_t d, int causal, bool split, Launch* out)
 {
     const bool c = causal != 0;
     if (d != 64 && d != 128)
         return false;
-    const bool d128 = d == 128;
     switch (dtype) {
     case FA_DTYPE_BF16:
-        *out = d128 ? (c ? mfma16<__bf16, 128, true>() : mfma16<__bf16, 128, false>())
-                    : (c ? mfma16<__bf16, 64, true>() : mfma16<__bf16, 64, false>());
+        *out = split ? mfma16_of<__bf16, true>(d, c) : mfma16_of<__bf16, false>(d, c);
         return true;
     case FA_DTYPE_F16:
-        *out = d128 ? (c ? mfma16<_Float16, 128, true>() : mfma16<_Float16, 128, false>())
-                    : (c ? mfma16<_Float16, 64, true>() : mfma16<_Float16, 64, false>());
+        *out = split ? mfma16_of<_Float16, true>(d, c) : mfma16_of<_Float16, false>(d, c);
         return true;
     case FA_DTYPE_F32:
-        *out = d128 ? (c ? f32<128, true>() : f32<128, false>())
-                    : (c ? f32<64, true>() : f32<64, false>());
+        *out = split ? f32_of<true>(d, c) : f32_of<false>(d, c);
         return true;
     }
     return false;
 }
 
+// Workgroups of the forward kernel that one CU holds at once (register and LDS
+// budgets of the kernels above): used only by fa_split_hint.
+int wgs_per_cu(fa_dtype_t dtype, int64_t d) { return d == 64 ? 2 : 1; }
+
+const void* merge_fn(fa_dtype_t dtype, int64_t d)
+{
+    switch (dtype) {
+    case FA_DTYPE_BF16:
+        return d == 128 ? reinterpret_cast<const void*>(&fa::fa_merge_kernel<__bf16, 128>)
+                        : reinterpret_cast<const void*>(&fa::fa_merge_kernel<__bf16, 64>);
+    case FA_DTYPE_F16:
+        return d == 128 ? reinterpret_cast<const void*>(&fa::fa_merge_kernel<_Float16, 128>)
+                        : reinterpret_cast<const void*>(&fa::fa_merge_kernel<_Float16, 64>);
+    case FA_DTYPE_F32:
+        return d == 128 ? reinterpret_cast<const void*>(&fa::fa_merge_kernel<float, 128>)
+                        : reinterpret_cast<const void*>(&fa::fa_merge_kernel<float, 64>);
+    }
+    return nullptr;
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-}  // namespace
-
-extern "C" fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
-                              float scale, fa_dtype_t dtype, fa_stream_t stream)
+bool valid_dtype(fa_dtype_t dtype)
 {
+    return dtype == FA_DTYPE_F32 || dtype == FA_DTYPE_F16 || dtype == FA_DTYPE_BF16;
+}
+
+// Checks shared by fa_fwd and fa_fwd_split, in the documented order; *empty is set
+// when there is nothing to compute.
+fa_status_t check_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                      int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal, float scale,
+                      fa_dtype_t dtype, bool split, Launch* L, bool* empty)
+{
+    *empty = false;
     if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
         return FA_ERR_INVALID_ARG;
-    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+    if (!valid_dtype(dtype))
         return FA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1)
         return FA_ERR_INVALID_ARG;
     if (!(scale > 0.0f) || !isfinite(scale))
         return FA_ERR_INVALID_ARG;
-    Launch L;
-    if (!pick(dtype, d, causal, &L))
+    if (!pick(dtype, d, causal, split, L))
         return FA_ERR_UNSUPPORTED;
-    if (B == 0 || H == 0 || Nq == 0)
-        return FA_OK;  // nothing to compute: no buffer is touched, pointers may be null
+    if (B == 0 || H == 0 || Nq == 0) {
+        *empty = true;  // nothing to compute: no buffer is touched, pointers may be null
+        return FA_OK;
+    }
     if (!q || !k || !v || !o || !lse)
         return FA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
@@ -90,19 +132,199 @@ extern "C" fa_status_t fa_fwd(const void* q, const void* k, const void* v, void*
     const int64_t lim = INT32_MAX;
     if (Nq * d > lim || Nk * d > lim || B > lim || H > lim || B * H > lim)
         return FA_ERR_INVALID_ARG;
-    const int64_t n_qtiles = (Nq + L.rows - 1) / L.rows;
+    const int64_t n_qtiles = (Nq + L->rows - 1) / L->rows;
     if (n_qtiles * B * H > lim)
         return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
 
-    // exp(x) = 2^(x * log2 e): fold log2(e) into the scale once, in double
-    const float c2 = (float)((double)scale * 1.4426950408889634074);
-    int nq = (int)Nq, nk = (int)Nk, nt = (int)n_qtiles;
-    void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse,
-                    (void*)&nq, (void*)&nk, (void*)&nt, (void*)&c2};
-    const hipError_t err = hipLaunchKernel(L.fn, dim3((unsigned)(n_qtiles * B * H)),
-                                           dim3((unsigned)L.threads), args, 0,
-                                           reinterpret_cast<hipStream_t>(stream));
+// exp(x) = 2^(x * log2 e): fold log2(e) into the scale once, in double
+float scale_log2e(float scale) { return (float)((double)scale * 1.4426950408889634074); }
+
+template <typename T>
+hipError_t launch_fwd(const Launch& L, const void* q, const void* k, const void* v, void* o,
+                      float* lse, float* o_part, float* lse_part, int64_t BH, int64_t Nq,
+                      int64_t Nk, int n_splits, int split_tiles, float scale, hipStream_t stream)
+{
+    fa::FwdParams<T> prm;
+    prm.q = static_cast<const T*>(q);
+    prm.k = static_cast<const T*>(k);
+    prm.v = static_cast<const T*>(v);
+    prm.o = static_cast<T*>(o);
+    prm.lse = lse;
+    prm.o_part = o_part;
+    prm.lse_part = lse_part;
+    prm.Nq = (int)Nq;
+    prm.Nk = (int)Nk;
+    prm.n_qtiles = (int)((Nq + L.rows - 1) / L.rows);
+    prm.bh_count = (int)BH;
+    prm.n_splits = n_splits;
+    prm.split_tiles = split_tiles;
+    prm.c2 = scale_log2e(scale);
+    void* args[] = {(void*)&prm};
+    const int64_t grid = (int64_t)prm.n_qtiles * BH * n_splits;
+    return hipLaunchKernel(L.fn, dim3((unsigned)grid), dim3((unsigned)L.threads), args, 0, stream);
+}
+
+hipError_t launch_fwd_any(fa_dtype_t dtype, const Launch& L, const void* q, const void* k,
+                          const void* v, void* o, float* lse, float* o_part, float* lse_part,
+                          int64_t BH, int64_t Nq, int64_t Nk, int n_splits, int split_tiles,
+                          float scale, hipStream_t stream)
+{
+    switch (dtype) {
+    case FA_DTYPE_BF16:
+        return launch_fwd<__bf16>(L, q, k, v, o, lse, o_part, lse_part, BH, Nq, Nk, n_splits,
+                                  split_tiles, scale, stream);
+    case FA_DTYPE_F16:
+        return launch_fwd<_Float16>(L, q, k, v, o, lse, o_part, lse_part, BH, Nq, Nk, n_splits,
+                                    split_tiles, scale, stream);
+    default:
+        return launch_fwd<float>(L, q, k, v, o, lse, o_part, lse_part, BH, Nq, Nk, n_splits,
+                                 split_tiles, scale, stream);
+    }
+}
+
+hipError_t launch_merge(fa_dtype_t dtype, int64_t d, const float* o_part, const float* lse_part,
+                        int n_parts, int64_t rows, void* o, float* lse, hipStream_t stream)
+{
+    const int rpb = 256 / (int)(d / 4);
+    const int64_t grid = (rows + rpb - 1) / rpb;
+    int np = n_parts;
+    void* args[] = {(void*)&o_part, (void*)&lse_part, (void*)&np, (void*)&rows, (void*)&o,
+                    (void*)&lse};
+    return hipLaunchKernel(merge_fn(dtype, d), dim3((unsigned)grid), dim3(256), args, 0, stream);
+}
+
+// The key ranges fa_fwd_split uses for a requested count: ranges of whole 64-key
+// tiles, as equal as possible, none empty.  Returns the number of ranges and the
+// tiles per range.
+int split_plan(int64_t Nk, int n_splits, int* tiles_per_split)
+{
+    const int64_t nkt = (Nk + kKeyTile - 1) / kKeyTile;
+    const int64_t s = n_splits < nkt ? n_splits : nkt;
+    const int64_t tps = (nkt + s - 1) / s;
+    *tiles_per_split = (int)tps;
+    return (int)((nkt + tps - 1) / tps);
+}
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                              float scale, fa_dtype_t dtype, fa_stream_t stream)
+{
+    Launch L;
+    bool empty;
+    const fa_status_t st =
+        check_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, false, &L, &empty);
+    if (st != FA_OK || empty)
+        return st;
+    const hipError_t err = launch_fwd_any(dtype, L, q, k, v, o, lse, nullptr, nullptr, B * H, Nq,
+                                          Nk, 1, 0, scale, reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+extern "C" int64_t fa_fwd_split_workspace(int64_t B, int64_t H, int64_t Nq, int64_t d,
+                                          int n_splits)
+{
+    if (B < 0 || H < 0 || Nq < 0 || (d != 64 && d != 128) || n_splits < 1 ||
+        n_splits > kMaxSplits)
+        return -1;
+    const int64_t rows = B * H * Nq;
+    return round_up((int64_t)n_splits * rows * d * 4, kAlign) + (int64_t)n_splits * rows * 4;
+}
+
+extern "C" fa_status_t fa_fwd_split(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                    int64_t d, int causal, float scale, fa_dtype_t dtype,
+                                    int n_splits, void* workspace, int64_t workspace_bytes,
+                                    fa_stream_t stream)
+{
+    if (n_splits < 1 || n_splits > kMaxSplits)
+        return FA_ERR_INVALID_ARG;
+    Launch L;
+    bool empty;
+    const fa_status_t st =
+        check_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, true, &L, &empty);
+    if (st != FA_OK || empty)
+        return st;
+    int tps;
+    const int s_eff = split_plan(Nk, n_splits, &tps);
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    if (s_eff == 1) {  // one range: the unsplit kernel writes o and lse directly
+        Launch L1;
+        pick(dtype, d, causal, false, &L1);
+        const hipError_t err = launch_fwd_any(dtype, L1, q, k, v, o, lse, nullptr, nullptr, B * H,
+                                              Nq, Nk, 1, 0, scale, hs);
+        return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    }
+    const int64_t need = fa_fwd_split_workspace(B, H, Nq, d, n_splits);
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes < need)
+        return FA_ERR_INVALID_ARG;
+    const int64_t rows = B * H * Nq;
+    if ((int64_t)s_eff * ((Nq + L.rows - 1) / L.rows) * B * H > INT32_MAX ||
+        (rows + 7) / 8 > INT32_MAX)
+        return FA_ERR_INVALID_ARG;
+    float* o_part = static_cast<float*>(workspace);
+    float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                               round_up((int64_t)n_splits * rows * d * 4, kAlign));
+    hipError_t err = launch_fwd_any(dtype, L, q, k, v, nullptr, nullptr, o_part, lse_part, B * H,
+                                    Nq, Nk, s_eff, tps, scale, hs);
+    if (err != hipSuccess)
+        return FA_ERR_LAUNCH;
+    err = launch_merge(dtype, d, o_part, lse_part, s_eff, rows, o, lse, hs);
+    return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+extern "C" fa_status_t fa_merge(const float* o_parts, const float* lse_parts, int n_parts,
+                                int64_t B, int64_t H, int64_t Nq, int64_t d, void* o, float* lse,
+                                fa_dtype_t dtype, fa_stream_t stream)
+{
+    if (B < 0 || H < 0 || Nq < 0 || n_parts < 1)
+        return FA_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype))
+        return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128)
+        return FA_ERR_UNSUPPORTED;
+    const int64_t rows = B * H * Nq;
+    if (rows == 0)
+        return FA_OK;
+    if (!o_parts || !lse_parts || !o || !lse)
+        return FA_ERR_INVALID_ARG;
+    if (!aligned(o_parts, 16) || !aligned(lse_parts, 4) || !aligned(o, 16) || !aligned(lse, 4))
+        return FA_ERR_INVALID_ARG;
+    if ((rows + 7) / 8 > INT32_MAX)
+        return FA_ERR_INVALID_ARG;
+    const hipError_t err = launch_merge(dtype, d, o_parts, lse_parts, n_parts, rows, o, lse,
+                                        reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+extern "C" int fa_split_hint(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                             fa_dtype_t dtype)
+{
+    Launch L;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || (causal != 0 && causal != 1) ||
+        !pick(dtype, d, causal, false, &L))
+        return 0;
+    const int64_t cus = 256;
+    const int64_t slots = cus * wgs_per_cu(dtype, d);
+    const int64_t wgs = B * H * ((Nq + L.rows - 1) / L.rows);
+    if (wgs >= slots)
+        return 1;
+    // each range must keep enough key tiles to amortise its partial-state write and
+    // the merge launch: 8 for the 16-bit kernels, 2 for the slower fp32 one
+    const int64_t nkt = (Nk + kKeyTile - 1) / kKeyTile;
+    const int64_t min_tiles = dtype == FA_DTYPE_F32 ? 2 : 8;
+    int64_t s = (slots + wgs - 1) / wgs;
+    const int64_t most = nkt / min_tiles > 1 ? nkt / min_tiles : 1;
+    if (s > most)
+        s = most;
+    if (s > 16)
+        s = 16;
+    return (int)s;
 }
 
 extern "C" const char* fa_status_str(fa_status_t status)
@@ -121,5 +343,5 @@ extern "C" int fa_tile_rows(fa_dtype_t dtype, int64_t d, int causal)
     if (causal != 0 && causal != 1)
         return 0;
     Launch L;
-    return pick(dtype, d, causal, &L) ? L.rows : 0;
+    return pick(dtype, d, causal, false, &L) ? L.rows : 0;
 }

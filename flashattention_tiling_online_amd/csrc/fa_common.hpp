@@ -2,7 +2,10 @@
 //
 // Work decomposition: one workgroup per (batch*head, query tile), as in the
 // course page "05_flash_attention.py" (flash_attention_forward: each query block
-// is owned by one thread block and its state stays on chip).
+// is owned by one thread block and its state stays on chip) — or, split along the
+// keys, per (batch*head, key range, query tile), each range leaving a partial
+// (O, L) state that the merge kernel folds with the (+) operator of the blog page
+// "Flash Attention" in its log-sum-exp form.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,6 +38,24 @@ __device__ __forceinline__ int xcd_remap(int wg, int n)
     const int j = wg / kXcds;     // its rank among that XCD's workgroups
     return x * per + (x < rem ? x : rem) + j;
 }
+
+// Arguments of one forward launch.  q, o: [bh_count, Nq, D]; k, v: [bh_count, Nk, D];
+// lse: [bh_count, Nq].  With key splits (n_splits > 1) the workgroup for split s
+// covers key tiles [s * split_tiles, (s + 1) * split_tiles) and writes fp32 partials
+// o_part [n_splits, bh_count, Nq, D] and lse_part [n_splits, bh_count, Nq] instead
+// of o and lse.
+template <typename T>
+struct FwdParams {
+    const T* q;
+    const T* k;
+    const T* v;
+    T* o;
+    float* lse;
+    float* o_part;
+    float* lse_part;
+    int Nq, Nk, n_qtiles, bh_count, n_splits, split_tiles;
+    float c2;  // scale * log2(e)
+};
 
 // -inf as a float constant usable in device code
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }

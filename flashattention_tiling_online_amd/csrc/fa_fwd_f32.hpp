@@ -32,19 +32,21 @@ struct TileF32 {
     static constexpr int DB = D / 32;
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(256)
-void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
-                       const float* __restrict__ V, float* __restrict__ O,
-                       float* __restrict__ LSE, int Nq, int Nk, int n_qtiles, float c2)
+void fa_fwd_f32_kernel(const FwdParams<float> prm)
 {
     using P = TileF32<D>;
     __shared__ __attribute__((aligned(16))) float Ks[P::BC * P::KS];
     __shared__ __attribute__((aligned(16))) float Vs[P::BC * P::VS];
+    const int Nq = prm.Nq, Nk = prm.Nk, n_qtiles = prm.n_qtiles;
+    const float c2 = prm.c2;
 
     const int logical = xcd_remap((int)blockIdx.x, (int)gridDim.x);
-    const int bh = logical / n_qtiles;
-    int qt = logical - bh * n_qtiles;
+    const int rest = logical / n_qtiles;
+    int qt = logical - rest * n_qtiles;
+    const int split = SPLIT ? rest % prm.n_splits : 0;
+    const int bh = SPLIT ? rest / prm.n_splits : rest;
     if (CAUSAL)
         qt = n_qtiles - 1 - qt;
     const int q0 = qt * P::BR;
@@ -57,22 +59,29 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     const int qw0 = q0 + wave * 32;
     const int my_q = qw0 + ql;
 
-    const float* Qh = Q + (size_t)bh * Nq * D;
-    const float* Kh = K + (size_t)bh * Nk * D;
-    const float* Vh = V + (size_t)bh * Nk * D;
+    // key range [kbeg, kbeg + Nks) of the head; key positions below are relative
+    // to kbeg, and so are the queries' causal limits
+    const int kbeg = SPLIT ? split * prm.split_tiles * P::BC : 0;
+    const int Nks = SPLIT ? min(Nk - kbeg, prm.split_tiles * P::BC) : Nk;
+    const int qkw0 = qw0 - kbeg;
+    const int my_qk = my_q - kbeg;
+
+    const float* Qh = prm.q + (size_t)bh * Nq * D;
+    const float* Kh = prm.k + ((size_t)bh * Nk + kbeg) * D;
+    const float* Vh = prm.v + ((size_t)bh * Nk + kbeg) * D;
 
     float qf[D / 2];
 #pragma unroll
     for (int c = 0; c < D / 2; ++c)
         qf[c] = my_q < Nq ? Qh[(size_t)my_q * D + 2 * c + hh] : 0.f;
 
-    int nkt = (Nk + P::BC - 1) / P::BC;
+    int nkt = (Nks + P::BC - 1) / P::BC;
     if (CAUSAL) {
-        const int qlast = min(q0 + P::BR, Nq) - 1;
-        nkt = min(nkt, qlast / P::BC + 1);
+        const int qlast = min(q0 + P::BR, Nq) - 1 - kbeg;
+        nkt = qlast < 0 ? 0 : min(nkt, qlast / P::BC + 1);
     }
     const bool wave_active = qw0 < Nq;
-    const int qw_last = min(qw0 + 31, Nq - 1);
+    const int qw_last = min(qw0 + 31, Nq - 1) - kbeg;  // may be negative: no key visible
 
     f32x16 o[P::DB];
 #pragma unroll
@@ -91,7 +100,7 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
             const int d4 = f % (D / 4);
             const int gk = key0 + key;
             f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-            if (gk < Nk) {
+            if (gk < Nks) {
                 kv = *reinterpret_cast<const f32x4*>(Kh + (size_t)gk * D + 4 * d4);
                 vv = *reinterpret_cast<const f32x4*>(Vh + (size_t)gk * D + 4 * d4);
             }
@@ -115,14 +124,14 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                              qf[c], s[kb], 0, 0, 0);
         }
 
-        const bool need_mask = (key0 + P::BC > Nk) || (CAUSAL && key0 + P::BC - 1 > qw0);
+        const bool need_mask = (key0 + P::BC > Nks) || (CAUSAL && key0 + P::BC - 1 > qkw0);
         if (need_mask) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    if (key >= Nk || (CAUSAL && key > my_q))
+                    if (key >= Nks || (CAUSAL && key > my_qk))
                         s[kb][r] = neg_inf();
                 }
         }
@@ -167,10 +176,14 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 
     if (!wave_active)
         return;
+    // split: a row that saw no key of its range leaves the merge identity
+    // (L = -inf, O = 0)
     const float lt = l + swap_halves(l);
     if (my_q < Nq) {
-        const float inv = 1.0f / lt;
-        float* orow = O + ((size_t)bh * Nq + my_q) * D;
+        const size_t row = SPLIT ? ((size_t)split * prm.bh_count + bh) * Nq + my_q
+                                 : (size_t)bh * Nq + my_q;
+        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+        float* orow = (SPLIT ? prm.o_part : prm.o) + row * D;
 #pragma unroll
         for (int db = 0; db < P::DB; ++db)
 #pragma unroll
@@ -182,7 +195,8 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                 *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * a + 4 * hh) = w;
             }
         if (hh == 0)
-            LSE[(size_t)bh * Nq + my_q] = (m2 + log2_fast(lt)) * kLn2;
+            (SPLIT ? prm.lse_part : prm.lse)[row] =
+                lt > 0.f ? (m2 + log2_fast(lt)) * kLn2 : neg_inf();
     }
 }
 

@@ -192,11 +192,9 @@ __device__ __forceinline__ void store_vt_block(char* dst, int kg, int dq, const 
     }
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(Tile16<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
-void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
-                          const T* __restrict__ V, T* __restrict__ O, float* __restrict__ LSE,
-                          int Nq, int Nk, int n_qtiles, float c2)
+void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
 {
     using P = Tile16<D>;
     using M = Mfma16<T>;
@@ -204,11 +202,16 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     typedef T T4 __attribute__((ext_vector_type(4)));
     __shared__ __attribute__((aligned(1024))) char smem[P::LDS];
     const char* const sm = smem;
+    const int Nq = prm.Nq, Nk = prm.Nk, n_qtiles = prm.n_qtiles;
+    const float c2 = prm.c2;
 
-    // ---- which (batch*head, query tile) this workgroup owns
+    // ---- which (batch*head, key split, query tile) this workgroup owns; the
+    // query tiles of one (head, split) are consecutive, so they share an XCD's L2
     const int logical = xcd_remap((int)blockIdx.x, (int)gridDim.x);
-    const int bh = logical / n_qtiles;
-    int qt = logical - bh * n_qtiles;
+    const int rest = logical / n_qtiles;
+    int qt = logical - rest * n_qtiles;
+    const int split = SPLIT ? rest % prm.n_splits : 0;
+    const int bh = SPLIT ? rest / prm.n_splits : rest;
     if (CAUSAL)
         qt = n_qtiles - 1 - qt;  // longest rows (most key tiles) are dispatched first
     const int q0 = qt * P::BR;
@@ -221,18 +224,31 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     const int qw0 = q0 + wave * 32;
     const int my_q = qw0 + ql;
 
-    const T* Qh = Q + (size_t)bh * Nq * D;
-    const T* Kh = K + (size_t)bh * Nk * D;
-    const T* Vh = V + (size_t)bh * Nk * D;
+    // ---- key range: keys [kbeg, kbeg + Nks) of the head (all of them unless split);
+    // key tiles and positions below are relative to kbeg, so a query's causal limit
+    // is its index minus kbeg
+    const int kbeg = SPLIT ? split * prm.split_tiles * P::BC : 0;
+    const int Nks = SPLIT ? min(Nk - kbeg, prm.split_tiles * P::BC) : Nk;
+    const int qkw0 = qw0 - kbeg;   // first query of the wave, in key positions
+    const int my_qk = my_q - kbeg;
+
+    const T* Qh = prm.q + (size_t)bh * Nq * D;
+    const T* Kh = prm.k + ((size_t)bh * Nk + kbeg) * D;
+    const T* Vh = prm.v + ((size_t)bh * Nk + kbeg) * D;
 
     // ---- key tiles: the workgroup stages nkt of them; this wave computes n_w
-    int nkt = (Nk + P::BC - 1) / P::BC;
-    if (CAUSAL)
-        nkt = min(nkt, (min(q0 + P::BR, Nq) - 1) / P::BC + 1);
+    // (a query before the range sees none of its keys)
+    int nkt = (Nks + P::BC - 1) / P::BC;
+    if (CAUSAL) {
+        const int last = min(q0 + P::BR, Nq) - 1 - kbeg;
+        nkt = last < 0 ? 0 : min(nkt, last / P::BC + 1);
+    }
     const bool wave_active = qw0 < Nq;
     int n_w = wave_active ? nkt : 0;
-    if (CAUSAL && wave_active)
-        n_w = min(nkt, min(qw0 + 31, Nq - 1) / P::BC + 1);
+    if (CAUSAL && wave_active) {
+        const int last = min(qw0 + 31, Nq - 1) - kbeg;
+        n_w = last < 0 ? 0 : min(nkt, last / P::BC + 1);
+    }
 
     // ---- K staging by DMA: per-lane source offsets of this wave's blocks (fixed)
     int ksrc[P::KPW];
@@ -240,7 +256,7 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     for (int i = 0; i < P::KPW; ++i)
         ksrc[i] = dma_src<D>(wave + P::NW * i, lane, P::KSTR);
     auto stage_k = [&](int tile, int lds_off) {
-        stage_tile<D, P::KNB, P::KPW, P::NW>(Kh, tile, Nk, smem + lds_off, wave, ksrc);
+        stage_tile<D, P::KNB, P::KPW, P::NW>(Kh, tile, Nks, smem + lds_off, wave, ksrc);
     };
     // ---- V staging through registers: this thread's 4-key x 4-dim block.  Within a
     // 32-lane half-wave the blocks cover 4 consecutive dim-quads x 8 key groups, which
@@ -260,14 +276,14 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     // ---- prologue: tiles 0 and 1 in flight, Q fragment into registers
     if (0 < nkt) {
         stage_k(0, P::K0);
-        load_v_block<D>(Vh, 0, Nk, v_kg, v_dq, vreg);
+        load_v_block<D>(Vh, 0, Nks, v_kg, v_dq, vreg);
     }
     if (1 < nkt)
         stage_k(1, P::K1);
     if (0 < nkt)
         store_vt_block<P::VTSTR>(smem + P::V0, v_kg, v_dq, vreg);
     if (1 < nkt)
-        load_v_block<D>(Vh, 1, Nk, v_kg, v_dq, vreg);  // written to LDS during step 0
+        load_v_block<D>(Vh, 1, Nks, v_kg, v_dq, vreg);  // written to LDS during step 0
     // Q (B operand of S^T = K Q^T): lane supplies Q[my_q][16c + 8hh .. +8]
     vec qf[P::DC];
 #pragma unroll
@@ -308,7 +324,7 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     // 64-key tile ends before qw0; the ragged end of the keys is the last tile.
     auto mask_tile = [&](int j, f32x16* s) {
         const int key0 = j * P::BC;
-        const int last = CAUSAL ? min(Nk - 1, my_q) : Nk - 1;
+        const int last = CAUSAL ? min(Nks - 1, my_qk) : Nks - 1;
         const int lim = last - key0 - 4 * hh;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -321,7 +337,7 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     };
     auto needs_mask = [&](int j) {
         const int key0 = j * P::BC;
-        return (key0 + P::BC > Nk) || (CAUSAL && key0 + P::BC - 1 > qw0);
+        return (key0 + P::BC > Nks) || (CAUSAL && key0 + P::BC - 1 > qkw0);
     };
 
     // Running-max update with a lazy reference: m2 (and with it O~, l, lr, rescaled
@@ -436,7 +452,7 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
             store_vt_block<P::VTSTR>(smem + vn, v_kg, v_dq, vreg);
         __syncthreads();
         if (j + 2 < nkt)
-            load_v_block<D>(Vh, j + 2, Nk, v_kg, v_dq, vreg);
+            load_v_block<D>(Vh, j + 2, Nks, v_kg, v_dq, vreg);
         if (j + 3 < nkt)
             stage_k(j + 3, kn);
     };
@@ -449,24 +465,44 @@ void fa_fwd_mfma16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     if (!wave_active)
         return;  // no barrier follows
 
-    // ---- epilogue: O = O~ / l (rounded to T, nearest-even), L = ln2 * (m2 + log2 l)
+    // ---- epilogue: O = O~ / l (rounded to T, nearest-even), L = ln2 * (m2 + log2 l);
+    // split: O~ / l and L in fp32 into the partial buffers, and for a row that saw
+    // no key of its range the identity of the merge, L = -inf with O = 0
     const float lt = l + swap_halves(l);
     const float lrt = lr + swap_halves(lr);
     if (my_q < Nq) {
-        const float inv = 1.0f / lrt;
-        T* orow = O + ((size_t)bh * Nq + my_q) * D;
+        if (SPLIT) {
+            const size_t row = ((size_t)split * prm.bh_count + bh) * Nq + my_q;
+            const float inv = lrt > 0.f ? 1.0f / lrt : 0.f;
+            float* orow = prm.o_part + row * D;
 #pragma unroll
-        for (int db = 0; db < P::DB; ++db)
+            for (int db = 0; db < P::DB; ++db)
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                T4 w;
+                for (int a = 0; a < 4; ++a) {
+                    f32x4 w;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    w[e] = (T)(o[db][4 * a + e] * inv);
-                *reinterpret_cast<T4*>(orow + 32 * db + 8 * a + 4 * hh) = w;
-            }
-        if (hh == 0)
-            LSE[(size_t)bh * Nq + my_q] = (m2 + log2_fast(lt)) * kLn2;
+                    for (int e = 0; e < 4; ++e)
+                        w[e] = o[db][4 * a + e] * inv;
+                    *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * a + 4 * hh) = w;
+                }
+            if (hh == 0)
+                prm.lse_part[row] = lt > 0.f ? (m2 + log2_fast(lt)) * kLn2 : neg_inf();
+        } else {
+            const float inv = 1.0f / lrt;
+            T* orow = prm.o + ((size_t)bh * Nq + my_q) * D;
+#pragma unroll
+            for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    T4 w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        w[e] = (T)(o[db][4 * a + e] * inv);
+                    *reinterpret_cast<T4*>(orow + 32 * db + 8 * a + 4 * hh) = w;
+                }
+            if (hh == 0)
+                prm.lse[(size_t)bh * Nq + my_q] = (m2 + log2_fast(lt)) * kLn2;
+        }
     }
 }
 

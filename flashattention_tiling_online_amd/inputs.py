@@ -78,6 +78,10 @@ WORKLOADS = {
     "cross_1k_8k": Workload("cross_1k_8k", 4, 16, 1024, 8192, 128, "bf16", False, seed=405),
     "ctx_32k_causal": Workload("ctx_32k_causal", 1, 32, 32768, 32768, 128, "bf16", True,
                                sigma_q=3.0, sigma_k=3.0, sigma_v=1.0, seed=505),
+    # short query block against a long key/value sequence: the shape whose grid the
+    # unsplit kernel under-fills (32 workgroups), measured with the key-split path
+    "short_q_long_kv": Workload("short_q_long_kv", 4, 8, 256, 16384, 128, "bf16", False,
+                                seed=606),
 }
 
 # seed of the row sample drawn for the largest workloads

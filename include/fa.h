@@ -1,7 +1,7 @@
 /*
  * fa.h — C-ABI of the MI355X (gfx950) fused attention forward library, libfa.so.
  *
- * One entry point computes, for every batch b and head h,
+ * The entry points compute, for every batch b and head h,
  *
  *     S = scale * Q[b,h] K[b,h]^T            (Nq x Nk, never written to memory)
  *     S[q,k] = -inf where causal and k > q   (key k visible to query q iff k <= q)
@@ -86,6 +86,75 @@ typedef void* fa_stream_t;
 fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                    int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
                    float scale, fa_dtype_t dtype, fa_stream_t stream);
+
+/*
+ * fa_fwd_split — the same result as fa_fwd, computed over key ranges in parallel and
+ * merged; for grids that fa_fwd leaves under-filled (few heads, short query
+ * sequences, long key sequences).
+ *
+ * The keys are cut into ranges of whole 64-key tiles: with nkt = ceil(Nk / 64) tiles,
+ * s = min(n_splits, nkt) and t = ceil(nkt / s) tiles per range, range r covers keys
+ * [64*t*r, min(64*t*(r+1), Nk)) and there are ceil(nkt / t) <= n_splits ranges.  Each
+ * range leaves, per query row, a partial state in fp32: the normalised partial output
+ * O_r and its log-sum-exp L_r (L_r = -inf and O_r = 0 where the range holds no key
+ * visible to the row).  A second kernel folds them with the (+) operator of the
+ * "Flash Attention" blog page (blog.cyberangel.work, the online-softmax merge of
+ * (m, d, o~) states, associative and commutative) in log-sum-exp form:
+ *     L = log sum_r exp(L_r),   O = sum_r exp(L_r - L) O_r,
+ * then rounds O to `dtype` (nearest-even).  The result equals fa_fwd's up to fp32
+ * rounding order.
+ *
+ * Arguments as fa_fwd, plus:
+ *   n_splits         requested number of key ranges, 1 .. 256 (fewer are used when
+ *                    Nk has fewer 64-key tiles); when only one range results, the
+ *                    unsplit kernel runs and the workspace is not touched
+ *   workspace        DEVICE buffer owned by the caller, 16-byte aligned, at least
+ *                    fa_fwd_split_workspace(B, H, Nq, d, n_splits) bytes; it holds the
+ *                    partials: O_r as fp32 [n_splits, B, H, Nq, d] at offset 0, then
+ *                    L_r as fp32 [n_splits, B, H, Nq] at the next multiple of 256 bytes
+ *                    (ranges beyond the number used are not written)
+ *   workspace_bytes  its size in bytes
+ *
+ * Behaviour: as fa_fwd (validation first, asynchronous, deterministic), and
+ * FA_ERR_INVALID_ARG for n_splits outside 1 .. 256 or a missing, misaligned or too
+ * small workspace when more than one range is used.  Two kernels are enqueued in
+ * order on `stream`; the workspace must not be reused until they complete.
+ */
+fa_status_t fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                         float scale, fa_dtype_t dtype, int n_splits, void* workspace,
+                         int64_t workspace_bytes, fa_stream_t stream);
+
+/* Workspace bytes fa_fwd_split needs for (B, H, Nq, d, n_splits); -1 for arguments
+ * it would reject (negative sizes, d outside {64, 128}, n_splits outside 1 .. 256). */
+int64_t fa_fwd_split_workspace(int64_t B, int64_t H, int64_t Nq, int64_t d, int n_splits);
+
+/*
+ * fa_merge — fold partial attention states over disjoint key ranges into the final
+ * output (the second half of fa_fwd_split, for partials computed elsewhere, e.g. one
+ * part per GPU of a key-sharded sequence).  Definition: as in fa_fwd_split above.
+ *
+ *   o_parts    [n_parts, B, H, Nq, d] fp32 DEVICE buffer: O_r, the normalised partial
+ *              output of key range r (16-byte aligned)
+ *   lse_parts  [n_parts, B, H, Nq] fp32: L_r, natural-log log-sum-exp of range r's
+ *              scaled, masked scores; -inf marks a range with no visible key (its O_r
+ *              is then ignored)
+ *   o          [B, H, Nq, d] output in `dtype`, rounded to nearest-even (16-byte aligned)
+ *   lse        [B, H, Nq] fp32 output, log sum_r exp(L_r)
+ * A row whose every L_r is -inf gets O = 0 and L = -inf.  n_parts >= 1; d 64 or 128
+ * (else FA_ERR_UNSUPPORTED); B*H*Nq == 0 returns FA_OK without touching anything.
+ * Asynchronous on `stream`; errors are reported before any HIP call.
+ */
+fa_status_t fa_merge(const float* o_parts, const float* lse_parts, int n_parts, int64_t B,
+                     int64_t H, int64_t Nq, int64_t d, void* o, float* lse, fa_dtype_t dtype,
+                     fa_stream_t stream);
+
+/* A key-range count for fa_fwd_split that fills the GPU (256 CUs) when fa_fwd's grid of
+ * B*H*ceil(Nq / fa_tile_rows(...)) workgroups would not: 1 when that grid already
+ * fills it, otherwise enough ranges to, keeping at least eight 64-key tiles per range
+ * (two for fp32) and at most 16 ranges.  0 for unsupported or empty arguments. */
+int fa_split_hint(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                  fa_dtype_t dtype);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* fa_status_str(fa_status_t status);

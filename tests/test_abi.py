@@ -103,6 +103,86 @@ def test_validation_before_any_hip_call(kw, want):
     assert _call(**kw) == want
 
 
+def _split(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Nq=8, Nk=1024, d=64, causal=0, scale=0.125,
+             dtype=fa.FA_DTYPE_BF16, n_splits=4, workspace=P, workspace_bytes=1 << 30, stream=0)
+    a.update(kw)
+    return fa.fa_fwd_split_raw(**a)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(n_splits=0), fa.FA_ERR_INVALID_ARG),
+    (dict(n_splits=257), fa.FA_ERR_INVALID_ARG),
+    (dict(n_splits=-3), fa.FA_ERR_INVALID_ARG),
+    (dict(workspace=0), fa.FA_ERR_INVALID_ARG),
+    (dict(workspace=P + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(workspace_bytes=100), fa.FA_ERR_INVALID_ARG),
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=P + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=9), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=3), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=0), fa.FA_OK),
+    (dict(B=0, q=0, k=0, v=0, o=0, lse=0, workspace=0), fa.FA_OK),
+])
+def test_split_validation_before_any_hip_call(kw, want):
+    assert _split(**kw) == want
+
+
+def _merge(**kw):
+    a = dict(o_parts=P, lse_parts=P, n_parts=3, B=1, H=2, Nq=8, d=128, o=P, lse=P,
+             dtype=fa.FA_DTYPE_BF16, stream=0)
+    a.update(kw)
+    return fa.fa_merge_raw(**a)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(n_parts=0), fa.FA_ERR_INVALID_ARG),
+    (dict(B=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=4), fa.FA_ERR_INVALID_ARG),
+    (dict(o_parts=0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse_parts=0), fa.FA_ERR_INVALID_ARG),
+    (dict(o=0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=0), fa.FA_ERR_INVALID_ARG),
+    (dict(o_parts=P + 4), fa.FA_ERR_INVALID_ARG),
+    (dict(o=P + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(lse_parts=P + 1), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=0, o_parts=0, lse_parts=0, o=0, lse=0), fa.FA_OK),
+])
+def test_merge_validation_before_any_hip_call(kw, want):
+    assert _merge(**kw) == want
+
+
+def test_split_workspace_size():
+    # n_splits * rows * d fp32 partial outputs, padded to 256 B, then n_splits * rows fp32 L
+    rows = 2 * 8 * 1024
+    assert fa.fa_fwd_split_workspace(2, 8, 1024, 64, 4) == 4 * rows * 64 * 4 + 4 * rows * 4
+    assert fa.fa_fwd_split_workspace(1, 1, 3, 128, 2) == 3072 + 24
+    assert fa.fa_fwd_split_workspace(1, 1, 0, 128, 2) == 0
+    for bad in [(-1, 1, 1, 64, 2), (1, 1, 1, 80, 2), (1, 1, 1, 64, 0), (1, 1, 1, 64, 257)]:
+        assert fa.fa_fwd_split_workspace(*bad) == -1
+
+
+def test_split_hint():
+    bf16, f32 = fa.FA_DTYPE_BF16, fa.FA_DTYPE_F32
+    # 2x8 heads x 8 query tiles of 128 rows = 128 workgroups, 2 per CU: 4 would fill the
+    # GPU, but 16 key tiles keep at most 2 ranges of 8 tiles
+    assert fa.fa_split_hint(2, 8, 1024, 1024, 64, 0, bf16) == 2
+    # 512 workgroups of 256 rows already fill the GPU
+    assert fa.fa_split_hint(1, 16, 8192, 8192, 128, 1, bf16) == 1
+    # fp32: 2 workgroups, 4 key tiles, two tiles per range
+    assert fa.fa_split_hint(1, 1, 256, 256, 64, 0, f32) == 2
+    # short queries, long keys: 32 workgroups -> 8 ranges of 32 tiles
+    assert fa.fa_split_hint(4, 8, 256, 16384, 128, 0, bf16) == 8
+    assert fa.fa_split_hint(1, 1, 1, 1 << 20, 128, 0, bf16) == 16
+    assert fa.fa_split_hint(1, 1, 8, 64, 64, 0, bf16) == 1
+    assert fa.fa_split_hint(0, 1, 8, 64, 64, 0, bf16) == 0
+    assert fa.fa_split_hint(1, 1, 8, 64, 96, 0, bf16) == 0
+
+
 def test_status_strings_and_tiles():
     assert fa.fa_status_str(fa.FA_OK) == "FA_OK"
     assert fa.fa_status_str(fa.FA_ERR_LAUNCH) == "FA_ERR_LAUNCH"

@@ -14,9 +14,6 @@ Workloads and shapes: the seven measured workloads (all rows where the oracle
 finishes in seconds, a seeded sample of 4 heads x 256 rows on the largest), plus
 ragged, rectangular, fp16, fp32, tiny and empty shapes.
 """
-import math
-import sys
-
 import numpy as np
 import pytest
 
@@ -30,26 +27,8 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import flashattention_tiling_online_amd as fa  # noqa: E402
-
-DEV = torch.device("cuda:0")
-TORCH_DT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
-
-
-def say(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
-
-
-def to_dev(a: np.ndarray, dtype: str):
-    if dtype == "bf16":
-        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV)
-    return torch.from_numpy(a).to(DEV)
-
-
-def to_host(t, dtype: str) -> np.ndarray:
-    if dtype == "bf16":
-        return t.view(torch.int16).cpu().numpy().view(np.uint16)
-    return t.cpu().numpy()
+from parity_util import (DEV, TORCH_DT, bf16_neighbours_ok, compare, say, to_dev,  # noqa: E402,F401
+                         to_host)
 
 
 def run_gpu(w, q, k, v):
@@ -57,38 +36,6 @@ def run_gpu(w, q, k, v):
     o, lse = fa.fa_fwd(tq, tk, tv, causal=w.causal, scale=w.scale)
     torch.cuda.synchronize()
     return o, lse
-
-
-def bf16_neighbours_ok(o_gpu64, o_ref):
-    """True where o_gpu is the bf16 value just below or just above o_ref in magnitude."""
-    e = np.frexp(np.abs(o_ref))[1].astype(np.int32)    # |o_ref| in [2^(e-1), 2^e)
-    quantum = np.ldexp(1.0, e - 1 - 7)                  # bf16 spacing there
-    lo = np.trunc(o_ref / quantum) * quantum
-    hi = lo + np.sign(o_ref) * quantum
-    return (o_gpu64 == lo) | (o_gpu64 == hi)
-
-
-def compare(w, o_gpu_np, lse_gpu, sel_bh, sel_row, o64, l64):
-    d = w.d
-    o_sel = oracle.widen(o_gpu_np.reshape(-1, d)[sel_bh * w.Nq + sel_row], w.dtype)
-    l_sel = lse_gpu.reshape(-1)[sel_bh * w.Nq + sel_row].astype(np.float64)
-    assert np.isfinite(o_sel).all() and np.isfinite(l_sel).all()
-    err = np.abs(o_sel - o64)
-    derr_l = np.abs(l_sel - l64)
-    if w.dtype == "f32":
-        say(f"  {w.name}: max|dO|={err.max():.3e} mean|dO|={err.mean():.3e} "
-            f"max|dL|={derr_l.max():.3e}")
-        assert err.max() <= 1e-4
-        assert derr_l.max() <= 1e-3
-        return
-    big = np.abs(o64) >= 4.0
-    over = err > 1e-2
-    faithful = over & big & (bf16_neighbours_ok(o_sel, o64) if w.dtype == "bf16" else False)
-    say(f"  {w.name}: max|dO|={err.max():.3e} mean|dO|={err.mean():.3e} "
-        f"max|dL|={derr_l.max():.3e} faithful-rounding exceptions={int(faithful.sum())}")
-    assert not (over & ~faithful).any(), f"max|dO| {err[over & ~faithful].max():.3e} > 1e-2"
-    assert err.mean() <= 1e-3
-    assert derr_l.max() <= 1e-3
 
 
 def check_workload(w, n_heads=None, n_rows=None):
@@ -129,7 +76,8 @@ def test_workload_all_rows(name):
     hull_property(w, v, o)
 
 
-@pytest.mark.parametrize("name", ["self_8k_causal", "cross_1k_8k", "ctx_32k_causal"])
+@pytest.mark.parametrize("name", ["self_8k_causal", "cross_1k_8k", "ctx_32k_causal",
+                                  "short_q_long_kv"])
 def test_workload_sampled_rows(name):
     w = inputs.WORKLOADS[name]
     _, _, v, o, lse = check_workload(w, n_heads=4, n_rows=256)
