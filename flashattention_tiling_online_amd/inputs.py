@@ -28,7 +28,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-TENSOR_IDS = {"q": 1, "k": 2, "v": 3}
+TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "do": 4}
 STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 
@@ -174,8 +174,8 @@ def round_fp32(x: np.ndarray, dtype: str) -> np.ndarray:
 
 def make_tensor(w: Workload, tensor: str) -> np.ndarray:
     """[B, H, N, d] array in the storage dtype."""
-    n = w.Nq if tensor == "q" else w.Nk
-    sigma = {"q": w.sigma_q, "k": w.sigma_k, "v": w.sigma_v}[tensor]
+    n = w.Nq if tensor in ("q", "do") else w.Nk
+    sigma = {"q": w.sigma_q, "k": w.sigma_k, "v": w.sigma_v, "do": 1.0}[tensor]
     out = np.empty((w.B, w.H, n, w.d), dtype=STORAGE[w.dtype])
 
     def fill(bh):
@@ -194,6 +194,12 @@ def make_tensor(w: Workload, tensor: str) -> np.ndarray:
 
 def make_qkv(w: Workload):
     return make_tensor(w, "q"), make_tensor(w, "k"), make_tensor(w, "v")
+
+
+def make_do(w: Workload) -> np.ndarray:
+    """The output gradient dO for the backward pass: [B, H, Nq, d], N(0, 1) per element,
+    drawn like q, k and v from its own per-head stream."""
+    return make_tensor(w, "do")
 
 
 def sample_rows(w: Workload, n_heads: int, n_rows: int, seed: int = SAMPLE_SEED):

@@ -2,7 +2,7 @@
  * fa_oracle.h — C-ABI of the fp64 CPU oracle (test infrastructure only).
  *
  * The oracle is a plain, slow, obviously-correct host implementation of what the
- * fused attention forward pass computes.  It exists to check the GPU library
+ * fused attention forward pass (and its gradients) compute.  It exists to check the GPU library
  * (fa.h) and is built into its own shared library, libfa_oracle.so, from
  * oracle/fa_oracle.c.  The GPU library never links it, and it shares no code,
  * header or table with the GPU library: the dtype codes below are restated here
@@ -20,7 +20,11 @@
  *   - row logsumexp L = m + ln(l), natural log (course file, flash_attention_forward
  *     and demo_online_softmax);
  *   - online softmax and the (+) merge on (m, d) and (m, d, o~)
- *     ("Flash Attention" blog page, sections "Online Softmax" and parallelisation).
+ *     ("Flash Attention" blog page, sections "Online Softmax" and parallelisation);
+ *   - gradients of the loss sum(dO o O): dV = P^T dO, dP = dO V^T,
+ *     dS = P o (dP - D) with D_r = P_r . dP_r (= do_r . o_r), dQ = scale dS K,
+ *     dK = scale dS^T Q (course file, flash_attention_backward; blog page,
+ *     Algorithm 4 and the softmax-Jacobian derivation after it).
  *
  * Conventions common to every function:
  *   - all pointers are HOST pointers; the caller owns every buffer;
@@ -126,6 +130,52 @@ int fa_fwd_ref(const void* q, const void* k, const void* v, void* o, float* lse,
 /* fp64 -> dtype rounding used by fa_fwd_ref (round to nearest, ties to even),
  * exposed so that it can be pinned against independent conversions. */
 int fa_oracle_round(const double* x, int64_t n, int dtype, void* out);
+
+/*
+ * Part 3: gradients, plain definition, one head of fp64 inputs (row-major
+ * q, dout [nq, d], k, v [nk, d]).  Writes dq [nq, d], dk, dv [nk, d].  Every row
+ * materialises P_r and dP_r = do_r V^T, takes D_r = P_r . dP_r and
+ * dS_r = P_r o (dP_r - D_r), and accumulates dq_r = scale dS_r K,
+ * dk += scale dS_r^T q_r, dv += P_r^T do_r.
+ */
+int fa_oracle_attention_bwd_f64(const double* q, const double* k, const double* v,
+                                const double* dout, int64_t nq, int64_t nk, int64_t d,
+                                int causal, double scale, double* dq, double* dk, double* dv);
+
+/* Part 3 on head bh of raw [B,H,N,d] buffers of `dtype` (dout like q): fp64 dq64
+ * [Nq, d], dk64 and dv64 [Nk, d]. */
+int fa_ref_bwd_head_f64(const void* q, const void* k, const void* v, const void* dout,
+                        int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                        float scale, int dtype, int64_t bh, double* dq64, double* dk64,
+                        double* dv64);
+
+/* dQ of selected rows (sel_bh[i], sel_row[i]) of raw buffers -> dq64 [n_sel, d]. */
+int fa_ref_bwd_dq_rows_f64(const void* q, const void* k, const void* v, const void* dout,
+                           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                           float scale, int dtype, int64_t n_sel, const int64_t* sel_bh,
+                           const int64_t* sel_row, double* dq64);
+
+/* Row statistics of selected rows: lse64[i] (as part 1) and D64[i] = P_r . dP_r. */
+int fa_ref_bwd_rowstats_f64(const void* q, const void* k, const void* v, const void* dout,
+                            int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                            float scale, int dtype, int64_t n_sel, const int64_t* sel_bh,
+                            const int64_t* sel_row, double* lse64, double* D64);
+
+/* dK and dV of selected keys (sel_bh[i], sel_key[i]) -> dk64, dv64 [n_sel, d], given
+ * the row statistics of every row of the heads involved (lse64_all, D64_all indexed
+ * [bh * Nq + r]): P[r, j] = exp(S[r, j] - lse_r), dv_j = sum_r P[r, j] do_r,
+ * dk_j = scale sum_r P[r, j] (dP[r, j] - D_r) q_r. */
+int fa_ref_bwd_dkv_keys_f64(const void* q, const void* k, const void* v, const void* dout,
+                            int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                            float scale, int dtype, const double* lse64_all,
+                            const double* D64_all, int64_t n_sel, const int64_t* sel_bh,
+                            const int64_t* sel_key, double* dk64, double* dv64);
+
+/* Whole-tensor host counterpart of the GPU backward: part 3 on every head, the
+ * gradients rounded from fp64 to `dtype` (nearest-even) into dq, dk, dv. */
+int fa_bwd_ref(const void* q, const void* k, const void* v, const void* dout, void* dq,
+               void* dk, void* dv, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+               int causal, float scale, int dtype);
 
 #ifdef __cplusplus
 }

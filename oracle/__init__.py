@@ -15,6 +15,9 @@ What is computed, and where it comes from (pages named by title / address):
 * part 2, ``online_f64`` / ``ref_online_f64``: the scalar online (m, d, o~)
   accumulator and the (+) merge — blog page, "Online Softmax" and the
   parallelisation section.
+* part 3, ``attention_bwd_f64`` / ``bwd_*``: the gradients of sum(dO o O) — course
+  file ``flash_attention_backward``; blog page, Algorithm 4 and the softmax-Jacobian
+  derivation that follows it.
 * ``softmax_online``: the one-dimensional online softmax with a per-block trace —
   course file ``online_softmax_stats``; the worked example of
   "手写 Flash Attention" (bjdmk.com.cn) section 2.2 is pinned against it.
@@ -76,9 +79,21 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_ref.argtypes = [_vp, _vp, _vp, _vp, ctypes.POINTER(ctypes.c_float), _i64, _i64,
                                _i64, _i64, _i64, ctypes.c_int, ctypes.c_float, ctypes.c_int]
     lib.fa_oracle_round.argtypes = [_dp, _i64, ctypes.c_int, _vp]
+    raw4 = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_float,
+            ctypes.c_int]
+    lib.fa_oracle_attention_bwd_f64.argtypes = [_dp, _dp, _dp, _dp, _i64, _i64, _i64,
+                                                ctypes.c_int, ctypes.c_double, _dp, _dp, _dp]
+    lib.fa_ref_bwd_head_f64.argtypes = raw4 + [_i64, _dp, _dp, _dp]
+    lib.fa_ref_bwd_dq_rows_f64.argtypes = raw4 + [_i64, _lp, _lp, _dp]
+    lib.fa_ref_bwd_rowstats_f64.argtypes = raw4 + [_i64, _lp, _lp, _dp, _dp]
+    lib.fa_ref_bwd_dkv_keys_f64.argtypes = raw4 + [_dp, _dp, _i64, _lp, _lp, _dp, _dp]
+    lib.fa_bwd_ref.argtypes = [_vp] * 7 + [_i64, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                           ctypes.c_float, ctypes.c_int]
     for name in ("fa_oracle_softmax_online", "fa_oracle_merge", "fa_oracle_attention_f64",
                  "fa_oracle_online_f64", "fa_ref_rows_f64", "fa_ref_online_f64", "fa_fwd_ref",
-                 "fa_oracle_round"):
+                 "fa_oracle_round", "fa_oracle_attention_bwd_f64", "fa_ref_bwd_head_f64",
+                 "fa_ref_bwd_dq_rows_f64", "fa_ref_bwd_rowstats_f64", "fa_ref_bwd_dkv_keys_f64",
+                 "fa_bwd_ref"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -247,6 +262,131 @@ def ref_rows_f64(q, k, v, causal: bool, scale: float, dtype: str, sel_bh, sel_ro
     if online_key_block is None:
         return o, lse
     return o, lse, raised
+
+
+# ---------------------------------------------------------------------------
+# gradients (part 3)
+# ---------------------------------------------------------------------------
+
+def attention_bwd_f64(q, k, v, dout, causal: bool, scale: float, L=None):
+    """Part 3 on one head of fp64 inputs; returns (dq [nq, d], dk [nk, d], dv [nk, d])."""
+    L = L or lib()
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    nq, d = q.shape
+    nk = k.shape[0]
+    dq, dk, dv = np.empty((nq, d)), np.empty((nk, d)), np.empty((nk, d))
+    _check(L.fa_oracle_attention_bwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), nq, nk, d,
+                                         int(causal), float(scale), _ptr(dq), _ptr(dk),
+                                         _ptr(dv)), "fa_oracle_attention_bwd_f64")
+    return dq, dk, dv
+
+
+def _raw4(q, k, v, dout, dtype):
+    q, k, v, dout = (_raw(a, dtype) for a in (q, k, v, dout))
+    B, H, Nq, d = q.shape
+    return q, k, v, dout, B, H, Nq, k.shape[2], d
+
+
+def bwd_head_f64(q, k, v, dout, causal: bool, scale: float, dtype: str, bh: int, L=None):
+    """Part 3 on head bh of raw [B,H,N,d] buffers; returns fp64 (dq, dk, dv)."""
+    L = L or lib()
+    q, k, v, dout, B, H, Nq, Nk, d = _raw4(q, k, v, dout, dtype)
+    dq, dk, dv = np.empty((Nq, d)), np.empty((Nk, d)), np.empty((Nk, d))
+    _check(L.fa_ref_bwd_head_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                                 B, H, Nq, Nk, d, int(causal), float(scale), DTYPE_CODES[dtype],
+                                 int(bh), _ptr(dq), _ptr(dk), _ptr(dv)), "fa_ref_bwd_head_f64")
+    return dq, dk, dv
+
+
+def _threaded(n, threads, work):
+    spans = _split(n, threads or os.cpu_count() or 1)
+    if len(spans) <= 1:
+        rcs = [work(spans[0])] if spans else []
+    else:
+        with ThreadPoolExecutor(max_workers=len(spans)) as ex:
+            rcs = list(ex.map(work, spans))
+    return rcs
+
+
+def bwd_dq_rows_f64(q, k, v, dout, causal: bool, scale: float, dtype: str, sel_bh, sel_row,
+                    threads: int | None = None, L=None):
+    """dQ of the selected rows (part 3), threaded over the rows; returns [n_sel, d]."""
+    L = L or lib()
+    q, k, v, dout, B, H, Nq, Nk, d = _raw4(q, k, v, dout, dtype)
+    sel_bh = np.ascontiguousarray(sel_bh, np.int64)
+    sel_row = np.ascontiguousarray(sel_row, np.int64)
+    dq = np.empty((sel_bh.size, d))
+
+    def work(span):
+        a, b = span
+        if b <= a:
+            return 0
+        return L.fa_ref_bwd_dq_rows_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                        dout.ctypes.data, B, H, Nq, Nk, d, int(causal),
+                                        float(scale), DTYPE_CODES[dtype], b - a,
+                                        _ptr(sel_bh[a:b], _lp), _ptr(sel_row[a:b], _lp),
+                                        _ptr(dq[a:b]))
+
+    for rc in _threaded(sel_bh.size, threads, work):
+        _check(rc, "fa_ref_bwd_dq_rows_f64")
+    return dq
+
+
+def bwd_dkv_keys_f64(q, k, v, dout, causal: bool, scale: float, dtype: str, sel_bh, sel_key,
+                     threads: int | None = None, L=None):
+    """dK and dV of the selected keys (part 3): the row statistics of every row of the
+    heads involved first (threaded over rows), then the keys (threaded)."""
+    L = L or lib()
+    q, k, v, dout, B, H, Nq, Nk, d = _raw4(q, k, v, dout, dtype)
+    sel_bh = np.ascontiguousarray(sel_bh, np.int64)
+    sel_key = np.ascontiguousarray(sel_key, np.int64)
+    heads = np.unique(sel_bh)
+    lse_all = np.full(B * H * Nq, np.nan)
+    D_all = np.full(B * H * Nq, np.nan)
+    rb = np.repeat(heads, Nq)
+    rr = np.tile(np.arange(Nq, dtype=np.int64), heads.size)
+    lse_sel, D_sel = np.empty(rb.size), np.empty(rb.size)
+
+    def stats(span):
+        a, b = span
+        if b <= a:
+            return 0
+        return L.fa_ref_bwd_rowstats_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                         dout.ctypes.data, B, H, Nq, Nk, d, int(causal),
+                                         float(scale), DTYPE_CODES[dtype], b - a,
+                                         _ptr(rb[a:b], _lp), _ptr(rr[a:b], _lp),
+                                         _ptr(lse_sel[a:b]), _ptr(D_sel[a:b]))
+
+    for rc in _threaded(rb.size, threads, stats):
+        _check(rc, "fa_ref_bwd_rowstats_f64")
+    lse_all[rb * Nq + rr] = lse_sel
+    D_all[rb * Nq + rr] = D_sel
+    dk, dv = np.empty((sel_bh.size, d)), np.empty((sel_bh.size, d))
+
+    def keys(span):
+        a, b = span
+        if b <= a:
+            return 0
+        return L.fa_ref_bwd_dkv_keys_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                         dout.ctypes.data, B, H, Nq, Nk, d, int(causal),
+                                         float(scale), DTYPE_CODES[dtype], _ptr(lse_all),
+                                         _ptr(D_all), b - a, _ptr(sel_bh[a:b], _lp),
+                                         _ptr(sel_key[a:b], _lp), _ptr(dk[a:b]), _ptr(dv[a:b]))
+
+    for rc in _threaded(sel_bh.size, threads, keys):
+        _check(rc, "fa_ref_bwd_dkv_keys_f64")
+    return dk, dv
+
+
+def bwd_ref(q, k, v, dout, causal: bool, scale: float, dtype: str, L=None):
+    """Whole-tensor host backward: dq, dk, dv in the input dtype (RNE from fp64)."""
+    L = L or lib()
+    q, k, v, dout, B, H, Nq, Nk, d = _raw4(q, k, v, dout, dtype)
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    _check(L.fa_bwd_ref(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                        dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, B, H, Nq, Nk, d,
+                        int(causal), float(scale), DTYPE_CODES[dtype]), "fa_bwd_ref")
+    return dq, dk, dv
 
 
 def fwd_ref(q, k, v, causal: bool, scale: float, dtype: str, L=None):

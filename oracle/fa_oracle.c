@@ -1,5 +1,5 @@
 /*
- * fa_oracle.c — fp64 CPU oracle for the fused attention forward pass.
+ * fa_oracle.c — fp64 CPU oracle for the fused attention forward pass and its gradients.
  *
  * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the benchmark's
  * CPU-baseline leg may load this code.  The GPU library shares nothing with it.
@@ -11,10 +11,12 @@
  * What it follows (the pages are named by their titles / addresses):
  *   [A] "05_flash_attention.py" (CS336 lecture-5 course file, semidirectx.com):
  *       standard_attention (scale, causal triu mask, softmax, @V),
- *       flash_attention_forward (returned L = m + log l), online_softmax_stats.
+ *       flash_attention_forward (returned L = m + log l), online_softmax_stats,
+ *       flash_attention_backward (the gradient formulas of part 3).
  *   [B] "Flash Attention" (blog.cyberangel.work): sections "Online Softmax"
  *       (safe softmax, the online recurrence and its invariant), the parallelisation
- *       section (the (+) operator on (m, d) and on (m, d, o~)), Algorithm 2 (tau, mask).
+ *       section (the (+) operator on (m, d) and on (m, d, o~)), Algorithm 2 (tau, mask),
+ *       Algorithm 4 (backward pass) and the softmax-Jacobian derivation after it.
  *   [C] "手写 Flash Attention：从算法原理到高性能实现" (bjdmk.com.cn), section 2.2:
  *       the worked two-block example that the tests pin.
  *
@@ -518,5 +520,297 @@ int fa_fwd_ref(const void* q, const void* k, const void* v, void* o, float* lse,
     free(l64);
     free(bh);
     free(row);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Part 3: gradients of attention, the plain definition                       */
+/*   [A] flash_attention_backward (course file, part 3): dV = P^T dO,          */
+/*       dP = dO V^T, dS = P o (dP - D) with D_i = rowsum(dO o O),             */
+/*       dQ = dS K * scale, dK = dS^T Q * scale;                               */
+/*   [B] Algorithm 4 (backward pass) and its derivation: the softmax Jacobian  */
+/*       diag(p) - p p^T gives dS_i = P_i o dP_i - (P_i . dP_i) P_i, and       */
+/*       D_i = P_i . dP_i, which equals do_i . o_i.                            */
+/* The loss whose gradients these are is sum(dO o O) for a given dO.  D is     */
+/* computed here from its definition P_i . dP_i (exact in fp64, equal to       */
+/* do_i . o_i up to rounding).                                                 */
+/* ------------------------------------------------------------------------- */
+
+/* P[r, :] of one query row (the softmax of the scaled, masked scores) */
+static void prob_row(const double* q_row, const double* k, int64_t nk, int64_t d, int causal,
+                     double scale, int64_t r, double* p)
+{
+    double m = -INFINITY;
+    for (int64_t kk = 0; kk < nk; ++kk) {
+        p[kk] = score(q_row, k + kk * d, d, scale, causal, r, kk);
+        if (p[kk] > m)
+            m = p[kk];
+    }
+    double l = 0.0;
+    for (int64_t kk = 0; kk < nk; ++kk) {
+        p[kk] = exp(p[kk] - m);
+        l += p[kk];
+    }
+    for (int64_t kk = 0; kk < nk; ++kk)
+        p[kk] = p[kk] / l;
+}
+
+/* dP[r, :] = do_r V^T and D_r = P_r . dP_r */
+static double dprob_row(const double* do_row, const double* v, const double* p, int64_t nk,
+                        int64_t d, double* dp)
+{
+    double D = 0.0;
+    for (int64_t kk = 0; kk < nk; ++kk) {
+        double acc = 0.0;
+        for (int64_t t = 0; t < d; ++t)
+            acc += do_row[t] * v[kk * d + t];
+        dp[kk] = acc;
+        D += p[kk] * dp[kk];
+    }
+    return D;
+}
+
+int fa_oracle_attention_bwd_f64(const double* q, const double* k, const double* v,
+                                const double* dout, int64_t nq, int64_t nk, int64_t d,
+                                int causal, double scale, double* dq, double* dk, double* dv)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || nq < 1 || nk < 1 || d < 1)
+        return FA_ORACLE_EINVAL;
+    double* p = (double*)malloc((size_t)nk * sizeof(double));
+    double* dp = (double*)malloc((size_t)nk * sizeof(double));
+    if (!p || !dp) {
+        free(p);
+        free(dp);
+        return FA_ORACLE_ENOMEM;
+    }
+    for (int64_t i = 0; i < nk * d; ++i) {
+        dk[i] = 0.0;
+        dv[i] = 0.0;
+    }
+    for (int64_t r = 0; r < nq; ++r) {
+        const double* q_row = q + r * d;
+        const double* do_row = dout + r * d;
+        prob_row(q_row, k, nk, d, causal, scale, r, p);    /* P[r, :] */
+        const double D = dprob_row(do_row, v, p, nk, d, dp); /* dP[r, :], D_r */
+        for (int64_t t = 0; t < d; ++t)
+            dq[r * d + t] = 0.0;
+        for (int64_t kk = 0; kk < nk; ++kk) {
+            const double ds = p[kk] * (dp[kk] - D); /* dS[r, kk] */
+            for (int64_t t = 0; t < d; ++t) {
+                dq[r * d + t] += scale * ds * k[kk * d + t];  /* dQ = dS K * scale */
+                dk[kk * d + t] += scale * ds * q_row[t];      /* dK = dS^T Q * scale */
+                dv[kk * d + t] += p[kk] * do_row[t];          /* dV = P^T dO */
+            }
+        }
+    }
+    free(p);
+    free(dp);
+    return FA_ORACLE_OK;
+}
+
+/* raw-buffer gradients ---------------------------------------------------- */
+
+static int check_bwd_raw(const void* q, const void* k, const void* v, const void* dout,
+                         int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int dtype)
+{
+    if (!dout)
+        return FA_ORACLE_EINVAL;
+    return check_raw(q, k, v, B, H, Nq, Nk, d, dtype);
+}
+
+/* One head bh of raw [B,H,N,d] buffers: every row of dQ and every key of dK, dV. */
+int fa_ref_bwd_head_f64(const void* q, const void* k, const void* v, const void* dout,
+                        int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                        float scale, int dtype, int64_t bh, double* dq64, double* dk64,
+                        double* dv64)
+{
+    int rc = check_bwd_raw(q, k, v, dout, B, H, Nq, Nk, d, dtype);
+    if (rc)
+        return rc;
+    if (bh < 0 || bh >= B * H || !dq64 || !dk64 || !dv64)
+        return FA_ORACLE_EINVAL;
+    double* buf = (double*)malloc((size_t)(2 * Nq * d + 2 * Nk * d) * sizeof(double));
+    if (!buf)
+        return FA_ORACLE_ENOMEM;
+    double *qh = buf, *doh = buf + Nq * d, *kh = doh + Nq * d, *vh = kh + Nk * d;
+    widen_span(q, bh * Nq * d, Nq * d, dtype, qh);
+    widen_span(dout, bh * Nq * d, Nq * d, dtype, doh);
+    widen_span(k, bh * Nk * d, Nk * d, dtype, kh);
+    widen_span(v, bh * Nk * d, Nk * d, dtype, vh);
+    rc = fa_oracle_attention_bwd_f64(qh, kh, vh, doh, Nq, Nk, d, causal, (double)scale, dq64,
+                                     dk64, dv64);
+    free(buf);
+    return rc;
+}
+
+/* dQ of selected query rows (sel_bh[i], sel_row[i]) -> dq64[i * d .. +d] */
+int fa_ref_bwd_dq_rows_f64(const void* q, const void* k, const void* v, const void* dout,
+                           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                           float scale, int dtype, int64_t n_sel, const int64_t* sel_bh,
+                           const int64_t* sel_row, double* dq64)
+{
+    int rc = check_bwd_raw(q, k, v, dout, B, H, Nq, Nk, d, dtype);
+    if (rc)
+        return rc;
+    if (n_sel < 0 || (n_sel > 0 && (!sel_bh || !sel_row || !dq64)))
+        return FA_ORACLE_EINVAL;
+    for (int64_t i = 0; i < n_sel; ++i)
+        if (sel_bh[i] < 0 || sel_bh[i] >= B * H || sel_row[i] < 0 || sel_row[i] >= Nq)
+            return FA_ORACLE_EINVAL;
+    double* buf = (double*)malloc((size_t)(2 * Nk * d + 2 * d + 2 * Nk) * sizeof(double));
+    if (!buf)
+        return FA_ORACLE_ENOMEM;
+    double *kh = buf, *vh = kh + Nk * d, *qr = vh + Nk * d, *dor = qr + d, *p = dor + d,
+           *dp = p + Nk;
+    const double sc = (double)scale;
+    int64_t cur = -1;
+    for (int64_t i = 0; i < n_sel; ++i) {
+        const int64_t bh = sel_bh[i], r = sel_row[i];
+        if (bh != cur) {
+            widen_span(k, bh * Nk * d, Nk * d, dtype, kh);
+            widen_span(v, bh * Nk * d, Nk * d, dtype, vh);
+            cur = bh;
+        }
+        widen_span(q, (bh * Nq + r) * d, d, dtype, qr);
+        widen_span(dout, (bh * Nq + r) * d, d, dtype, dor);
+        prob_row(qr, kh, Nk, d, causal, sc, r, p);
+        const double D = dprob_row(dor, vh, p, Nk, d, dp);
+        double* out = dq64 + i * d;
+        for (int64_t t = 0; t < d; ++t)
+            out[t] = 0.0;
+        for (int64_t kk = 0; kk < Nk; ++kk) {
+            const double ds = p[kk] * (dp[kk] - D);
+            for (int64_t t = 0; t < d; ++t)
+                out[t] += sc * ds * kh[kk * d + t];
+        }
+    }
+    free(buf);
+    return FA_ORACLE_OK;
+}
+
+/* Per-row statistics of selected rows: lse64[i] = log-sum-exp of the scaled, masked
+ * scores of row (sel_bh[i], sel_row[i]) and D64[i] = P_r . dP_r. */
+int fa_ref_bwd_rowstats_f64(const void* q, const void* k, const void* v, const void* dout,
+                            int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                            float scale, int dtype, int64_t n_sel, const int64_t* sel_bh,
+                            const int64_t* sel_row, double* lse64, double* D64)
+{
+    int rc = check_bwd_raw(q, k, v, dout, B, H, Nq, Nk, d, dtype);
+    if (rc)
+        return rc;
+    if (n_sel < 0 || (n_sel > 0 && (!sel_bh || !sel_row || !lse64 || !D64)))
+        return FA_ORACLE_EINVAL;
+    for (int64_t i = 0; i < n_sel; ++i)
+        if (sel_bh[i] < 0 || sel_bh[i] >= B * H || sel_row[i] < 0 || sel_row[i] >= Nq)
+            return FA_ORACLE_EINVAL;
+    double* buf = (double*)malloc((size_t)(2 * Nk * d + 2 * d + 2 * Nk + d) * sizeof(double));
+    if (!buf)
+        return FA_ORACLE_ENOMEM;
+    double *kh = buf, *vh = kh + Nk * d, *qr = vh + Nk * d, *dor = qr + d, *p = dor + d,
+           *dp = p + Nk, *o_row = dp + Nk;
+    const double sc = (double)scale;
+    int64_t cur = -1;
+    for (int64_t i = 0; i < n_sel; ++i) {
+        const int64_t bh = sel_bh[i], r = sel_row[i];
+        if (bh != cur) {
+            widen_span(k, bh * Nk * d, Nk * d, dtype, kh);
+            widen_span(v, bh * Nk * d, Nk * d, dtype, vh);
+            cur = bh;
+        }
+        widen_span(q, (bh * Nq + r) * d, d, dtype, qr);
+        widen_span(dout, (bh * Nq + r) * d, d, dtype, dor);
+        three_step_row(qr, kh, vh, Nk, d, causal, sc, r, p, o_row, lse64 + i);
+        prob_row(qr, kh, Nk, d, causal, sc, r, p);
+        D64[i] = dprob_row(dor, vh, p, Nk, d, dp);
+    }
+    free(buf);
+    return FA_ORACLE_OK;
+}
+
+/* dK and dV of selected keys (sel_bh[i], sel_key[i]), given every row's statistics
+ * of the heads involved (lse64_all and D64_all, [B*H*Nq], from
+ * fa_ref_bwd_rowstats_f64): P[r, j] = exp(S[r, j] - lse_r),
+ * dv_j = sum_r P[r, j] do_r, dk_j = scale * sum_r P[r, j] (dP[r, j] - D_r) q_r. */
+int fa_ref_bwd_dkv_keys_f64(const void* q, const void* k, const void* v, const void* dout,
+                            int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                            float scale, int dtype, const double* lse64_all,
+                            const double* D64_all, int64_t n_sel, const int64_t* sel_bh,
+                            const int64_t* sel_key, double* dk64, double* dv64)
+{
+    int rc = check_bwd_raw(q, k, v, dout, B, H, Nq, Nk, d, dtype);
+    if (rc)
+        return rc;
+    if (!lse64_all || !D64_all || n_sel < 0 ||
+        (n_sel > 0 && (!sel_bh || !sel_key || !dk64 || !dv64)))
+        return FA_ORACLE_EINVAL;
+    for (int64_t i = 0; i < n_sel; ++i)
+        if (sel_bh[i] < 0 || sel_bh[i] >= B * H || sel_key[i] < 0 || sel_key[i] >= Nk)
+            return FA_ORACLE_EINVAL;
+    double* buf = (double*)malloc((size_t)(2 * Nq * d + 2 * d) * sizeof(double));
+    if (!buf)
+        return FA_ORACLE_ENOMEM;
+    double *qh = buf, *doh = qh + Nq * d, *kr = doh + Nq * d, *vr = kr + d;
+    const double sc = (double)scale;
+    int64_t cur = -1;
+    for (int64_t i = 0; i < n_sel; ++i) {
+        const int64_t bh = sel_bh[i], j = sel_key[i];
+        if (bh != cur) {
+            widen_span(q, bh * Nq * d, Nq * d, dtype, qh);
+            widen_span(dout, bh * Nq * d, Nq * d, dtype, doh);
+            cur = bh;
+        }
+        widen_span(k, (bh * Nk + j) * d, d, dtype, kr);
+        widen_span(v, (bh * Nk + j) * d, d, dtype, vr);
+        double* dkj = dk64 + i * d;
+        double* dvj = dv64 + i * d;
+        for (int64_t t = 0; t < d; ++t) {
+            dkj[t] = 0.0;
+            dvj[t] = 0.0;
+        }
+        for (int64_t r = 0; r < Nq; ++r) {
+            const double s = score(qh + r * d, kr, d, sc, causal, r, j);
+            if (s == -INFINITY)
+                continue; /* masked: P[r, j] = 0 */
+            const double p = exp(s - lse64_all[bh * Nq + r]);
+            double dp = 0.0;
+            for (int64_t t = 0; t < d; ++t)
+                dp += doh[r * d + t] * vr[t];
+            const double ds = p * (dp - D64_all[bh * Nq + r]);
+            for (int64_t t = 0; t < d; ++t) {
+                dvj[t] += p * doh[r * d + t];
+                dkj[t] += sc * ds * qh[r * d + t];
+            }
+        }
+    }
+    free(buf);
+    return FA_ORACLE_OK;
+}
+
+/* Host counterpart of the GPU backward: dq, dk, dv of every head, rounded to dtype. */
+int fa_bwd_ref(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
+               void* dv, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+               float scale, int dtype)
+{
+    int rc = check_bwd_raw(q, k, v, dout, B, H, Nq, Nk, d, dtype);
+    if (rc)
+        return rc;
+    if (!dq || !dk || !dv)
+        return FA_ORACLE_EINVAL;
+    double* g = (double*)malloc((size_t)(Nq * d + 2 * Nk * d) * sizeof(double));
+    if (!g)
+        return FA_ORACLE_ENOMEM;
+    for (int64_t bh = 0; bh < B * H && rc == FA_ORACLE_OK; ++bh) {
+        rc = fa_ref_bwd_head_f64(q, k, v, dout, B, H, Nq, Nk, d, causal, scale, dtype, bh, g,
+                                 g + Nq * d, g + Nq * d + Nk * d);
+        if (rc)
+            break;
+        for (int64_t i = 0; i < Nq * d; ++i)
+            store_rounded(g[i], dtype, dq, bh * Nq * d + i);
+        for (int64_t i = 0; i < Nk * d; ++i) {
+            store_rounded(g[Nq * d + i], dtype, dk, bh * Nk * d + i);
+            store_rounded(g[Nq * d + Nk * d + i], dtype, dv, bh * Nk * d + i);
+        }
+    }
+    free(g);
     return rc;
 }

@@ -5,7 +5,9 @@ source — compiled into a temporary library, never touching the real one — an
 checks that at least one pin of the battery below rejects it.  The first cases
 are the blog/article's own troubleshooting entry (a rescale factor forgotten in
 the running sum — "手写"/CUTLASS article section 3.3 and its section 6.3 table);
-the rest are a dropped scale, an inverted mask, a wrong index, a wrong sign.
+the rest are a dropped scale, an inverted mask, a wrong index, a wrong sign, and in
+the gradients a dropped softmax-Jacobian term, a flipped sign, an unweighted D, a
+dropped scale and wrong operands.
 """
 import json
 import math
@@ -37,6 +39,18 @@ MUTANTS = {
                                "o_row[t] += s[kk] * v[kk * d + (d - 1 - t)];"),
     "lse_wrong_sign": ("*lse = m + log(l);", "*lse = m - log(l);"),
     "online_lse_wrong_sign": ("*lse = run[0] + log(run[1]);", "*lse = run[0] - log(run[1]);"),
+    # gradients (part 3): the softmax-Jacobian term, signs, scales and operands
+    "bwd_D_dropped": ("const double ds = p[kk] * (dp[kk] - D);",
+                      "const double ds = p[kk] * dp[kk];"),
+    "bwd_dS_wrong_sign": ("const double ds = p[kk] * (dp[kk] - D);",
+                          "const double ds = p[kk] * (D - dp[kk]);"),
+    "bwd_D_not_weighted": ("D += p[kk] * dp[kk];", "D += dp[kk];"),
+    "bwd_dq_scale_dropped": ("dq[r * d + t] += scale * ds * k[kk * d + t];",
+                             "dq[r * d + t] += ds * k[kk * d + t];"),
+    "bwd_dk_uses_k": ("dk[kk * d + t] += scale * ds * q_row[t];",
+                      "dk[kk * d + t] += scale * ds * k[kk * d + t];"),
+    "bwd_dv_uses_dp": ("dv[kk * d + t] += p[kk] * do_row[t];",
+                       "dv[kk * d + t] += dp[kk] * do_row[t];"),
 }
 
 
@@ -95,9 +109,37 @@ def _pins(L):
         np.testing.assert_allclose(ab, [m, 2.5 * ca + 0.7 * cb, 1.0 * ca + 0.5 * cb,
                                         -2.0 * ca + 4.0 * cb], rtol=1e-15)
 
+    def bwd_finite_differences():
+        rng = np.random.default_rng(6)
+        q, k, v, dout = (rng.standard_normal((4, 3)) for _ in range(4))
+        for causal in (False, True):
+            got = oracle.attention_bwd_f64(q, k, v, dout, causal, 0.6, L=L)
+            h = 1e-5
+            for which in range(3):
+                for idx in np.ndindex(4, 3):
+                    args = [q.copy(), k.copy(), v.copy()]
+                    args[which][idx] += h
+                    up = np.sum(dout * oracle.attention_f64(*args, causal, 0.6, L=L)[0])
+                    args[which][idx] -= 2 * h
+                    dn = np.sum(dout * oracle.attention_f64(*args, causal, 0.6, L=L)[0])
+                    assert abs((up - dn) / (2 * h) - got[which][idx]) < 1e-7
+
+    def bwd_torch_autograd():
+        import torch
+        rng = np.random.default_rng(8)
+        q, k, v, dout = (rng.standard_normal((12, 4)) for _ in range(4))
+        t = [torch.from_numpy(a).clone().requires_grad_(True) for a in (q, k, v)]
+        torch.nn.functional.scaled_dot_product_attention(
+            *(x[None] for x in t), scale=0.5)[0].backward(torch.from_numpy(dout))
+        got = oracle.attention_bwd_f64(q, k, v, dout, False, 0.5, L=L)
+        for g, x in zip(got, t):
+            np.testing.assert_allclose(g, x.grad.numpy(), rtol=1e-10, atol=1e-12)
+
     for name, fn in [("worked_example", worked_example), ("torch_sdpa", torch_sdpa),
                      ("lse_scipy", lse_scipy), ("part2_vs_part1", part2_vs_part1),
-                     ("merge_closed_form", merge_closed_form)]:
+                     ("merge_closed_form", merge_closed_form),
+                     ("bwd_finite_differences", bwd_finite_differences),
+                     ("bwd_torch_autograd", bwd_torch_autograd)]:
         check(name, fn)
     return failed
 
