@@ -18,7 +18,7 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH = 0, 1, 2, 3
 
 # symbols include/fa.h declares
 EXPORTS = ("fa_fwd", "fa_fwd_split", "fa_fwd_split_workspace", "fa_merge", "fa_split_hint",
-           "fa_status_str", "fa_tile_rows")
+           "fa_bwd", "fa_bwd_workspace", "fa_status_str", "fa_tile_rows")
 
 _lib = None
 
@@ -56,6 +56,12 @@ def lib() -> ctypes.CDLL:
         L.fa_merge.restype = ctypes.c_int
         L.fa_split_hint.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
         L.fa_split_hint.restype = ctypes.c_int
+        L.fa_bwd.argtypes = [ctypes.c_void_p] * 9 + [i64, i64, i64, i64, i64, ctypes.c_int,
+                                                      ctypes.c_float, ctypes.c_int,
+                                                      ctypes.c_void_p, i64, ctypes.c_void_p]
+        L.fa_bwd.restype = ctypes.c_int
+        L.fa_bwd_workspace.argtypes = [i64, i64, i64, i64]
+        L.fa_bwd_workspace.restype = i64
         _lib = L
     return _lib
 
@@ -88,6 +94,18 @@ def fa_merge_raw(o_parts: int, lse_parts: int, n_parts: int, B: int, H: int, Nq:
     """Direct call of fa_merge with integer device pointers; returns the status code."""
     return lib().fa_merge(o_parts, lse_parts, int(n_parts), B, H, Nq, d, o, lse, int(dtype),
                           stream)
+
+
+def fa_bwd_raw(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int,
+               B: int, H: int, Nq: int, Nk: int, d: int, causal: int, scale: float, dtype: int,
+               workspace: int, workspace_bytes: int, stream: int) -> int:
+    """Direct call of fa_bwd with integer device pointers; returns the status code."""
+    return lib().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, int(causal),
+                        float(scale), int(dtype), workspace, int(workspace_bytes), stream)
+
+
+def fa_bwd_workspace(B: int, H: int, Nq: int, d: int) -> int:
+    return lib().fa_bwd_workspace(B, H, Nq, d)
 
 
 def fa_fwd_split_workspace(B: int, H: int, Nq: int, d: int, n_splits: int) -> int:
@@ -176,6 +194,36 @@ def fa_merge(o_parts, lse_parts, dtype=None, o=None, lse=None, stream=None):
     if st != FA_OK:
         raise FAError(st)
     return o, lse
+
+
+def fa_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, dq=None,
+           dk=None, dv=None, workspace=None, stream=None):
+    """dQ, dK, dV of the attention forward (fa_bwd) from the forward's o and lse and the
+    output gradient dout; the fp32 workspace for D = rowsum(dO o O) is allocated with
+    torch when not given."""
+    import torch
+    B, H, Nq, Nk, d = _check_qkv(q, k, v)
+    for name, t in (("o", o), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor shaped and typed like q")
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(max(16, fa_bwd_workspace(B, H, Nq, d)), dtype=torch.uint8,
+                                device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Nq, Nk, d,
+                    int(bool(causal)), scale, code, workspace.data_ptr(),
+                    workspace.numel() * workspace.element_size(), stream.cuda_stream)
+    if st != FA_OK:
+        raise FAError(st)
+    return dq, dk, dv
 
 
 def fa_fwd(q, k, v, causal: bool = False, scale: float | None = None, o=None, lse=None,

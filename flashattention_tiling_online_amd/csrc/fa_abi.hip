@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include "../../include/fa.h"
+#include "fa_bwd.hpp"
 #include "fa_fwd_f32.hpp"
 #include "fa_fwd_mfma16.hpp"
 #include "fa_merge.hpp"
@@ -325,6 +326,124 @@ extern "C" int fa_split_hint(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
     if (s > 16)
         s = 16;
     return (int)s;
+}
+
+// ---- backward ------------------------------------------------------------
+
+namespace {
+
+template <typename T, int D, bool C>
+hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        int64_t BH, int64_t Nq, int64_t Nk, float scale, float* delta,
+                        hipStream_t stream)
+{
+    using P = fa::BwdTile<D>;
+    fa::BwdParams<T> prm;
+    prm.q = static_cast<const T*>(q);
+    prm.k = static_cast<const T*>(k);
+    prm.v = static_cast<const T*>(v);
+    prm.o = static_cast<const T*>(o);
+    prm.dout = static_cast<const T*>(dout);
+    prm.lse = lse;
+    prm.delta = delta;
+    prm.dq = static_cast<T*>(dq);
+    prm.dk = static_cast<T*>(dk);
+    prm.dv = static_cast<T*>(dv);
+    prm.Nq = (int)Nq;
+    prm.Nk = (int)Nk;
+    prm.c2 = scale_log2e(scale);
+    prm.scale = scale;
+    hipError_t err;
+    const int64_t rows = BH * Nq;
+    if (rows > 0) {  // D = rowsum(dO o O)
+        const int rpb = 256 / (D / 4);
+        const T* po = prm.o;
+        const T* pd = prm.dout;
+        int64_t r = rows;
+        void* a0[] = {(void*)&po, (void*)&pd, (void*)&delta, (void*)&r};
+        err = hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_delta_kernel<T, D>),
+                              dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), a0, 0, stream);
+        if (err != hipSuccess)
+            return err;
+    }
+    void* args[] = {(void*)&prm};
+    prm.n_tiles = (int)((Nk + P::ROWS - 1) / P::ROWS);  // dK, dV (zeros when Nq == 0)
+    err = hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dkv_kernel<T, D, C>),
+                          dim3((unsigned)(prm.n_tiles * BH)), dim3(P::NT), args, 0, stream);
+    if (err != hipSuccess || rows == 0)
+        return err;
+    prm.n_tiles = (int)((Nq + P::ROWS - 1) / P::ROWS);  // dQ
+    return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dq_kernel<T, D, C>),
+                           dim3((unsigned)(prm.n_tiles * BH)), dim3(P::NT), args, 0, stream);
+}
+
+template <typename T>
+hipError_t launch_bwd_d(int64_t d, int causal, const void* q, const void* k, const void* v,
+                        const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                        void* dv, int64_t BH, int64_t Nq, int64_t Nk, float scale, float* delta,
+                        hipStream_t s)
+{
+    if (d == 128)
+        return causal ? launch_bwd_t<T, 128, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, Nq, Nk, scale, delta, s)
+                      : launch_bwd_t<T, 128, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Nq, Nk, scale, delta, s);
+    return causal ? launch_bwd_t<T, 64, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, Nq, Nk, scale, delta, s)
+                  : launch_bwd_t<T, 64, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Nq, Nk, scale, delta, s);
+}
+
+}  // namespace
+
+extern "C" int64_t fa_bwd_workspace(int64_t B, int64_t H, int64_t Nq, int64_t d)
+{
+    if (B < 0 || H < 0 || Nq < 0 || (d != 64 && d != 128))
+        return -1;
+    return round_up(B * H * Nq * 4, kAlign);
+}
+
+extern "C" fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                              float scale, fa_dtype_t dtype, void* workspace,
+                              int64_t workspace_bytes, fa_stream_t stream)
+{
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
+        return FA_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype))
+        return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1)
+        return FA_ERR_INVALID_ARG;
+    if (!(scale > 0.0f) || !isfinite(scale))
+        return FA_ERR_INVALID_ARG;
+    if ((d != 64 && d != 128) || dtype == FA_DTYPE_F32)
+        return FA_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0 || (Nq == 0 && Nk == 0))
+        return FA_OK;  // nothing to compute
+    if (Nk == 0)
+        return FA_ERR_INVALID_ARG;  // queries without keys: the forward is undefined
+    if (!k || !v || !dk || !dv || !aligned(k, 16) || !aligned(v, 16) || !aligned(dk, 16) ||
+        !aligned(dv, 16))
+        return FA_ERR_INVALID_ARG;
+    if (Nq > 0) {
+        if (!q || !o || !lse || !dout || !dq || !aligned(q, 16) || !aligned(o, 16) ||
+            !aligned(dout, 16) || !aligned(dq, 16) || !aligned(lse, 4))
+            return FA_ERR_INVALID_ARG;
+        if (!workspace || !aligned(workspace, 16) ||
+            workspace_bytes < fa_bwd_workspace(B, H, Nq, d))
+            return FA_ERR_INVALID_ARG;
+    }
+    const int64_t lim = INT32_MAX;
+    if (Nq * d > lim || Nk * d > lim || B * H > lim || B * H * ((Nq + 127) / 128) > lim ||
+        B * H * ((Nk + 127) / 128) > lim || B * H * Nq / 8 > lim)
+        return FA_ERR_INVALID_ARG;
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    float* delta = static_cast<float*>(workspace);
+    const hipError_t err =
+        dtype == FA_DTYPE_BF16
+            ? launch_bwd_d<__bf16>(d, causal, q, k, v, o, lse, dout, dq, dk, dv, B * H, Nq, Nk,
+                                   scale, delta, hs)
+            : launch_bwd_d<_Float16>(d, causal, q, k, v, o, lse, dout, dq, dk, dv, B * H, Nq, Nk,
+                                     scale, delta, hs);
+    return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 extern "C" const char* fa_status_str(fa_status_t status)

@@ -1,0 +1,404 @@
+// fa_bwd.hpp — gradients of the fused attention forward on gfx950 (bf16 / fp16 inputs).
+//
+// The backward pass recomputes the scores from Q, K and the forward's row log-sum-exp
+// L instead of storing P (course page "05_flash_attention.py", flash_attention_backward;
+// "Flash Attention" blog page, Algorithm 4):
+//     P = exp(S - L),  dV = P^T dO,  dP = dO V^T,  D = rowsum(dO o O),
+//     dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q,
+// with S = scale Q K^T masked as in the forward.  D uses the O the forward stored.
+//
+// Three kernels, no atomics, so the results are deterministic:
+//   * fa_bwd_delta_kernel: D per query row (memory-bound, one row per D/4 threads);
+//   * fa_bwd_dkv_kernel: one workgroup per 128-key tile (4 waves x 32 keys, lane =
+//     key), looping over 64-query tiles: S = Q K^T and dP = dO V^T with K and V in
+//     registers as the B operands, then dV^T += dO^T P and dK^T += Q^T dS with P and
+//     dS rounded to T straight from the accumulators;
+//   * fa_bwd_dq_kernel: one workgroup per 128-query tile (4 waves x 32 queries, lane =
+//     query, the forward's orientation), looping over 64-key tiles: S^T = K Q^T and
+//     dP^T = V dO^T with Q and dO in registers, then dQ^T += K^T dS^T.
+// Both main kernels stage row tiles and transposed tiles through LDS in the layouts
+// of fa_tiles.hpp; exp is exp2 with scale * log2(e) folded into one FMA and L taken in
+// base 2.
+#pragma once
+
+#include "fa_tiles.hpp"
+
+namespace fa {
+
+template <typename T>
+struct BwdParams {
+    const T* q;       // [bh, Nq, D]
+    const T* k;       // [bh, Nk, D]
+    const T* v;       // [bh, Nk, D]
+    const T* o;       // [bh, Nq, D], the forward's output
+    const T* dout;    // [bh, Nq, D]
+    const float* lse; // [bh, Nq], the forward's natural-log row log-sum-exp
+    float* delta;     // [bh, Nq], D = rowsum(dO o O) (written by the delta kernel)
+    T* dq;            // [bh, Nq, D]
+    T* dk;            // [bh, Nk, D]
+    T* dv;            // [bh, Nk, D]
+    int Nq, Nk;
+    int n_tiles;      // tiles per head of the kernel's outer dimension
+    float c2;         // scale * log2(e)
+    float scale;
+};
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// ---------------------------------------------------------------------------
+// D = rowsum(dO o O)
+// ---------------------------------------------------------------------------
+
+template <typename T, int D>
+__global__ __launch_bounds__(256)
+void fa_bwd_delta_kernel(const T* __restrict__ O, const T* __restrict__ dO,
+                         float* __restrict__ delta, int64_t rows)
+{
+    constexpr int TPR = D / 4;  // threads per row, 4 elements each
+    typedef T T4 __attribute__((ext_vector_type(4)));
+    const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+    const int t = (int)(threadIdx.x % TPR);
+    float acc = 0.f;
+    if (row < rows) {
+        const T4 a = *reinterpret_cast<const T4*>(O + row * D + 4 * t);
+        const T4 b = *reinterpret_cast<const T4*>(dO + row * D + 4 * t);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            acc += (float)a[e] * (float)b[e];
+    }
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m /= 2)
+        acc += __shfl_xor(acc, m);
+    if (row < rows && t == 0)
+        delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// shared tile staging (plain loads; every thread of the workgroup takes part)
+// ---------------------------------------------------------------------------
+
+template <int D>
+struct BwdTile {
+    static constexpr int NW = 4;                 // waves per workgroup
+    static constexpr int NT = 64 * NW;           // threads
+    static constexpr int ROWS = 32 * NW;         // rows of the outer dimension per workgroup
+    static constexpr int TILE = 64;              // rows of the inner dimension per step
+    static constexpr int RSTR = 2 * D + 16;      // row-tile stride (bytes)
+    static constexpr int TSTR = 2 * TILE + 16;   // transposed-tile stride (bytes)
+    static constexpr int RT = TILE * RSTR;       // bytes of one row tile
+    static constexpr int TT = D * TSTR;          // bytes of one transposed tile
+    static constexpr int DC = D / 16;            // 16-wide chunks of the D contraction
+    static constexpr int DB = D / 32;            // 32-wide blocks of D
+};
+
+// Rows [tile*64, tile*64 + 64) of a [nrows, D] head matrix into a padded row tile.
+template <int D, int NT, typename T>
+__device__ __forceinline__ void load_row_tile(const T* head, int tile, int nrows, char* dst,
+                                              int tid)
+{
+    constexpr int CPR = (2 * D) / 16;  // 16-byte chunks per row
+    constexpr int N = 64 * CPR;
+    const __amdgpu_buffer_rsrc_t r = rows_rsrc<D>(head, tile * 64, nrows);
+#pragma unroll
+    for (int i = 0; i < N / NT; ++i) {
+        const int c = tid + i * NT;
+        const int row = c / CPR, ch = c - (c / CPR) * CPR;
+        const u32x4 w = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (row * D + ch * 8) * 2, 0, 0));
+        *reinterpret_cast<u32x4*>(dst + row * (2 * D + 16) + ch * 16) = w;
+    }
+}
+
+// The same rows, transposed into a [D, 64] tile in accumulator order (fa_tiles.hpp).
+template <int D, int NT, typename T>
+__device__ __forceinline__ void load_t_tile(const T* head, int tile, int nrows, char* dst, int tid)
+{
+#pragma unroll
+    for (int i = 0; i < (4 * D) / NT; ++i) {
+        const int b = tid + i * NT;  // one 4-row x 4-column block
+        const int dq = (b & 3) + 4 * (b >> 6);
+        const int kg = ((b >> 2) & 3) + 4 * (((b >> 4) & 1) + 2 * ((b >> 5) & 1));
+        u32x2 r[4];
+        load_v_block<D>(head, tile, nrows, kg, dq, r);
+        store_vt_block<2 * 64 + 16>(dst, kg, dq, r);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per 128 keys, lane = key
+// ---------------------------------------------------------------------------
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(BwdTile<D>::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_bwd_dkv_kernel(const BwdParams<T> prm)
+{
+    using P = BwdTile<D>;
+    using M = Mfma16<T>;
+    using vec = typename M::vec;
+    typedef T T4 __attribute__((ext_vector_type(4)));
+    constexpr int QR = 0, DOR = P::RT, QT = 2 * P::RT, DOT = 2 * P::RT + P::TT,
+                  LS = 2 * P::RT + 2 * P::TT, DS = LS + 64 * 4;
+    __shared__ __attribute__((aligned(1024))) char smem[DS + 64 * 4];
+    const char* const sm = smem;
+    const int Nq = prm.Nq, Nk = prm.Nk;
+
+    const int logical = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+    const int bh = logical / prm.n_tiles;
+    const int kt = logical - bh * prm.n_tiles;  // key tile: heaviest (causal) first
+    const int k0 = kt * P::ROWS;
+
+    const int tid = (int)threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int kl = lane & 31;
+    const int hh = lane >> 5;
+    const int kw0 = k0 + 32 * wave;
+    const int my_k = kw0 + kl;
+
+    const T* Qh = prm.q + (size_t)bh * Nq * D;
+    const T* dOh = prm.dout + (size_t)bh * Nq * D;
+    const float* Lh = prm.lse + (size_t)bh * Nq;
+    const float* Dh = prm.delta + (size_t)bh * Nq;
+
+    // K and V rows of this lane's key as the B operands (lane half hh: d-chunk 8hh)
+    vec kf[P::DC], vf[P::DC];
+#pragma unroll
+    for (int c = 0; c < P::DC; ++c) {
+        u32x4 rk = {0u, 0u, 0u, 0u}, rv = {0u, 0u, 0u, 0u};
+        if (my_k < Nk) {
+            const size_t off = ((size_t)bh * Nk + my_k) * D + 16 * c + 8 * hh;
+            rk = *reinterpret_cast<const u32x4*>(prm.k + off);
+            rv = *reinterpret_cast<const u32x4*>(prm.v + off);
+        }
+        kf[c] = __builtin_bit_cast(vec, rk);
+        vf[c] = __builtin_bit_cast(vec, rv);
+    }
+    f32x16 dvt[P::DB], dkt[P::DB];
+#pragma unroll
+    for (int db = 0; db < P::DB; ++db) {
+        dvt[db] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+        dkt[db] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    }
+
+    // query tiles: causal ones before the first key of the workgroup see none of it
+    const int nqt = (Nq + P::TILE - 1) / P::TILE;
+    const int i0 = CAUSAL ? min(nqt, k0 / P::TILE) : 0;
+    const int iw0 = CAUSAL ? kw0 / P::TILE : 0;  // first query tile this wave sees
+
+    const int rbase = kl * P::RSTR + hh * 16;   // row-tile operand: row kl, chunk 8hh
+    const int tbase = kl * P::TSTR + hh * 16;   // transposed-tile operand
+
+    for (int i = i0; i < nqt; ++i) {
+        __syncthreads();  // the previous tile is consumed
+        load_row_tile<D, P::NT>(Qh, i, Nq, smem + QR, tid);
+        load_row_tile<D, P::NT>(dOh, i, Nq, smem + DOR, tid);
+        load_t_tile<D, P::NT>(Qh, i, Nq, smem + QT, tid);
+        load_t_tile<D, P::NT>(dOh, i, Nq, smem + DOT, tid);
+        if (tid < 64) {
+            const int q = i * P::TILE + tid;
+            // rows past Nq: P = exp2(-inf) = 0
+            reinterpret_cast<float*>(smem + LS)[tid] = q < Nq ? Lh[q] * kLog2e : __builtin_inff();
+            reinterpret_cast<float*>(smem + DS)[tid] = q < Nq ? Dh[q] : 0.f;
+        }
+        __syncthreads();
+        if (i < iw0)
+            continue;
+        const bool diag = CAUSAL && (i * P::TILE < kw0 + 31);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            // S = Q K^T and dP = dO V^T for queries 32qb .. 32qb+31 of the tile
+            f32x16 s = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+            f32x16 dp = s;
+#pragma unroll
+            for (int c = 0; c < P::DC; ++c) {
+                const vec a = *reinterpret_cast<const vec*>(sm + QR + rbase + 32 * qb * P::RSTR + 32 * c);
+                s = M::mma(a, kf[c], s);
+                const vec b = *reinterpret_cast<const vec*>(sm + DOR + rbase + 32 * qb * P::RSTR + 32 * c);
+                dp = M::mma(b, vf[c], dp);
+            }
+            // P = 2^(s c2 - L2), dS = P (dP - D); register r holds query
+            // 32qb + 8(r/4) + 4hh + r%4 of the tile
+            vec pp[2], ps[2];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int qo = 32 * qb + 8 * g + 4 * hh;
+                const f32x4 l2 = *reinterpret_cast<const f32x4*>(sm + LS + qo * 4);
+                const f32x4 dd = *reinterpret_cast<const f32x4*>(sm + DS + qo * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g + e;
+                    float p = exp2_fast(fmaf(s[r], prm.c2, -l2[e]));
+                    if (diag && my_k > i * P::TILE + qo + e)
+                        p = 0.f;  // key after the query
+                    const float ds = p * (dp[r] - dd[e]);
+                    pp[r >> 3][r & 7] = (T)p;
+                    ps[r >> 3][r & 7] = (T)ds;
+                }
+            }
+            // dV^T += dO^T P, dK^T += Q^T dS over chunks 2qb, 2qb+1 of the tile
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int cc = 2 * qb + h;
+#pragma unroll
+                for (int db = 0; db < P::DB; ++db) {
+                    const vec a = *reinterpret_cast<const vec*>(sm + DOT + tbase + 32 * db * P::TSTR + 32 * cc);
+                    dvt[db] = M::mma(a, pp[h], dvt[db]);
+                    const vec b = *reinterpret_cast<const vec*>(sm + QT + tbase + 32 * db * P::TSTR + 32 * cc);
+                    dkt[db] = M::mma(b, ps[h], dkt[db]);
+                }
+            }
+        }
+    }
+
+    // epilogue: accumulator register r of block db holds d = 32db + 8(r/4) + 4hh + r%4
+    if (my_k < Nk) {
+        T* dkrow = prm.dk + ((size_t)bh * Nk + my_k) * D;
+        T* dvrow = prm.dv + ((size_t)bh * Nk + my_k) * D;
+#pragma unroll
+        for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                T4 wk, wv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    wk[e] = (T)(dkt[db][4 * a + e] * prm.scale);
+                    wv[e] = (T)dvt[db][4 * a + e];
+                }
+                *reinterpret_cast<T4*>(dkrow + 32 * db + 8 * a + 4 * hh) = wk;
+                *reinterpret_cast<T4*>(dvrow + 32 * db + 8 * a + 4 * hh) = wv;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per 128 queries, lane = query
+// ---------------------------------------------------------------------------
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(BwdTile<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
+void fa_bwd_dq_kernel(const BwdParams<T> prm)
+{
+    using P = BwdTile<D>;
+    using M = Mfma16<T>;
+    using vec = typename M::vec;
+    typedef T T4 __attribute__((ext_vector_type(4)));
+    constexpr int KR = 0, VR = P::RT, KTT = 2 * P::RT;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * P::RT + P::TT];
+    const char* const sm = smem;
+    const int Nq = prm.Nq, Nk = prm.Nk;
+
+    const int logical = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+    const int bh = logical / prm.n_tiles;
+    int qt = logical - bh * prm.n_tiles;
+    if (CAUSAL)
+        qt = prm.n_tiles - 1 - qt;  // longest rows first
+    const int q0 = qt * P::ROWS;
+
+    const int tid = (int)threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int ql = lane & 31;
+    const int hh = lane >> 5;
+    const int qw0 = q0 + 32 * wave;
+    const int my_q = qw0 + ql;
+
+    const T* Kh = prm.k + (size_t)bh * Nk * D;
+    const T* Vh = prm.v + (size_t)bh * Nk * D;
+
+    // Q and dO rows of this lane's query as the B operands
+    vec qf[P::DC], df[P::DC];
+#pragma unroll
+    for (int c = 0; c < P::DC; ++c) {
+        u32x4 rq = {0u, 0u, 0u, 0u}, rd = {0u, 0u, 0u, 0u};
+        if (my_q < Nq) {
+            const size_t off = ((size_t)bh * Nq + my_q) * D + 16 * c + 8 * hh;
+            rq = *reinterpret_cast<const u32x4*>(prm.q + off);
+            rd = *reinterpret_cast<const u32x4*>(prm.dout + off);
+        }
+        qf[c] = __builtin_bit_cast(vec, rq);
+        df[c] = __builtin_bit_cast(vec, rd);
+    }
+    const float l2 = my_q < Nq ? prm.lse[(size_t)bh * Nq + my_q] * kLog2e : 0.f;
+    const float dd = my_q < Nq ? prm.delta[(size_t)bh * Nq + my_q] : 0.f;
+
+    f32x16 dqt[P::DB];
+#pragma unroll
+    for (int db = 0; db < P::DB; ++db)
+        dqt[db] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+
+    // key tiles, as in the forward: causal tiles after the workgroup's last query are
+    // skipped, a wave stops after its own last query, only its last tile is masked
+    int nkt = (Nk + P::TILE - 1) / P::TILE;
+    if (CAUSAL)
+        nkt = min(nkt, (min(q0 + P::ROWS, Nq) - 1) / P::TILE + 1);
+    const bool wave_active = qw0 < Nq;
+    int n_w = wave_active ? nkt : 0;
+    if (CAUSAL && wave_active)
+        n_w = min(nkt, min(qw0 + 31, Nq - 1) / P::TILE + 1);
+
+    const int rbase = ql * P::RSTR + hh * 16;
+    const int tbase = ql * P::TSTR + hh * 16;
+
+    for (int j = 0; j < nkt; ++j) {
+        __syncthreads();
+        load_row_tile<D, P::NT>(Kh, j, Nk, smem + KR, tid);
+        load_row_tile<D, P::NT>(Vh, j, Nk, smem + VR, tid);
+        load_t_tile<D, P::NT>(Kh, j, Nk, smem + KTT, tid);
+        __syncthreads();
+        if (j >= n_w)
+            continue;
+        // S^T = K Q^T, dP^T = V dO^T: register r of block kb holds key
+        // 32kb + 8(r/4) + 4hh + r%4 of the tile
+        f32x16 st[2], dpt[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            st[kb] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+            dpt[kb] = st[kb];
+#pragma unroll
+            for (int c = 0; c < P::DC; ++c) {
+                const vec a = *reinterpret_cast<const vec*>(sm + KR + rbase + 32 * kb * P::RSTR + 32 * c);
+                st[kb] = M::mma(a, qf[c], st[kb]);
+                const vec b = *reinterpret_cast<const vec*>(sm + VR + rbase + 32 * kb * P::RSTR + 32 * c);
+                dpt[kb] = M::mma(b, df[c], dpt[kb]);
+            }
+        }
+        const int key0 = j * P::TILE;
+        const bool mask = (key0 + P::TILE > Nk) || (CAUSAL && key0 + P::TILE - 1 > qw0);
+        const int last = CAUSAL ? min(Nk - 1, my_q) : Nk - 1;
+        vec ps[4];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int kb = cc >> 1, r = 8 * (cc & 1) + e;
+                float p = exp2_fast(fmaf(st[kb][r], prm.c2, -l2));
+                if (mask && key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3) > last)
+                    p = 0.f;
+                ps[cc][e] = (T)(p * (dpt[kb][r] - dd));
+            }
+        // dQ^T += K^T dS^T
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+            for (int db = 0; db < P::DB; ++db) {
+                const vec a = *reinterpret_cast<const vec*>(sm + KTT + tbase + 32 * db * P::TSTR + 32 * cc);
+                dqt[db] = M::mma(a, ps[cc], dqt[db]);
+            }
+    }
+
+    if (my_q < Nq) {
+        T* row = prm.dq + ((size_t)bh * Nq + my_q) * D;
+#pragma unroll
+        for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                T4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = (T)(dqt[db][4 * a + e] * prm.scale);
+                *reinterpret_cast<T4*>(row + 32 * db + 8 * a + 4 * hh) = w;
+            }
+    }
+}
+
+}  // namespace fa

@@ -44,46 +44,9 @@
 //     from (see update_max).
 #pragma once
 
-#include "fa_common.hpp"
+#include "fa_tiles.hpp"
 
 namespace fa {
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) char lds_char;
-
-template <typename T>
-struct Mfma16;
-
-template <>
-struct Mfma16<__bf16> {
-    typedef bf16x8 vec;
-    static __device__ __forceinline__ f32x16 mma(vec a, vec b, f32x16 c)
-    {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-    // acc + (sum of the two elements of a packed pair), fp32 accumulate
-    static __device__ __forceinline__ float dot_ones(uint32_t pair, float acc)
-    {
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
-    }
-};
-
-template <>
-struct Mfma16<_Float16> {
-    typedef f16x8 vec;
-    static __device__ __forceinline__ f32x16 mma(vec a, vec b, f32x16 c)
-    {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-    }
-    static __device__ __forceinline__ float dot_ones(uint32_t pair, float acc)
-    {
-        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
-    }
-};
 
 template <int D>
 struct Tile16 {
@@ -108,89 +71,6 @@ struct Tile16 {
     static constexpr int K0 = 0, K1 = KT, V0 = 2 * KT, V1 = 2 * KT + VT;
     static_assert(KT % 1024 == 0, "K tiles must be whole DMA blocks");
 };
-
-// Byte offset, inside a tile of the [rows, D] matrix in memory, that lane `lane` of
-// the 1-KB DMA block `blk` fetches for an LDS tile with row stride `str`: the LDS
-// byte it lands on is blk*1024 + 16*lane.  -1 for lanes that land on row padding
-// (they are masked off and fetch nothing).
-template <int D>
-__device__ __forceinline__ int dma_src(int blk, int lane, int str)
-{
-    const int pos = blk * 1024 + 16 * lane;
-    const int row = pos / str;
-    const int ch = (pos - row * str) / 16;
-    return ch < (2 * D) / 16 ? row * (2 * D) + ch * 16 : -1;
-}
-
-// Word 3 of a gfx9 buffer resource for untyped (raw) loads: 32-bit data format.
-constexpr int kRsrcWord3 = 0x00020000;
-
-// Buffer resource over rows [row0, nrows) of a [nrows, D] matrix: offsets past the
-// end read as zero.
-template <int D, typename T>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const T* base, int row0, int nrows)
-{
-    const int n = nrows > row0 ? nrows - row0 : 0;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base) + (size_t)row0 * D, 0,
-                                             n * D * (int)sizeof(T), kRsrcWord3);
-}
-
-// DMA one K or V tile (rows [tile*BC, tile*BC + BC) of a head) into the LDS tile at
-// `dst`: this wave's blocks wave, wave+NW, ... (< NB); src[i] is the lane's source
-// offset for its i-th block (-1: padding, lane masked off).  A device function (not
-// a lambda) so that the host pass never sees the builtin.
-template <int D, int NB, int PW, int NW, typename T>
-__device__ __forceinline__ void stage_tile(const T* head, int tile, int nrows, char* dst,
-                                           int wave, const int* src)
-{
-    const __amdgpu_buffer_rsrc_t r = rows_rsrc<D>(head, tile * 64, nrows);
-#pragma unroll
-    for (int i = 0; i < PW; ++i) {
-        const int blk = wave + NW * i;
-        if (blk < NB && src[i] >= 0)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + blk * 1024), 16, src[i],
-                                                     0, 0, 0);
-    }
-}
-
-// V staging of one thread: the 4-key x 4-dim block (keys 4kg..4kg+3, dims
-// 4dq..4dq+3) of 64-key tile `tile`, loaded as four 8-byte rows (rows past nrows
-// read 0).
-template <int D, typename T>
-__device__ __forceinline__ void load_v_block(const T* head, int tile, int nrows, int kg, int dq,
-                                             u32x2* r)
-{
-    const __amdgpu_buffer_rsrc_t rs = rows_rsrc<D>(head, tile * 64, nrows);
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-        r[m] = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, ((4 * kg + m) * D + 4 * dq) * 2, 0, 0));
-}
-
-// Transpose the block and write it as four V^T row segments (dim 4dq+e, 4 keys each)
-// at LDS byte `dst` + (4dq+e)*VTSTR + 2*slot, where the keys of 16-key chunk cc are
-// stored in the order the P registers hold them: slots 16cc + 8h + 0..3 hold keys
-// 16cc + 4h + 0..3 and slots 16cc + 8h + 4..7 hold keys 16cc + 8 + 4h + 0..3.
-template <int VTSTR>
-__device__ __forceinline__ void store_vt_block(char* dst, int kg, int dq, const u32x2* r)
-{
-    const int cc = kg >> 2, x = kg & 3;
-    const int slot = 16 * cc + 4 * (((x & 1) << 1) | (x >> 1));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const uint32_t a0 = (e < 2) ? r[0].x : r[0].y, a1 = (e < 2) ? r[1].x : r[1].y;
-        const uint32_t a2 = (e < 2) ? r[2].x : r[2].y, a3 = (e < 2) ? r[3].x : r[3].y;
-        u32x2 w;
-        if (e & 1) {
-            w.x = (a0 >> 16) | (a1 & 0xffff0000u);
-            w.y = (a2 >> 16) | (a3 & 0xffff0000u);
-        } else {
-            w.x = (a0 & 0xffffu) | (a1 << 16);
-            w.y = (a2 & 0xffffu) | (a3 << 16);
-        }
-        *reinterpret_cast<u32x2*>(dst + (4 * dq + e) * VTSTR + 2 * slot) = w;
-    }
-}
 
 template <typename T, int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(Tile16<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))

@@ -1,7 +1,7 @@
 /*
  * fa.h — C-ABI of the MI355X (gfx950) fused attention forward library, libfa.so.
  *
- * The entry points compute, for every batch b and head h,
+ * The forward entry points compute, for every batch b and head h,
  *
  *     S = scale * Q[b,h] K[b,h]^T            (Nq x Nk, never written to memory)
  *     S[q,k] = -inf where causal and k > q   (key k visible to query q iff k <= q)
@@ -155,6 +155,45 @@ fa_status_t fa_merge(const float* o_parts, const float* lse_parts, int n_parts, 
  * (two for fp32) and at most 16 ranges.  0 for unsupported or empty arguments. */
 int fa_split_hint(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
                   fa_dtype_t dtype);
+
+/*
+ * fa_bwd — gradients of the forward above by recomputation: from Q, K, V, the
+ * forward's O and L and the output gradient dO, the gradients of sum(dO o O):
+ *
+ *     P = exp(S - L)              (S scaled and masked as in fa_fwd)
+ *     dV = P^T dO,  dP = dO V^T,  D = rowsum(dO o O),  dS = P o (dP - D),
+ *     dQ = scale dS K,  dK = scale dS^T Q
+ *
+ * as the "05_flash_attention.py" course page (flash_attention_backward) and the
+ * "Flash Attention" blog page (Algorithm 4 and the softmax-Jacobian derivation: D_i =
+ * P_i . dP_i = do_i . o_i) define them.  P is never stored; D uses the O passed in.
+ *
+ * Arguments (DEVICE pointers owned by the caller, contiguous, d fastest):
+ *   q, o, dout  [B, H, Nq, d]  `dtype`; o and lse as fa_fwd returned them
+ *   k, v        [B, H, Nk, d]  `dtype`
+ *   lse         [B, H, Nq]     fp32
+ *   dq          [B, H, Nq, d]  output, `dtype`, rounded to nearest-even
+ *   dk, dv      [B, H, Nk, d]  outputs, same
+ *   B, H, Nq, Nk, d, causal, scale: as fa_fwd
+ *   dtype       FA_DTYPE_BF16 or FA_DTYPE_F16 (FA_DTYPE_F32: FA_ERR_UNSUPPORTED)
+ *   workspace   DEVICE buffer, 16-byte aligned, at least fa_bwd_workspace(B, H, Nq, d)
+ *               bytes: D as fp32 [B, H, Nq]
+ *
+ * Alignment: as fa_fwd (16 bytes for every tensor, 4 for lse).  Behaviour:
+ * asynchronous on `stream` (three kernels, in order); deterministic (no atomics:
+ * bitwise-identical results for the same inputs); every argument error before any
+ * HIP call.  B*H == 0, or Nq == Nk == 0: FA_OK, nothing touched.  Nq == 0 < Nk:
+ * dk = dv = 0 are written (q, o, lse, dout, dq and the workspace may be NULL).
+ * Nk == 0 < Nq: FA_ERR_INVALID_ARG.  Limits as fa_fwd, with 128-row tiles.
+ */
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                   int64_t Nq, int64_t Nk, int64_t d, int causal, float scale, fa_dtype_t dtype,
+                   void* workspace, int64_t workspace_bytes, fa_stream_t stream);
+
+/* Workspace bytes fa_bwd needs (D as fp32, rounded up to 256); -1 for negative sizes or
+ * d outside {64, 128}. */
+int64_t fa_bwd_workspace(int64_t B, int64_t H, int64_t Nq, int64_t d);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* fa_status_str(fa_status_t status);

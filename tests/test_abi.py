@@ -156,6 +156,50 @@ def test_merge_validation_before_any_hip_call(kw, want):
     assert _merge(**kw) == want
 
 
+def _bwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, B=1, H=2, Nq=64, Nk=64, d=128,
+             causal=0, scale=0.1, dtype=fa.FA_DTYPE_BF16, workspace=P, workspace_bytes=1 << 20,
+             stream=0)
+    a.update(kw)
+    return fa.fa_bwd_raw(**a)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=fa.FA_DTYPE_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=5), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(B=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(o=0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dout=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dv=P + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=P + 1), fa.FA_ERR_INVALID_ARG),
+    (dict(workspace=0), fa.FA_ERR_INVALID_ARG),
+    (dict(workspace=P + 4), fa.FA_ERR_INVALID_ARG),
+    (dict(workspace_bytes=256), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=1 << 31), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_OK),
+    (dict(Nq=0, Nk=0, k=0, v=0, dk=0, dv=0), fa.FA_OK),
+])
+def test_bwd_validation_before_any_hip_call(kw, want):
+    assert _bwd(**kw) == want
+
+
+def test_bwd_workspace_size():
+    assert fa.fa_bwd_workspace(2, 8, 1024, 64) == 2 * 8 * 1024 * 4
+    assert fa.fa_bwd_workspace(1, 1, 3, 128) == 256
+    assert fa.fa_bwd_workspace(1, 1, 0, 64) == 0
+    assert fa.fa_bwd_workspace(1, 1, 8, 96) == -1
+    assert fa.fa_bwd_workspace(-1, 1, 8, 64) == -1
+
+
 def test_split_workspace_size():
     # n_splits * rows * d fp32 partial outputs, padded to 256 B, then n_splits * rows fp32 L
     rows = 2 * 8 * 1024
