@@ -368,9 +368,10 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
             return err;
     }
     void* args[] = {(void*)&prm};
-    prm.n_tiles = (int)((Nk + P::ROWS - 1) / P::ROWS);  // dK, dV (zeros when Nq == 0)
+    using PK = fa::DkvTile<D>;
+    prm.n_tiles = (int)((Nk + PK::KEYS - 1) / PK::KEYS);  // dK, dV (zeros when Nq == 0)
     err = hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dkv_kernel<T, D, C>),
-                          dim3((unsigned)(prm.n_tiles * BH)), dim3(P::NT), args, 0, stream);
+                          dim3((unsigned)(prm.n_tiles * BH)), dim3(PK::NT), args, 0, stream);
     if (err != hipSuccess || rows == 0)
         return err;
     prm.n_tiles = (int)((Nq + P::ROWS - 1) / P::ROWS);  // dQ

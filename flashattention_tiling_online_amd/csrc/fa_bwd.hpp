@@ -9,10 +9,11 @@
 //
 // Three kernels, no atomics, so the results are deterministic:
 //   * fa_bwd_delta_kernel: D per query row (memory-bound, one row per D/4 threads);
-//   * fa_bwd_dkv_kernel: one workgroup per 128-key tile (4 waves x 32 keys, lane =
-//     key), looping over 64-query tiles: S = Q K^T and dP = dO V^T with K and V in
-//     registers as the B operands, then dV^T += dO^T P and dK^T += Q^T dS with P and
-//     dS rounded to T straight from the accumulators;
+//   * fa_bwd_dkv_kernel: one workgroup per 128-key tile (8 waves: 4 blocks of 32 keys,
+//     lane = key, times the two 32-query halves of every 64-query tile), K and V
+//     resident in LDS: S = Q K^T and dP = dO V^T, then dV^T += dO^T P and
+//     dK^T += Q^T dS with P and dS rounded to T straight from the accumulators; the
+//     two halves' partial sums meet in LDS at the end;
 //   * fa_bwd_dq_kernel: one workgroup per 128-query tile (4 waves x 32 queries, lane =
 //     query, the forward's orientation), looping over 64-key tiles: S^T = K Q^T and
 //     dP^T = V dO^T with Q and dO in registers, then dQ^T += K^T dS^T.
@@ -128,31 +129,76 @@ __device__ __forceinline__ void load_t_tile(const T* head, int tile, int nrows, 
 // dK, dV: one workgroup per 128 keys, lane = key
 // ---------------------------------------------------------------------------
 
+template <int D>
+struct DkvTile {
+    static constexpr int NW = 8;                 // waves: 4 key blocks x 2 query halves
+    static constexpr int NT = 64 * NW;
+    static constexpr int KEYS = 128;             // keys per workgroup
+    static constexpr int TILE = 64;              // queries per step
+    static constexpr int RSTR = 2 * D + 16;
+    static constexpr int TSTR = 2 * TILE + 16;
+    static constexpr int DC = D / 16;
+    static constexpr int DB = D / 32;
+    // LDS: K and V of the workgroup's keys (resident), then per step Q and dO as
+    // row tiles and as transposed tiles, and the 64 queries' L2 and D
+    static constexpr int KS = 0;
+    static constexpr int VS = KEYS * RSTR;
+    static constexpr int QR = 2 * KEYS * RSTR;
+    static constexpr int DOR = QR + TILE * RSTR;
+    static constexpr int QT = DOR + TILE * RSTR;
+    static constexpr int DOT = QT + D * TSTR;
+    static constexpr int LS = DOT + D * TSTR;
+    static constexpr int DS = LS + TILE * 4;
+    static constexpr int LDS = DS + TILE * 4;
+    // thread blocks of 4 rows x 4 columns per staged [64, D] tile: 16 x D/4
+    static constexpr int BLOCKS = 16 * (D / 4);
+    // partial accumulators of the second query half, exchanged at the end
+    static constexpr int XCH = 4 * 2 * DB * 16 * 64 * 4;
+    static_assert(XCH <= LDS, "reduction buffer must fit the staging space");
+};
+
+// The 4-row x 4-column block b of a [64, D] tile (rows 4kg.., columns 4dq..): the
+// block -> (kg, dq) map keeps the transposed writes of a half-wave conflict-free.
+__device__ __forceinline__ int blk_dq(int b) { return (b & 3) + 4 * (b >> 6); }
+__device__ __forceinline__ int blk_kg(int b)
+{
+    return ((b >> 2) & 3) + 4 * (((b >> 4) & 1) + 2 * ((b >> 5) & 1));
+}
+
+// Write a loaded 4x4 block as four 8-byte row segments of a padded row tile.
+template <int RSTR>
+__device__ __forceinline__ void store_row_block(char* dst, int kg, int dq, const u32x2* r)
+{
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        *reinterpret_cast<u32x2*>(dst + (4 * kg + m) * RSTR + 8 * dq) = r[m];
+}
+
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(BwdTile<D>::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(DkvTile<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_bwd_dkv_kernel(const BwdParams<T> prm)
 {
-    using P = BwdTile<D>;
+    using P = DkvTile<D>;
     using M = Mfma16<T>;
     using vec = typename M::vec;
     typedef T T4 __attribute__((ext_vector_type(4)));
-    constexpr int QR = 0, DOR = P::RT, QT = 2 * P::RT, DOT = 2 * P::RT + P::TT,
-                  LS = 2 * P::RT + 2 * P::TT, DS = LS + 64 * 4;
-    __shared__ __attribute__((aligned(1024))) char smem[DS + 64 * 4];
+    __shared__ __attribute__((aligned(1024))) char smem[P::LDS];
     const char* const sm = smem;
     const int Nq = prm.Nq, Nk = prm.Nk;
 
     const int logical = xcd_remap((int)blockIdx.x, (int)gridDim.x);
     const int bh = logical / prm.n_tiles;
     const int kt = logical - bh * prm.n_tiles;  // key tile: heaviest (causal) first
-    const int k0 = kt * P::ROWS;
+    const int k0 = kt * P::KEYS;
 
     const int tid = (int)threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int kl = lane & 31;
     const int hh = lane >> 5;
-    const int kw0 = k0 + 32 * wave;
+    const int kblk = wave & 3;   // 32-key block of this wave
+    const int qh = wave >> 2;    // query half of every 64-query tile
+    const int kw0 = k0 + 32 * kblk;
     const int my_k = kw0 + kl;
 
     const T* Qh = prm.q + (size_t)bh * Nq * D;
@@ -160,19 +206,26 @@ void fa_bwd_dkv_kernel(const BwdParams<T> prm)
     const float* Lh = prm.lse + (size_t)bh * Nq;
     const float* Dh = prm.delta + (size_t)bh * Nq;
 
-    // K and V rows of this lane's key as the B operands (lane half hh: d-chunk 8hh)
-    vec kf[P::DC], vf[P::DC];
+    // K and V rows of the workgroup's keys, resident for the whole loop (rows past Nk
+    // read as zero; their gradients are not stored)
+    {
+        constexpr int CPR = (2 * D) / 16;
+        const T* Kh = prm.k + (size_t)bh * Nk * D;
+        const T* Vh = prm.v + (size_t)bh * Nk * D;
+        const __amdgpu_buffer_rsrc_t rk = rows_rsrc<D>(Kh, k0, Nk);
+        const __amdgpu_buffer_rsrc_t rv = rows_rsrc<D>(Vh, k0, Nk);
 #pragma unroll
-    for (int c = 0; c < P::DC; ++c) {
-        u32x4 rk = {0u, 0u, 0u, 0u}, rv = {0u, 0u, 0u, 0u};
-        if (my_k < Nk) {
-            const size_t off = ((size_t)bh * Nk + my_k) * D + 16 * c + 8 * hh;
-            rk = *reinterpret_cast<const u32x4*>(prm.k + off);
-            rv = *reinterpret_cast<const u32x4*>(prm.v + off);
+        for (int i = 0; i < (P::KEYS * CPR) / P::NT; ++i) {
+            const int c = tid + i * P::NT;
+            const int row = c / CPR, ch = c - (c / CPR) * CPR;
+            const int src = (row * D + ch * 8) * 2, dst = row * P::RSTR + ch * 16;
+            *reinterpret_cast<u32x4*>(smem + P::KS + dst) =
+                __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, src, 0, 0));
+            *reinterpret_cast<u32x4*>(smem + P::VS + dst) =
+                __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, src, 0, 0));
         }
-        kf[c] = __builtin_bit_cast(vec, rk);
-        vf[c] = __builtin_bit_cast(vec, rv);
     }
+
     f32x16 dvt[P::DB], dkt[P::DB];
 #pragma unroll
     for (int db = 0; db < P::DB; ++db) {
@@ -180,94 +233,136 @@ void fa_bwd_dkv_kernel(const BwdParams<T> prm)
         dkt[db] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     }
 
-    // query tiles: causal ones before the first key of the workgroup see none of it
+    // query tiles: causal ones before the workgroup's first key see none of its keys
     const int nqt = (Nq + P::TILE - 1) / P::TILE;
     const int i0 = CAUSAL ? min(nqt, k0 / P::TILE) : 0;
-    const int iw0 = CAUSAL ? kw0 / P::TILE : 0;  // first query tile this wave sees
+
+    // staging of Q and dO: each thread loads one 4x4 block of one tensor (d = 64:
+    // threads split between Q and dO) one tile ahead, and writes it both as rows and
+    // transposed
+    constexpr int PER = P::BLOCKS >= P::NT ? 2 : 1;  // tensors per thread
+    const int sb = P::BLOCKS >= P::NT ? tid : tid % P::BLOCKS;
+    const bool first_t = P::BLOCKS >= P::NT || tid < P::BLOCKS;  // Q (else dO)
+    const int s_kg = blk_kg(sb), s_dq = blk_dq(sb);
+    u32x2 sreg[PER][4];
+    auto load_tile = [&](int i) {
+        if (PER == 2) {
+            load_v_block<D>(Qh, i, Nq, s_kg, s_dq, sreg[0]);
+            load_v_block<D>(dOh, i, Nq, s_kg, s_dq, sreg[PER - 1]);
+        } else {
+            load_v_block<D>(first_t ? Qh : dOh, i, Nq, s_kg, s_dq, sreg[0]);
+        }
+    };
+    auto store_tile = [&](int i) {
+#pragma unroll
+        for (int t = 0; t < PER; ++t) {
+            const bool is_q = PER == 2 ? t == 0 : first_t;
+            store_row_block<P::RSTR>(smem + (is_q ? P::QR : P::DOR), s_kg, s_dq, sreg[t]);
+            store_vt_block<P::TSTR>(smem + (is_q ? P::QT : P::DOT), s_kg, s_dq, sreg[t]);
+        }
+        if (tid < P::TILE) {
+            const int q = i * P::TILE + tid;
+            // rows past Nq: P = exp2(-inf) = 0
+            reinterpret_cast<float*>(smem + P::LS)[tid] = q < Nq ? Lh[q] * kLog2e : __builtin_inff();
+            reinterpret_cast<float*>(smem + P::DS)[tid] = q < Nq ? Dh[q] : 0.f;
+        }
+    };
 
     const int rbase = kl * P::RSTR + hh * 16;   // row-tile operand: row kl, chunk 8hh
     const int tbase = kl * P::TSTR + hh * 16;   // transposed-tile operand
+    const int kbase = P::KS + 32 * kblk * P::RSTR + rbase;
+    const int vbase = P::VS + 32 * kblk * P::RSTR + rbase;
 
+    if (i0 < nqt)
+        load_tile(i0);
     for (int i = i0; i < nqt; ++i) {
-        __syncthreads();  // the previous tile is consumed
-        load_row_tile<D, P::NT>(Qh, i, Nq, smem + QR, tid);
-        load_row_tile<D, P::NT>(dOh, i, Nq, smem + DOR, tid);
-        load_t_tile<D, P::NT>(Qh, i, Nq, smem + QT, tid);
-        load_t_tile<D, P::NT>(dOh, i, Nq, smem + DOT, tid);
-        if (tid < 64) {
-            const int q = i * P::TILE + tid;
-            // rows past Nq: P = exp2(-inf) = 0
-            reinterpret_cast<float*>(smem + LS)[tid] = q < Nq ? Lh[q] * kLog2e : __builtin_inff();
-            reinterpret_cast<float*>(smem + DS)[tid] = q < Nq ? Dh[q] : 0.f;
-        }
+        __syncthreads();  // the previous tile is consumed (and K, V are staged)
+        store_tile(i);
         __syncthreads();
-        if (i < iw0)
-            continue;
-        const bool diag = CAUSAL && (i * P::TILE < kw0 + 31);
+        if (i + 1 < nqt)
+            load_tile(i + 1);  // in flight while this tile is computed
+        const int qw = i * P::TILE + 32 * qh;  // first query of this wave's half
+        if (CAUSAL && qw + 31 < kw0)
+            continue;  // every query of the half precedes every key of the block
+        const bool diag = CAUSAL && (qw < kw0 + 31);
+        // S = Q K^T and dP = dO V^T for the 32 queries of this half
+        f32x16 s = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+        f32x16 dp = s;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            // S = Q K^T and dP = dO V^T for queries 32qb .. 32qb+31 of the tile
-            f32x16 s = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-            f32x16 dp = s;
+        for (int c = 0; c < P::DC; ++c) {
+            const vec kf = *reinterpret_cast<const vec*>(sm + kbase + 32 * c);
+            const vec a = *reinterpret_cast<const vec*>(sm + P::QR + rbase + 32 * qh * P::RSTR + 32 * c);
+            s = M::mma(a, kf, s);
+            const vec vf = *reinterpret_cast<const vec*>(sm + vbase + 32 * c);
+            const vec b = *reinterpret_cast<const vec*>(sm + P::DOR + rbase + 32 * qh * P::RSTR + 32 * c);
+            dp = M::mma(b, vf, dp);
+        }
+        // P = 2^(s c2 - L2), dS = P (dP - D); register r holds query
+        // qw + 8(r/4) + 4hh + r%4
+        vec pp[2], ps[2];
 #pragma unroll
-            for (int c = 0; c < P::DC; ++c) {
-                const vec a = *reinterpret_cast<const vec*>(sm + QR + rbase + 32 * qb * P::RSTR + 32 * c);
-                s = M::mma(a, kf[c], s);
-                const vec b = *reinterpret_cast<const vec*>(sm + DOR + rbase + 32 * qb * P::RSTR + 32 * c);
-                dp = M::mma(b, vf[c], dp);
+        for (int g = 0; g < 4; ++g) {
+            const int qo = 32 * qh + 8 * g + 4 * hh;
+            const f32x4 l2 = *reinterpret_cast<const f32x4*>(sm + P::LS + qo * 4);
+            const f32x4 dd = *reinterpret_cast<const f32x4*>(sm + P::DS + qo * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                float p = exp2_fast(fmaf(s[r], prm.c2, -l2[e]));
+                if (diag && my_k > i * P::TILE + qo + e)
+                    p = 0.f;  // key after the query
+                pp[r >> 3][r & 7] = (T)p;
+                ps[r >> 3][r & 7] = (T)(p * (dp[r] - dd[e]));
             }
-            // P = 2^(s c2 - L2), dS = P (dP - D); register r holds query
-            // 32qb + 8(r/4) + 4hh + r%4 of the tile
-            vec pp[2], ps[2];
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS over chunks 2qh, 2qh+1 of the tile
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int qo = 32 * qb + 8 * g + 4 * hh;
-                const f32x4 l2 = *reinterpret_cast<const f32x4*>(sm + LS + qo * 4);
-                const f32x4 dd = *reinterpret_cast<const f32x4*>(sm + DS + qo * 4);
+        for (int h = 0; h < 2; ++h) {
+            const int cc = 2 * qh + h;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * g + e;
-                    float p = exp2_fast(fmaf(s[r], prm.c2, -l2[e]));
-                    if (diag && my_k > i * P::TILE + qo + e)
-                        p = 0.f;  // key after the query
-                    const float ds = p * (dp[r] - dd[e]);
-                    pp[r >> 3][r & 7] = (T)p;
-                    ps[r >> 3][r & 7] = (T)ds;
-                }
-            }
-            // dV^T += dO^T P, dK^T += Q^T dS over chunks 2qb, 2qb+1 of the tile
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int cc = 2 * qb + h;
-#pragma unroll
-                for (int db = 0; db < P::DB; ++db) {
-                    const vec a = *reinterpret_cast<const vec*>(sm + DOT + tbase + 32 * db * P::TSTR + 32 * cc);
-                    dvt[db] = M::mma(a, pp[h], dvt[db]);
-                    const vec b = *reinterpret_cast<const vec*>(sm + QT + tbase + 32 * db * P::TSTR + 32 * cc);
-                    dkt[db] = M::mma(b, ps[h], dkt[db]);
-                }
+            for (int db = 0; db < P::DB; ++db) {
+                const vec a = *reinterpret_cast<const vec*>(sm + P::DOT + tbase + 32 * db * P::TSTR + 32 * cc);
+                dvt[db] = M::mma(a, pp[h], dvt[db]);
+                const vec b = *reinterpret_cast<const vec*>(sm + P::QT + tbase + 32 * db * P::TSTR + 32 * cc);
+                dkt[db] = M::mma(b, ps[h], dkt[db]);
             }
         }
     }
 
-    // epilogue: accumulator register r of block db holds d = 32db + 8(r/4) + 4hh + r%4
-    if (my_k < Nk) {
-        T* dkrow = prm.dk + ((size_t)bh * Nk + my_k) * D;
-        T* dvrow = prm.dv + ((size_t)bh * Nk + my_k) * D;
+    // the second query half hands its partial sums to the first through LDS
+    __syncthreads();
+    float* xch = reinterpret_cast<float*>(smem);
+    if (qh == 1) {
 #pragma unroll
         for (int db = 0; db < P::DB; ++db)
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                T4 wk, wv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    wk[e] = (T)(dkt[db][4 * a + e] * prm.scale);
-                    wv[e] = (T)dvt[db][4 * a + e];
-                }
-                *reinterpret_cast<T4*>(dkrow + 32 * db + 8 * a + 4 * hh) = wk;
-                *reinterpret_cast<T4*>(dvrow + 32 * db + 8 * a + 4 * hh) = wv;
+            for (int r = 0; r < 16; ++r) {
+                xch[(((kblk * 2 + 0) * P::DB + db) * 16 + r) * 64 + lane] = dkt[db][r];
+                xch[(((kblk * 2 + 1) * P::DB + db) * 16 + r) * 64 + lane] = dvt[db][r];
             }
     }
+    __syncthreads();
+    if (qh == 1 || my_k >= Nk)
+        return;
+    // epilogue: accumulator register r of block db holds d = 32db + 8(r/4) + 4hh + r%4
+    T* dkrow = prm.dk + ((size_t)bh * Nk + my_k) * D;
+    T* dvrow = prm.dv + ((size_t)bh * Nk + my_k) * D;
+#pragma unroll
+    for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            T4 wk, wv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * a + e;
+                const float sk = dkt[db][r] + xch[(((kblk * 2 + 0) * P::DB + db) * 16 + r) * 64 + lane];
+                const float sv = dvt[db][r] + xch[(((kblk * 2 + 1) * P::DB + db) * 16 + r) * 64 + lane];
+                wk[e] = (T)(sk * prm.scale);
+                wv[e] = (T)sv;
+            }
+            *reinterpret_cast<T4*>(dkrow + 32 * db + 8 * a + 4 * hh) = wk;
+            *reinterpret_cast<T4*>(dvrow + 32 * db + 8 * a + 4 * hh) = wv;
+        }
 }
 
 // ---------------------------------------------------------------------------
