@@ -338,7 +338,6 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
                         int64_t BH, int64_t Nq, int64_t Nk, float scale, float* delta,
                         hipStream_t stream)
 {
-    using P = fa::BwdTile<D>;
     fa::BwdParams<T> prm;
     prm.q = static_cast<const T*>(q);
     prm.k = static_cast<const T*>(k);
@@ -374,9 +373,10 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
                           dim3((unsigned)(prm.n_tiles * BH)), dim3(PK::NT), args, 0, stream);
     if (err != hipSuccess || rows == 0)
         return err;
-    prm.n_tiles = (int)((Nq + P::ROWS - 1) / P::ROWS);  // dQ
+    using PQ = fa::DqTile<D>;
+    prm.n_tiles = (int)((Nq + PQ::ROWS - 1) / PQ::ROWS);  // dQ
     return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dq_kernel<T, D, C>),
-                           dim3((unsigned)(prm.n_tiles * BH)), dim3(P::NT), args, 0, stream);
+                           dim3((unsigned)(prm.n_tiles * BH)), dim3(PQ::NT), args, 0, stream);
 }
 
 template <typename T>

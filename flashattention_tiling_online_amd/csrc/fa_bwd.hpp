@@ -14,12 +14,14 @@
 //     resident in LDS: S = Q K^T and dP = dO V^T, then dV^T += dO^T P and
 //     dK^T += Q^T dS with P and dS rounded to T straight from the accumulators; the
 //     two halves' partial sums meet in LDS at the end;
-//   * fa_bwd_dq_kernel: one workgroup per 128-query tile (4 waves x 32 queries, lane =
-//     query, the forward's orientation), looping over 64-key tiles: S^T = K Q^T and
-//     dP^T = V dO^T with Q and dO in registers, then dQ^T += K^T dS^T.
+//   * fa_bwd_dq_kernel: one workgroup per 256-query tile for d = 128 (8 waves x 32
+//     queries, lane = query, the forward's orientation; 128 queries for d = 64),
+//     looping over 64-key tiles: S^T = K Q^T and dP^T = V dO^T with Q and dO in
+//     registers, then dQ^T += K^T dS^T.
 // Both main kernels stage row tiles and transposed tiles through LDS in the layouts
-// of fa_tiles.hpp; exp is exp2 with scale * log2(e) folded into one FMA and L taken in
-// base 2.
+// of fa_tiles.hpp, each thread loading one 4x4 block per tensor one tile ahead and
+// writing it in both layouts; exp is exp2 with scale * log2(e) folded into one FMA
+// and L taken in base 2.
 #pragma once
 
 #include "fa_tiles.hpp"
@@ -72,57 +74,6 @@ void fa_bwd_delta_kernel(const T* __restrict__ O, const T* __restrict__ dO,
         acc += __shfl_xor(acc, m);
     if (row < rows && t == 0)
         delta[row] = acc;
-}
-
-// ---------------------------------------------------------------------------
-// shared tile staging (plain loads; every thread of the workgroup takes part)
-// ---------------------------------------------------------------------------
-
-template <int D>
-struct BwdTile {
-    static constexpr int NW = 4;                 // waves per workgroup
-    static constexpr int NT = 64 * NW;           // threads
-    static constexpr int ROWS = 32 * NW;         // rows of the outer dimension per workgroup
-    static constexpr int TILE = 64;              // rows of the inner dimension per step
-    static constexpr int RSTR = 2 * D + 16;      // row-tile stride (bytes)
-    static constexpr int TSTR = 2 * TILE + 16;   // transposed-tile stride (bytes)
-    static constexpr int RT = TILE * RSTR;       // bytes of one row tile
-    static constexpr int TT = D * TSTR;          // bytes of one transposed tile
-    static constexpr int DC = D / 16;            // 16-wide chunks of the D contraction
-    static constexpr int DB = D / 32;            // 32-wide blocks of D
-};
-
-// Rows [tile*64, tile*64 + 64) of a [nrows, D] head matrix into a padded row tile.
-template <int D, int NT, typename T>
-__device__ __forceinline__ void load_row_tile(const T* head, int tile, int nrows, char* dst,
-                                              int tid)
-{
-    constexpr int CPR = (2 * D) / 16;  // 16-byte chunks per row
-    constexpr int N = 64 * CPR;
-    const __amdgpu_buffer_rsrc_t r = rows_rsrc<D>(head, tile * 64, nrows);
-#pragma unroll
-    for (int i = 0; i < N / NT; ++i) {
-        const int c = tid + i * NT;
-        const int row = c / CPR, ch = c - (c / CPR) * CPR;
-        const u32x4 w = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (row * D + ch * 8) * 2, 0, 0));
-        *reinterpret_cast<u32x4*>(dst + row * (2 * D + 16) + ch * 16) = w;
-    }
-}
-
-// The same rows, transposed into a [D, 64] tile in accumulator order (fa_tiles.hpp).
-template <int D, int NT, typename T>
-__device__ __forceinline__ void load_t_tile(const T* head, int tile, int nrows, char* dst, int tid)
-{
-#pragma unroll
-    for (int i = 0; i < (4 * D) / NT; ++i) {
-        const int b = tid + i * NT;  // one 4-row x 4-column block
-        const int dq = (b & 3) + 4 * (b >> 6);
-        const int kg = ((b >> 2) & 3) + 4 * (((b >> 4) & 1) + 2 * ((b >> 5) & 1));
-        u32x2 r[4];
-        load_v_block<D>(head, tile, nrows, kg, dq, r);
-        store_vt_block<2 * 64 + 16>(dst, kg, dq, r);
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -369,16 +320,34 @@ void fa_bwd_dkv_kernel(const BwdParams<T> prm)
 // dQ: one workgroup per 128 queries, lane = query
 // ---------------------------------------------------------------------------
 
+template <int D>
+struct DqTile {
+    // d = 128: 8 waves (256 queries) per workgroup, one per CU; d = 64: 4 waves (128
+    // queries), two per CU; either way each thread stages one 4x4 block per tensor
+    static constexpr int NW = D == 128 ? 8 : 4;
+    static constexpr int NT = 64 * NW;
+    static constexpr int ROWS = 32 * NW;        // queries per workgroup
+    static constexpr int TILE = 64;             // keys per step
+    static constexpr int RSTR = 2 * D + 16;
+    static constexpr int TSTR = 2 * TILE + 16;
+    static constexpr int DC = D / 16;
+    static constexpr int DB = D / 32;
+    static constexpr int KR = 0;                       // K row tile
+    static constexpr int VR = TILE * RSTR;             // V row tile
+    static constexpr int KT = 2 * TILE * RSTR;         // K transposed tile
+    static constexpr int LDS = KT + D * TSTR;
+    static_assert(NT == 4 * D, "one 4x4 block per tensor per thread");
+};
+
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(BwdTile<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(DqTile<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_bwd_dq_kernel(const BwdParams<T> prm)
 {
-    using P = BwdTile<D>;
+    using P = DqTile<D>;
     using M = Mfma16<T>;
     using vec = typename M::vec;
     typedef T T4 __attribute__((ext_vector_type(4)));
-    constexpr int KR = 0, VR = P::RT, KTT = 2 * P::RT;
-    __shared__ __attribute__((aligned(1024))) char smem[2 * P::RT + P::TT];
+    __shared__ __attribute__((aligned(1024))) char smem[P::LDS];
     const char* const sm = smem;
     const int Nq = prm.Nq, Nk = prm.Nk;
 
@@ -399,6 +368,25 @@ void fa_bwd_dq_kernel(const BwdParams<T> prm)
 
     const T* Kh = prm.k + (size_t)bh * Nk * D;
     const T* Vh = prm.v + (size_t)bh * Nk * D;
+
+    // key tiles, as in the forward: causal tiles after the workgroup's last query are
+    // skipped, a wave stops after its own last query, only its last tile is masked
+    int nkt = (Nk + P::TILE - 1) / P::TILE;
+    if (CAUSAL)
+        nkt = min(nkt, (min(q0 + P::ROWS, Nq) - 1) / P::TILE + 1);
+    const bool wave_active = qw0 < Nq;
+    int n_w = wave_active ? nkt : 0;
+    if (CAUSAL && wave_active)
+        n_w = min(nkt, min(qw0 + 31, Nq - 1) / P::TILE + 1);
+
+    // staging: this thread's 4x4 block of K and of V, loaded one tile ahead; K is
+    // written as a row tile and transposed, V as a row tile
+    const int s_kg = blk_kg(tid), s_dq = blk_dq(tid);
+    u32x2 kreg[4], vreg[4];
+    if (0 < nkt) {
+        load_v_block<D>(Kh, 0, Nk, s_kg, s_dq, kreg);
+        load_v_block<D>(Vh, 0, Nk, s_kg, s_dq, vreg);
+    }
 
     // Q and dO rows of this lane's query as the B operands
     vec qf[P::DC], df[P::DC];
@@ -421,25 +409,19 @@ void fa_bwd_dq_kernel(const BwdParams<T> prm)
     for (int db = 0; db < P::DB; ++db)
         dqt[db] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 
-    // key tiles, as in the forward: causal tiles after the workgroup's last query are
-    // skipped, a wave stops after its own last query, only its last tile is masked
-    int nkt = (Nk + P::TILE - 1) / P::TILE;
-    if (CAUSAL)
-        nkt = min(nkt, (min(q0 + P::ROWS, Nq) - 1) / P::TILE + 1);
-    const bool wave_active = qw0 < Nq;
-    int n_w = wave_active ? nkt : 0;
-    if (CAUSAL && wave_active)
-        n_w = min(nkt, min(qw0 + 31, Nq - 1) / P::TILE + 1);
-
     const int rbase = ql * P::RSTR + hh * 16;
     const int tbase = ql * P::TSTR + hh * 16;
 
     for (int j = 0; j < nkt; ++j) {
+        __syncthreads();  // the previous tile is consumed
+        store_row_block<P::RSTR>(smem + P::KR, s_kg, s_dq, kreg);
+        store_vt_block<P::TSTR>(smem + P::KT, s_kg, s_dq, kreg);
+        store_row_block<P::RSTR>(smem + P::VR, s_kg, s_dq, vreg);
         __syncthreads();
-        load_row_tile<D, P::NT>(Kh, j, Nk, smem + KR, tid);
-        load_row_tile<D, P::NT>(Vh, j, Nk, smem + VR, tid);
-        load_t_tile<D, P::NT>(Kh, j, Nk, smem + KTT, tid);
-        __syncthreads();
+        if (j + 1 < nkt) {  // in flight while this tile is computed
+            load_v_block<D>(Kh, j + 1, Nk, s_kg, s_dq, kreg);
+            load_v_block<D>(Vh, j + 1, Nk, s_kg, s_dq, vreg);
+        }
         if (j >= n_w)
             continue;
         // S^T = K Q^T, dP^T = V dO^T: register r of block kb holds key
@@ -451,9 +433,9 @@ void fa_bwd_dq_kernel(const BwdParams<T> prm)
             dpt[kb] = st[kb];
 #pragma unroll
             for (int c = 0; c < P::DC; ++c) {
-                const vec a = *reinterpret_cast<const vec*>(sm + KR + rbase + 32 * kb * P::RSTR + 32 * c);
+                const vec a = *reinterpret_cast<const vec*>(sm + P::KR + rbase + 32 * kb * P::RSTR + 32 * c);
                 st[kb] = M::mma(a, qf[c], st[kb]);
-                const vec b = *reinterpret_cast<const vec*>(sm + VR + rbase + 32 * kb * P::RSTR + 32 * c);
+                const vec b = *reinterpret_cast<const vec*>(sm + P::VR + rbase + 32 * kb * P::RSTR + 32 * c);
                 dpt[kb] = M::mma(b, df[c], dpt[kb]);
             }
         }
@@ -476,7 +458,7 @@ void fa_bwd_dq_kernel(const BwdParams<T> prm)
         for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
             for (int db = 0; db < P::DB; ++db) {
-                const vec a = *reinterpret_cast<const vec*>(sm + KTT + tbase + 32 * db * P::TSTR + 32 * cc);
+                const vec a = *reinterpret_cast<const vec*>(sm + P::KT + tbase + 32 * db * P::TSTR + 32 * cc);
                 dqt[db] = M::mma(a, ps[cc], dqt[db]);
             }
     }
