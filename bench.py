@@ -48,9 +48,14 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+# the sources the forward kernels are built from (the profiles in profiles/ that
+# bench.py reads belong to the forward kernel)
+FWD_SOURCES = ("fa_common.hpp", "fa_tiles.hpp", "fa_fwd_mfma16.hpp", "fa_fwd_f32.hpp")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
+    for f in FWD_SOURCES:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -344,7 +349,7 @@ def main() -> int:
                              f"N(0,{w.sigma_v:g}^2) V, seeded"},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "kernel_sources_sha256_16": kernel_source_hash(),
+        "fwd_kernel_sources_sha256_16": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)
     return 0
