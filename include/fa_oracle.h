@@ -171,6 +171,39 @@ int fa_ref_bwd_dkv_keys_f64(const void* q, const void* k, const void* v, const v
                             const double* D64_all, int64_t n_sel, const int64_t* sel_bh,
                             const int64_t* sel_key, double* dk64, double* dv64);
 
+/*
+ * Dropout on P (blog page, Algorithm 2 and Algorithm 4, whose random numbers the
+ * pages leave open).  Reading: Philox4x32-10 (Salmon et al., SC'11) with key
+ * (seed low, seed high) and counter (k/4, q/4, bh, 0); element (q, k) takes output
+ * byte 4(q%4) + k%4 (byte b of word w = bits 8b.. of w, index 4w + b) and is dropped
+ * iff that byte is below t (0 <= t <= 255); kept elements are scaled by
+ * 256 / (256 - t).  L is unchanged (the softmax's), O = (P o Z) V, and in the
+ * gradients dV = (P o Z)^T dO and dP = (dO V^T) o Z.
+ */
+int fa_oracle_philox4x32_10(const uint32_t* ctr, const uint32_t* key, uint32_t* out);
+/* keep[q * nk + k] = 1 where element (q, k) of head bh is kept, else 0 */
+int fa_oracle_dropout_keep(uint64_t seed, int t, int64_t bh, int64_t nq, int64_t nk,
+                           uint8_t* keep);
+/* Part 1 with dropout on P (head index bh selects the random numbers). */
+int fa_oracle_attention_dropout_f64(const double* q, const double* k, const double* v,
+                                    int64_t nq, int64_t nk, int64_t d, int causal, double scale,
+                                    int t, uint64_t seed, int64_t bh, int64_t n_rows,
+                                    const int64_t* rows, double* o, double* lse);
+/* Part 3 with dropout on P. */
+int fa_oracle_attention_bwd_dropout_f64(const double* q, const double* k, const double* v,
+                                        const double* dout, int64_t nq, int64_t nk, int64_t d,
+                                        int causal, double scale, int t, uint64_t seed,
+                                        int64_t bh, double* dq, double* dk, double* dv);
+/* Raw-buffer counterparts of the two above (selected rows; one head). */
+int fa_ref_rows_dropout_f64(const void* q, const void* k, const void* v, int64_t B, int64_t H,
+                            int64_t Nq, int64_t Nk, int64_t d, int causal, float scale, int dtype,
+                            int t, uint64_t seed, int64_t n_sel, const int64_t* sel_bh,
+                            const int64_t* sel_row, double* o64, double* lse64);
+int fa_ref_bwd_head_dropout_f64(const void* q, const void* k, const void* v, const void* dout,
+                                int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                int causal, float scale, int dtype, int t, uint64_t seed,
+                                int64_t bh, double* dq64, double* dk64, double* dv64);
+
 /* Whole-tensor host counterpart of the GPU backward: part 3 on every head, the
  * gradients rounded from fp64 to `dtype` (nearest-even) into dq, dk, dv. */
 int fa_bwd_ref(const void* q, const void* k, const void* v, const void* dout, void* dq,

@@ -18,6 +18,9 @@ What is computed, and where it comes from (pages named by title / address):
 * part 3, ``attention_bwd_f64`` / ``bwd_*``: the gradients of sum(dO o O) — course
   file ``flash_attention_backward``; blog page, Algorithm 4 and the softmax-Jacobian
   derivation that follows it.
+* part 4, ``philox4x32_10`` / ``*_dropout_*``: dropout on P (blog page, Algorithms 2
+  and 4) with Philox4x32-10 random numbers (Salmon et al., SC'11), the reading taken
+  for the generator the pages leave open.
 * ``softmax_online``: the one-dimensional online softmax with a per-block trace —
   course file ``online_softmax_stats``; the worked example of
   "手写 Flash Attention" (bjdmk.com.cn) section 2.2 is pinned against it.
@@ -89,6 +92,26 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.fa_ref_bwd_dkv_keys_f64.argtypes = raw4 + [_dp, _dp, _i64, _lp, _lp, _dp, _dp]
     lib.fa_bwd_ref.argtypes = [_vp] * 7 + [_i64, _i64, _i64, _i64, _i64, ctypes.c_int,
                                            ctypes.c_float, ctypes.c_int]
+    u32p = ctypes.POINTER(ctypes.c_uint32)
+    lib.fa_oracle_philox4x32_10.argtypes = [u32p, u32p, u32p]
+    lib.fa_oracle_dropout_keep.argtypes = [ctypes.c_uint64, ctypes.c_int, _i64, _i64, _i64, _vp]
+    lib.fa_oracle_attention_dropout_f64.argtypes = [_dp, _dp, _dp, _i64, _i64, _i64, ctypes.c_int,
+                                                    ctypes.c_double, ctypes.c_int,
+                                                    ctypes.c_uint64, _i64, _i64, _lp, _dp, _dp]
+    lib.fa_oracle_attention_bwd_dropout_f64.argtypes = [_dp, _dp, _dp, _dp, _i64, _i64, _i64,
+                                                        ctypes.c_int, ctypes.c_double,
+                                                        ctypes.c_int, ctypes.c_uint64, _i64,
+                                                        _dp, _dp, _dp]
+    lib.fa_ref_rows_dropout_f64.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                            ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_uint64, _i64, _lp, _lp, _dp,
+                                            _dp]
+    lib.fa_ref_bwd_head_dropout_f64.argtypes = raw4 + [ctypes.c_int, ctypes.c_uint64, _i64, _dp,
+                                                       _dp, _dp]
+    for name in ("fa_oracle_philox4x32_10", "fa_oracle_dropout_keep",
+                 "fa_oracle_attention_dropout_f64", "fa_oracle_attention_bwd_dropout_f64",
+                 "fa_ref_rows_dropout_f64", "fa_ref_bwd_head_dropout_f64"):
+        getattr(lib, name).restype = ctypes.c_int
     for name in ("fa_oracle_softmax_online", "fa_oracle_merge", "fa_oracle_attention_f64",
                  "fa_oracle_online_f64", "fa_ref_rows_f64", "fa_ref_online_f64", "fa_fwd_ref",
                  "fa_oracle_round", "fa_oracle_attention_bwd_f64", "fa_ref_bwd_head_f64",
@@ -386,6 +409,100 @@ def bwd_ref(q, k, v, dout, causal: bool, scale: float, dtype: str, L=None):
     _check(L.fa_bwd_ref(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
                         dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, B, H, Nq, Nk, d,
                         int(causal), float(scale), DTYPE_CODES[dtype]), "fa_bwd_ref")
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# dropout (part 4): Philox4x32-10 and dropout on P
+# ---------------------------------------------------------------------------
+
+def philox4x32_10(ctr, key, L=None):
+    """One Philox4x32-10 block: four 32-bit counter words, two key words -> four words."""
+    L = L or lib()
+    c = (ctypes.c_uint32 * 4)(*[int(x) & 0xFFFFFFFF for x in ctr])
+    k = (ctypes.c_uint32 * 2)(*[int(x) & 0xFFFFFFFF for x in key])
+    out = (ctypes.c_uint32 * 4)()
+    _check(L.fa_oracle_philox4x32_10(c, k, out), "fa_oracle_philox4x32_10")
+    return [int(x) for x in out]
+
+
+def dropout_keep(seed: int, t: int, bh: int, nq: int, nk: int, L=None) -> np.ndarray:
+    """[nq, nk] uint8: 1 where element (q, k) of head bh is kept."""
+    L = L or lib()
+    keep = np.empty((nq, nk), dtype=np.uint8)
+    _check(L.fa_oracle_dropout_keep(int(seed), int(t), int(bh), nq, nk, keep.ctypes.data),
+           "fa_oracle_dropout_keep")
+    return keep
+
+
+def attention_dropout_f64(q, k, v, causal: bool, scale: float, t: int, seed: int, bh: int = 0,
+                          rows=None, L=None):
+    """Part 1 with dropout on P (one head of fp64 inputs); returns (o, lse)."""
+    L = L or lib()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    nq, d = q.shape
+    nk = k.shape[0]
+    rows = np.arange(nq, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
+    o = np.empty((rows.size, d))
+    lse = np.empty(rows.size)
+    _check(L.fa_oracle_attention_dropout_f64(_ptr(q), _ptr(k), _ptr(v), nq, nk, d, int(causal),
+                                             float(scale), int(t), int(seed), int(bh), rows.size,
+                                             _ptr(rows, _lp), _ptr(o), _ptr(lse)),
+           "fa_oracle_attention_dropout_f64")
+    return o, lse
+
+
+def attention_bwd_dropout_f64(q, k, v, dout, causal: bool, scale: float, t: int, seed: int,
+                              bh: int = 0, L=None):
+    """Part 3 with dropout on P (one head of fp64 inputs); returns (dq, dk, dv)."""
+    L = L or lib()
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    nq, d = q.shape
+    nk = k.shape[0]
+    dq, dk, dv = np.empty((nq, d)), np.empty((nk, d)), np.empty((nk, d))
+    _check(L.fa_oracle_attention_bwd_dropout_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), nq, nk,
+                                                 d, int(causal), float(scale), int(t), int(seed),
+                                                 int(bh), _ptr(dq), _ptr(dk), _ptr(dv)),
+           "fa_oracle_attention_bwd_dropout_f64")
+    return dq, dk, dv
+
+
+def ref_rows_dropout_f64(q, k, v, causal: bool, scale: float, dtype: str, t: int, seed: int,
+                         sel_bh, sel_row, threads: int | None = None, L=None):
+    """Part 1 with dropout on selected rows of raw buffers (threaded); (o64, lse64)."""
+    L = L or lib()
+    q, k, v = _raw(q, dtype), _raw(k, dtype), _raw(v, dtype)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    sel_bh = np.ascontiguousarray(sel_bh, np.int64)
+    sel_row = np.ascontiguousarray(sel_row, np.int64)
+    o, lse = np.empty((sel_bh.size, d)), np.empty(sel_bh.size)
+
+    def work(span):
+        a, b = span
+        if b <= a:
+            return 0
+        return L.fa_ref_rows_dropout_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, Nq, Nk,
+                                         d, int(causal), float(scale), DTYPE_CODES[dtype], int(t),
+                                         int(seed), b - a, _ptr(sel_bh[a:b], _lp),
+                                         _ptr(sel_row[a:b], _lp), _ptr(o[a:b]), _ptr(lse[a:b]))
+
+    for rc in _threaded(sel_bh.size, threads, work):
+        _check(rc, "fa_ref_rows_dropout_f64")
+    return o, lse
+
+
+def bwd_head_dropout_f64(q, k, v, dout, causal: bool, scale: float, dtype: str, t: int,
+                         seed: int, bh: int, L=None):
+    """Part 3 with dropout on head bh of raw buffers; returns fp64 (dq, dk, dv)."""
+    L = L or lib()
+    q, k, v, dout, B, H, Nq, Nk, d = _raw4(q, k, v, dout, dtype)
+    dq, dk, dv = np.empty((Nq, d)), np.empty((Nk, d)), np.empty((Nk, d))
+    _check(L.fa_ref_bwd_head_dropout_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                         dout.ctypes.data, B, H, Nq, Nk, d, int(causal),
+                                         float(scale), DTYPE_CODES[dtype], int(t), int(seed),
+                                         int(bh), _ptr(dq), _ptr(dk), _ptr(dv)),
+           "fa_ref_bwd_head_dropout_f64")
     return dq, dk, dv
 
 

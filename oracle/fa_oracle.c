@@ -19,12 +19,16 @@
  *       Algorithm 4 (backward pass) and the softmax-Jacobian derivation after it.
  *   [C] "手写 Flash Attention：从算法原理到高性能实现" (bjdmk.com.cn), section 2.2:
  *       the worked two-block example that the tests pin.
+ *   [D] Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+ *       easy as 1, 2, 3", SC'11): the random numbers of dropout, which [B] leaves
+ *       unspecified.
  *
  * Readings where the pages are silent are listed beside the code that takes them.
  */
 #include "../include/fa_oracle.h"
 
 #include <math.h>
+#include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -155,6 +159,98 @@ int fa_oracle_merge(int64_t dim, const double* a, const double* b, double* out)
 }
 
 /* ------------------------------------------------------------------------- */
+/* Dropout on P and its random numbers                                        */
+/*   [B] Algorithm 2 (P_dropped = dropout(P, p), O = P_dropped V; the forward  */
+/*   returns the RNG state R) and Algorithm 4 (Z regenerated from R,          */
+/*   P_dropped = P o Z, dP = dP_dropped o Z).  The pages name no generator;   */
+/*   the reading taken here: Philox4x32-10, the counter-based generator of    */
+/*   Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1,   */
+/*   2, 3" (SC'11), with key = (seed low 32 bits, seed high 32 bits) and       */
+/*   counter = (k / 4, q / 4, bh, 0) for element (bh, q, k); its 16 output     */
+/*   bytes (word w, byte b = bits 8b..8b+7, index 4w + b) cover the 4x4 block  */
+/*   of queries 4(q/4).. and keys 4(k/4)..: element (q, k) takes byte          */
+/*   4 (q % 4) + k % 4.  The element is dropped iff that byte is below the     */
+/*   threshold t (0 <= t < 256, the drop probability is t / 256) and kept      */
+/*   values are scaled by 256 / (256 - t), so that E[Z] = 1.                   */
+/* ------------------------------------------------------------------------- */
+
+#define PHILOX_M0 0xD2511F53u
+#define PHILOX_M1 0xCD9E8D57u
+#define PHILOX_W0 0x9E3779B9u
+#define PHILOX_W1 0xBB67AE85u
+
+int fa_oracle_philox4x32_10(const uint32_t* ctr_in, const uint32_t* key_in, uint32_t* out)
+{
+    if (!ctr_in || !key_in || !out)
+        return FA_ORACLE_EINVAL;
+    uint32_t c[4] = {ctr_in[0], ctr_in[1], ctr_in[2], ctr_in[3]};
+    uint32_t k0 = key_in[0], k1 = key_in[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) { /* bump the key between rounds */
+            k0 += PHILOX_W0;
+            k1 += PHILOX_W1;
+        }
+        const uint64_t p0 = (uint64_t)PHILOX_M0 * c[0];
+        const uint64_t p1 = (uint64_t)PHILOX_M1 * c[2];
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+        const uint32_t n1 = (uint32_t)p1;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+        const uint32_t n3 = (uint32_t)p0;
+        c[0] = n0;
+        c[1] = n1;
+        c[2] = n2;
+        c[3] = n3;
+    }
+    for (int i = 0; i < 4; ++i)
+        out[i] = c[i];
+    return FA_ORACLE_OK;
+}
+
+typedef struct {
+    uint64_t seed;
+    int t;             /* drop iff byte < t */
+    double keep_scale; /* 256 / (256 - t) */
+    int64_t bh;
+} Drop;
+
+/* Z[q, k] of head dr->bh: 0 (dropped) or keep_scale; 1 without dropout (dr NULL) */
+static double drop_factor(const Drop* dr, int64_t q, int64_t k)
+{
+    if (!dr)
+        return 1.0;
+    const uint32_t ctr[4] = {(uint32_t)(k >> 2), (uint32_t)(q >> 2), (uint32_t)dr->bh, 0u};
+    const uint32_t key[2] = {(uint32_t)dr->seed, (uint32_t)(dr->seed >> 32)};
+    uint32_t w[4];
+    fa_oracle_philox4x32_10(ctr, key, w);
+    const int idx = (int)(4 * (q & 3) + (k & 3));
+    const uint32_t byte = (w[idx >> 2] >> (8 * (idx & 3))) & 0xFFu;
+    return (int)byte < dr->t ? 0.0 : dr->keep_scale;
+}
+
+static int make_drop(Drop* dr, int t, uint64_t seed, int64_t bh)
+{
+    if (t < 0 || t > 255)
+        return FA_ORACLE_EINVAL;
+    dr->seed = seed;
+    dr->t = t;
+    dr->keep_scale = 256.0 / (256.0 - (double)t);
+    dr->bh = bh;
+    return FA_ORACLE_OK;
+}
+
+int fa_oracle_dropout_keep(uint64_t seed, int t, int64_t bh, int64_t nq, int64_t nk,
+                           uint8_t* keep)
+{
+    Drop dr;
+    if (!keep || nq < 0 || nk < 0 || bh < 0 || make_drop(&dr, t, seed, bh))
+        return FA_ORACLE_EINVAL;
+    for (int64_t q = 0; q < nq; ++q)
+        for (int64_t k = 0; k < nk; ++k)
+            keep[q * nk + k] = drop_factor(&dr, q, k) != 0.0;
+    return FA_ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Part 1: standard three-step attention, one row  [A] standard_attention     */
 /* ------------------------------------------------------------------------- */
 
@@ -173,7 +269,7 @@ static double score(const double* q_row, const double* k_row, int64_t d, double 
 /* s is caller scratch of nk doubles */
 static void three_step_row(const double* q_row, const double* k, const double* v, int64_t nk,
                            int64_t d, int causal, double scale, int64_t r, double* s,
-                           double* o_row, double* lse)
+                           double* o_row, double* lse, const Drop* dr)
 {
     /* step 1: materialise the score row S[r, :] */
     for (int64_t kk = 0; kk < nk; ++kk)
@@ -192,12 +288,14 @@ static void three_step_row(const double* q_row, const double* k, const double* v
     for (int64_t kk = 0; kk < nk; ++kk)
         s[kk] = s[kk] / l; /* P[r, :] */
 
-    /* step 3: O[r, :] = P[r, :] V */
+    /* step 3: O[r, :] = P_dropped[r, :] V, P_dropped = P o Z (Z = 1 without dropout) */
     for (int64_t t = 0; t < d; ++t)
         o_row[t] = 0.0;
-    for (int64_t kk = 0; kk < nk; ++kk)
+    for (int64_t kk = 0; kk < nk; ++kk) {
+        const double pk = s[kk] * drop_factor(dr, r, kk);
         for (int64_t t = 0; t < d; ++t)
-            o_row[t] += s[kk] * v[kk * d + t];
+            o_row[t] += pk * v[kk * d + t];
+    }
 
     /* logsumexp of the scaled, masked scores */
     *lse = m + log(l);
@@ -218,7 +316,29 @@ int fa_oracle_attention_f64(const double* q, const double* k, const double* v,
         return FA_ORACLE_ENOMEM;
     for (int64_t i = 0; i < n_rows; ++i)
         three_step_row(q + rows[i] * d, k, v, nk, d, causal, scale, rows[i], s, o + i * d,
-                       lse + i);
+                       lse + i, NULL);
+    free(s);
+    return FA_ORACLE_OK;
+}
+
+int fa_oracle_attention_dropout_f64(const double* q, const double* k, const double* v,
+                                    int64_t nq, int64_t nk, int64_t d, int causal, double scale,
+                                    int t, uint64_t seed, int64_t bh, int64_t n_rows,
+                                    const int64_t* rows, double* o, double* lse)
+{
+    Drop dr;
+    if (!q || !k || !v || !o || !lse || nq < 1 || nk < 1 || d < 1 || n_rows < 0 ||
+        (n_rows > 0 && !rows) || bh < 0 || make_drop(&dr, t, seed, bh))
+        return FA_ORACLE_EINVAL;
+    for (int64_t i = 0; i < n_rows; ++i)
+        if (rows[i] < 0 || rows[i] >= nq)
+            return FA_ORACLE_EINVAL;
+    double* s = (double*)malloc((size_t)nk * sizeof(double));
+    if (!s)
+        return FA_ORACLE_ENOMEM;
+    for (int64_t i = 0; i < n_rows; ++i)
+        three_step_row(q + rows[i] * d, k, v, nk, d, causal, scale, rows[i], s, o + i * d,
+                       lse + i, &dr);
     free(s);
     return FA_ORACLE_OK;
 }
@@ -341,11 +461,14 @@ static int ref_rows(const void* q, const void* k, const void* v, int64_t B, int6
                     int64_t Nq, int64_t Nk, int64_t d, int causal, float scale, int dtype,
                     int64_t n_sel, const int64_t* sel_bh, const int64_t* sel_row,
                     int use_online, int64_t key_block, double* o64, double* lse64,
-                    int64_t* max_raised)
+                    int64_t* max_raised, int drop_t, uint64_t seed)
 {
     int rc = check_raw(q, k, v, B, H, Nq, Nk, d, dtype);
     if (rc)
         return rc;
+    Drop dr;
+    if (drop_t >= 0 && make_drop(&dr, drop_t, seed, 0))
+        return FA_ORACLE_EINVAL;
     if (n_sel < 0 || (n_sel > 0 && (!sel_bh || !sel_row || !o64 || !lse64)))
         return FA_ORACLE_EINVAL;
     for (int64_t i = 0; i < n_sel; ++i)
@@ -375,11 +498,13 @@ static int ref_rows(const void* q, const void* k, const void* v, int64_t B, int6
             cur = bh;
         }
         widen_span(q, (bh * Nq + r) * d, d, dtype, qr);
+        dr.bh = bh;
         if (use_online)
             online_row(qr, kh, vh, Nk, d, causal, sc, r, key_block, st, st + (d + 2),
                        o64 + i * d, lse64 + i, max_raised ? max_raised + i : NULL);
         else
-            three_step_row(qr, kh, vh, Nk, d, causal, sc, r, s, o64 + i * d, lse64 + i);
+            three_step_row(qr, kh, vh, Nk, d, causal, sc, r, s, o64 + i * d, lse64 + i,
+                           drop_t >= 0 ? &dr : NULL);
     }
     free(kh);
     free(vh);
@@ -395,7 +520,18 @@ int fa_ref_rows_f64(const void* q, const void* k, const void* v, int64_t B, int6
                     double* lse64)
 {
     return ref_rows(q, k, v, B, H, Nq, Nk, d, causal, scale, dtype, n_sel, sel_bh, sel_row, 0, 0,
-                    o64, lse64, NULL);
+                    o64, lse64, NULL, -1, 0);
+}
+
+int fa_ref_rows_dropout_f64(const void* q, const void* k, const void* v, int64_t B, int64_t H,
+                            int64_t Nq, int64_t Nk, int64_t d, int causal, float scale, int dtype,
+                            int t, uint64_t seed, int64_t n_sel, const int64_t* sel_bh,
+                            const int64_t* sel_row, double* o64, double* lse64)
+{
+    if (t < 0 || t > 255)
+        return FA_ORACLE_EINVAL;
+    return ref_rows(q, k, v, B, H, Nq, Nk, d, causal, scale, dtype, n_sel, sel_bh, sel_row, 0, 0,
+                    o64, lse64, NULL, t, seed);
 }
 
 int fa_ref_online_f64(const void* q, const void* k, const void* v, int64_t B, int64_t H,
@@ -404,7 +540,7 @@ int fa_ref_online_f64(const void* q, const void* k, const void* v, int64_t B, in
                       int64_t key_block, double* o64, double* lse64, int64_t* max_raised)
 {
     return ref_rows(q, k, v, B, H, Nq, Nk, d, causal, scale, dtype, n_sel, sel_bh, sel_row, 1,
-                    key_block, o64, lse64, max_raised);
+                    key_block, o64, lse64, max_raised, -1, 0);
 }
 
 /* ------------------------------------------------------------------------- */
@@ -555,24 +691,24 @@ static void prob_row(const double* q_row, const double* k, int64_t nk, int64_t d
         p[kk] = p[kk] / l;
 }
 
-/* dP[r, :] = do_r V^T and D_r = P_r . dP_r */
+/* dP[r, :] = (do_r V^T) o Z[r, :] and D_r = P_r . dP_r */
 static double dprob_row(const double* do_row, const double* v, const double* p, int64_t nk,
-                        int64_t d, double* dp)
+                        int64_t d, double* dp, const Drop* dr, int64_t r)
 {
     double D = 0.0;
     for (int64_t kk = 0; kk < nk; ++kk) {
         double acc = 0.0;
         for (int64_t t = 0; t < d; ++t)
             acc += do_row[t] * v[kk * d + t];
-        dp[kk] = acc;
+        dp[kk] = acc * drop_factor(dr, r, kk);
         D += p[kk] * dp[kk];
     }
     return D;
 }
 
-int fa_oracle_attention_bwd_f64(const double* q, const double* k, const double* v,
-                                const double* dout, int64_t nq, int64_t nk, int64_t d,
-                                int causal, double scale, double* dq, double* dk, double* dv)
+static int attention_bwd(const double* q, const double* k, const double* v, const double* dout,
+                         int64_t nq, int64_t nk, int64_t d, int causal, double scale,
+                         double* dq, double* dk, double* dv, const Drop* dr)
 {
     if (!q || !k || !v || !dout || !dq || !dk || !dv || nq < 1 || nk < 1 || d < 1)
         return FA_ORACLE_EINVAL;
@@ -590,22 +726,41 @@ int fa_oracle_attention_bwd_f64(const double* q, const double* k, const double* 
     for (int64_t r = 0; r < nq; ++r) {
         const double* q_row = q + r * d;
         const double* do_row = dout + r * d;
-        prob_row(q_row, k, nk, d, causal, scale, r, p);    /* P[r, :] */
-        const double D = dprob_row(do_row, v, p, nk, d, dp); /* dP[r, :], D_r */
+        prob_row(q_row, k, nk, d, causal, scale, r, p);            /* P[r, :] */
+        const double D = dprob_row(do_row, v, p, nk, d, dp, dr, r); /* dP[r, :], D_r */
         for (int64_t t = 0; t < d; ++t)
             dq[r * d + t] = 0.0;
         for (int64_t kk = 0; kk < nk; ++kk) {
             const double ds = p[kk] * (dp[kk] - D); /* dS[r, kk] */
+            const double pz = p[kk] * drop_factor(dr, r, kk); /* P_dropped[r, kk] */
             for (int64_t t = 0; t < d; ++t) {
                 dq[r * d + t] += scale * ds * k[kk * d + t];  /* dQ = dS K * scale */
                 dk[kk * d + t] += scale * ds * q_row[t];      /* dK = dS^T Q * scale */
-                dv[kk * d + t] += p[kk] * do_row[t];          /* dV = P^T dO */
+                dv[kk * d + t] += pz * do_row[t];             /* dV = P_dropped^T dO */
             }
         }
     }
     free(p);
     free(dp);
     return FA_ORACLE_OK;
+}
+
+int fa_oracle_attention_bwd_f64(const double* q, const double* k, const double* v,
+                                const double* dout, int64_t nq, int64_t nk, int64_t d,
+                                int causal, double scale, double* dq, double* dk, double* dv)
+{
+    return attention_bwd(q, k, v, dout, nq, nk, d, causal, scale, dq, dk, dv, NULL);
+}
+
+int fa_oracle_attention_bwd_dropout_f64(const double* q, const double* k, const double* v,
+                                        const double* dout, int64_t nq, int64_t nk, int64_t d,
+                                        int causal, double scale, int t, uint64_t seed,
+                                        int64_t bh, double* dq, double* dk, double* dv)
+{
+    Drop dr;
+    if (bh < 0 || make_drop(&dr, t, seed, bh))
+        return FA_ORACLE_EINVAL;
+    return attention_bwd(q, k, v, dout, nq, nk, d, causal, scale, dq, dk, dv, &dr);
 }
 
 /* raw-buffer gradients ---------------------------------------------------- */
@@ -618,11 +773,10 @@ static int check_bwd_raw(const void* q, const void* k, const void* v, const void
     return check_raw(q, k, v, B, H, Nq, Nk, d, dtype);
 }
 
-/* One head bh of raw [B,H,N,d] buffers: every row of dQ and every key of dK, dV. */
-int fa_ref_bwd_head_f64(const void* q, const void* k, const void* v, const void* dout,
-                        int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
-                        float scale, int dtype, int64_t bh, double* dq64, double* dk64,
-                        double* dv64)
+static int bwd_head(const void* q, const void* k, const void* v, const void* dout, int64_t B,
+                    int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal, float scale,
+                    int dtype, int64_t bh, double* dq64, double* dk64, double* dv64,
+                    const Drop* dr)
 {
     int rc = check_bwd_raw(q, k, v, dout, B, H, Nq, Nk, d, dtype);
     if (rc)
@@ -637,10 +791,32 @@ int fa_ref_bwd_head_f64(const void* q, const void* k, const void* v, const void*
     widen_span(dout, bh * Nq * d, Nq * d, dtype, doh);
     widen_span(k, bh * Nk * d, Nk * d, dtype, kh);
     widen_span(v, bh * Nk * d, Nk * d, dtype, vh);
-    rc = fa_oracle_attention_bwd_f64(qh, kh, vh, doh, Nq, Nk, d, causal, (double)scale, dq64,
-                                     dk64, dv64);
+    rc = attention_bwd(qh, kh, vh, doh, Nq, Nk, d, causal, (double)scale, dq64, dk64, dv64, dr);
     free(buf);
     return rc;
+}
+
+/* One head bh of raw [B,H,N,d] buffers: every row of dQ and every key of dK, dV. */
+int fa_ref_bwd_head_f64(const void* q, const void* k, const void* v, const void* dout,
+                        int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                        float scale, int dtype, int64_t bh, double* dq64, double* dk64,
+                        double* dv64)
+{
+    return bwd_head(q, k, v, dout, B, H, Nq, Nk, d, causal, scale, dtype, bh, dq64, dk64, dv64,
+                    NULL);
+}
+
+/* The same with dropout (threshold t, seed) on P. */
+int fa_ref_bwd_head_dropout_f64(const void* q, const void* k, const void* v, const void* dout,
+                                int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                int causal, float scale, int dtype, int t, uint64_t seed,
+                                int64_t bh, double* dq64, double* dk64, double* dv64)
+{
+    Drop dr;
+    if (make_drop(&dr, t, seed, bh))
+        return FA_ORACLE_EINVAL;
+    return bwd_head(q, k, v, dout, B, H, Nq, Nk, d, causal, scale, dtype, bh, dq64, dk64, dv64,
+                    &dr);
 }
 
 /* dQ of selected query rows (sel_bh[i], sel_row[i]) -> dq64[i * d .. +d] */
@@ -674,7 +850,7 @@ int fa_ref_bwd_dq_rows_f64(const void* q, const void* k, const void* v, const vo
         widen_span(q, (bh * Nq + r) * d, d, dtype, qr);
         widen_span(dout, (bh * Nq + r) * d, d, dtype, dor);
         prob_row(qr, kh, Nk, d, causal, sc, r, p);
-        const double D = dprob_row(dor, vh, p, Nk, d, dp);
+        const double D = dprob_row(dor, vh, p, Nk, d, dp, NULL, r);
         double* out = dq64 + i * d;
         for (int64_t t = 0; t < d; ++t)
             out[t] = 0.0;
@@ -719,9 +895,9 @@ int fa_ref_bwd_rowstats_f64(const void* q, const void* k, const void* v, const v
         }
         widen_span(q, (bh * Nq + r) * d, d, dtype, qr);
         widen_span(dout, (bh * Nq + r) * d, d, dtype, dor);
-        three_step_row(qr, kh, vh, Nk, d, causal, sc, r, p, o_row, lse64 + i);
+        three_step_row(qr, kh, vh, Nk, d, causal, sc, r, p, o_row, lse64 + i, NULL);
         prob_row(qr, kh, Nk, d, causal, sc, r, p);
-        D64[i] = dprob_row(dor, vh, p, Nk, d, dp);
+        D64[i] = dprob_row(dor, vh, p, Nk, d, dp, NULL, r);
     }
     free(buf);
     return FA_ORACLE_OK;

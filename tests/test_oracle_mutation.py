@@ -7,7 +7,8 @@ are the blog/article's own troubleshooting entry (a rescale factor forgotten in
 the running sum — "手写"/CUTLASS article section 3.3 and its section 6.3 table);
 the rest are a dropped scale, an inverted mask, a wrong index, a wrong sign, and in
 the gradients a dropped softmax-Jacobian term, a flipped sign, an unweighted D, a
-dropped scale and wrong operands.
+dropped scale and wrong operands, and in dropout a broken generator round, an
+inverted keep test, a dropped keep scale and the mask left out of dV or dP.
 """
 import json
 import math
@@ -35,8 +36,8 @@ MUTANTS = {
     "scale_dropped": ("return scale * dot;", "return dot;"),
     "mask_inverted": ("if (causal && kk > r)", "if (causal && kk < r)"),
     "mask_off_by_one": ("if (causal && kk > r)", "if (causal && kk >= r)"),
-    "value_index_transposed": ("o_row[t] += s[kk] * v[kk * d + t];",
-                               "o_row[t] += s[kk] * v[kk * d + (d - 1 - t)];"),
+    "value_index_transposed": ("o_row[t] += pk * v[kk * d + t];",
+                               "o_row[t] += pk * v[kk * d + (d - 1 - t)];"),
     "lse_wrong_sign": ("*lse = m + log(l);", "*lse = m - log(l);"),
     "online_lse_wrong_sign": ("*lse = run[0] + log(run[1]);", "*lse = run[0] - log(run[1]);"),
     # gradients (part 3): the softmax-Jacobian term, signs, scales and operands
@@ -49,8 +50,17 @@ MUTANTS = {
                              "dq[r * d + t] += ds * k[kk * d + t];"),
     "bwd_dk_uses_k": ("dk[kk * d + t] += scale * ds * q_row[t];",
                       "dk[kk * d + t] += scale * ds * k[kk * d + t];"),
-    "bwd_dv_uses_dp": ("dv[kk * d + t] += p[kk] * do_row[t];",
+    "bwd_dv_uses_dp": ("dv[kk * d + t] += pz * do_row[t];",
                        "dv[kk * d + t] += dp[kk] * do_row[t];"),
+    # dropout (part 4): the generator, the keep test, the scale, the mask's two uses
+    "philox_key_dropped": ("(uint32_t)(p1 >> 32) ^ c[1] ^ k0;", "(uint32_t)(p1 >> 32) ^ c[1];"),
+    "dropout_compare_inverted": ("return (int)byte < dr->t ? 0.0 : dr->keep_scale;",
+                                 "return (int)byte >= dr->t ? 0.0 : dr->keep_scale;"),
+    "dropout_scale_dropped": ("dr->keep_scale = 256.0 / (256.0 - (double)t);",
+                              "dr->keep_scale = 1.0;"),
+    "dropout_dv_unmasked": ("const double pz = p[kk] * drop_factor(dr, r, kk);",
+                            "const double pz = p[kk];"),
+    "dropout_dp_unmasked": ("dp[kk] = acc * drop_factor(dr, r, kk);", "dp[kk] = acc;"),
 }
 
 
@@ -135,11 +145,43 @@ def _pins(L):
         for g, x in zip(got, t):
             np.testing.assert_allclose(g, x.grad.numpy(), rtol=1e-10, atol=1e-12)
 
+    def philox_kat():
+        g = json.load(open(os.path.join(GOLDEN, "philox4x32_10_kat.json")))
+        for vec in g["vectors"]:
+            got = oracle.philox4x32_10([int(x, 16) for x in vec["ctr"]],
+                                       [int(x, 16) for x in vec["key"]], L=L)
+            assert got == [int(x, 16) for x in vec["out"]]
+
+    def dropout_unbiased():
+        keep = oracle.dropout_keep(77, 64, 1, 256, 256, L=L).astype(np.float64)
+        assert abs(keep.mean() - 0.75) < 0.01
+        rng = np.random.default_rng(9)
+        q, k, v = (rng.standard_normal((64, 4)) for _ in range(3))
+        v[:] = 1.0  # O = sum_j P_j Z_j: its mean over rows is E[Z] = 1
+        o, _ = oracle.attention_dropout_f64(q, k, v, False, 0.0001, 64, 5, L=L)
+        assert abs(o.mean() - 1.0) < 0.05
+
+    def dropout_finite_differences():
+        rng = np.random.default_rng(10)
+        q, k, v, dout = (rng.standard_normal((4, 3)) for _ in range(4))
+        got = oracle.attention_bwd_dropout_f64(q, k, v, dout, False, 0.6, 90, 3, 0, L=L)
+        h = 1e-5
+        for which in range(3):
+            for idx in np.ndindex(4, 3):
+                args = [q.copy(), k.copy(), v.copy()]
+                args[which][idx] += h
+                up = np.sum(dout * oracle.attention_dropout_f64(*args, False, 0.6, 90, 3, L=L)[0])
+                args[which][idx] -= 2 * h
+                dn = np.sum(dout * oracle.attention_dropout_f64(*args, False, 0.6, 90, 3, L=L)[0])
+                assert abs((up - dn) / (2 * h) - got[which][idx]) < 1e-7
+
     for name, fn in [("worked_example", worked_example), ("torch_sdpa", torch_sdpa),
                      ("lse_scipy", lse_scipy), ("part2_vs_part1", part2_vs_part1),
                      ("merge_closed_form", merge_closed_form),
                      ("bwd_finite_differences", bwd_finite_differences),
-                     ("bwd_torch_autograd", bwd_torch_autograd)]:
+                     ("bwd_torch_autograd", bwd_torch_autograd), ("philox_kat", philox_kat),
+                     ("dropout_unbiased", dropout_unbiased),
+                     ("dropout_finite_differences", dropout_finite_differences)]:
         check(name, fn)
     return failed
 
