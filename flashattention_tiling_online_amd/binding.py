@@ -18,7 +18,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH = 0, 1, 2, 3
 
 # symbols include/fa.h declares
 EXPORTS = ("fa_fwd", "fa_fwd_split", "fa_fwd_split_workspace", "fa_merge", "fa_split_hint",
-           "fa_bwd", "fa_bwd_workspace", "fa_status_str", "fa_tile_rows")
+           "fa_bwd", "fa_bwd_workspace", "fa_fwd_dropout", "fa_bwd_dropout", "fa_status_str",
+           "fa_tile_rows")
 
 _lib = None
 
@@ -62,6 +63,11 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd.restype = ctypes.c_int
         L.fa_bwd_workspace.argtypes = [i64, i64, i64, i64]
         L.fa_bwd_workspace.restype = i64
+        drop = [ctypes.c_float, ctypes.c_uint64]
+        L.fa_fwd_dropout.argtypes = L.fa_fwd.argtypes[:12] + drop + L.fa_fwd.argtypes[12:]
+        L.fa_fwd_dropout.restype = ctypes.c_int
+        L.fa_bwd_dropout.argtypes = L.fa_bwd.argtypes[:16] + drop + L.fa_bwd.argtypes[16:]
+        L.fa_bwd_dropout.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -102,6 +108,24 @@ def fa_bwd_raw(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk:
     """Direct call of fa_bwd with integer device pointers; returns the status code."""
     return lib().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, int(causal),
                         float(scale), int(dtype), workspace, int(workspace_bytes), stream)
+
+
+def fa_fwd_dropout_raw(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int,
+                       Nk: int, d: int, causal: bool, scale: float, p_drop: float, seed: int,
+                       dtype: int, stream: int) -> int:
+    """Direct call of fa_fwd_dropout with integer device pointers; returns the status code."""
+    return lib().fa_fwd_dropout(q, k, v, o, lse, B, H, Nq, Nk, d, int(causal), float(scale),
+                                float(p_drop), int(seed) & 0xFFFFFFFFFFFFFFFF, int(dtype), stream)
+
+
+def fa_bwd_dropout_raw(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int,
+                       dv: int, B: int, H: int, Nq: int, Nk: int, d: int, causal: bool,
+                       scale: float, p_drop: float, seed: int, dtype: int, workspace: int,
+                       workspace_bytes: int, stream: int) -> int:
+    """Direct call of fa_bwd_dropout with integer device pointers; returns the status code."""
+    return lib().fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, int(causal),
+                                float(scale), float(p_drop), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                                int(dtype), workspace, workspace_bytes, stream)
 
 
 def fa_bwd_workspace(B: int, H: int, Nq: int, d: int) -> int:
@@ -249,3 +273,55 @@ def fa_fwd(q, k, v, causal: bool = False, scale: float | None = None, o=None, ls
     if st != FA_OK:
         raise FAError(st)
     return o, lse
+
+
+def fa_fwd_dropout(q, k, v, p_drop: float, seed: int, causal: bool = False,
+                   scale: float | None = None, o=None, lse=None, stream=None):
+    """fa_fwd with dropout on P (fa_fwd_dropout): O = (P o Z) V, L as without dropout."""
+    import torch
+    B, H, Nq, Nk, d = _check_qkv(q, k, v)
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_fwd_dropout_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                            lse.data_ptr(), B, H, Nq, Nk, d, bool(causal), scale, p_drop, seed,
+                            code, stream.cuda_stream)
+    if st != FA_OK:
+        raise FAError(st)
+    return o, lse
+
+
+def fa_bwd_dropout(q, k, v, o, lse, dout, p_drop: float, seed: int, causal: bool = False,
+                   scale: float | None = None, dq=None, dk=None, dv=None, workspace=None,
+                   stream=None):
+    """fa_bwd with the dropout of fa_fwd_dropout (same p_drop and seed)."""
+    import torch
+    B, H, Nq, Nk, d = _check_qkv(q, k, v)
+    for name, t in (("o", o), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor shaped and typed like q")
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(max(16, fa_bwd_workspace(B, H, Nq, d)), dtype=torch.uint8,
+                                device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_bwd_dropout_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                            lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                            dv.data_ptr(), B, H, Nq, Nk, d, bool(causal), scale, p_drop, seed,
+                            code, workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), stream.cuda_stream)
+    if st != FA_OK:
+        raise FAError(st)
+    return dq, dk, dv

@@ -73,6 +73,32 @@ bool pick(fa_dtype_t dtype, int64_t d, int causal, bool split, Launch* out)
     return false;
 }
 
+// the forward kernel with dropout on P (16-bit inputs, unsplit)
+template <typename T>
+Launch mfma16_drop(int64_t d, bool c)
+{
+    auto one = [](const void* fn, int rows, int threads) { return Launch{fn, rows, threads}; };
+    if (d == 128)
+        return c ? one(reinterpret_cast<const void*>(&fa::fa_fwd_mfma16_kernel<T, 128, true, false, true>),
+                       fa::Tile16<128>::BR, fa::Tile16<128>::NT)
+                 : one(reinterpret_cast<const void*>(&fa::fa_fwd_mfma16_kernel<T, 128, false, false, true>),
+                       fa::Tile16<128>::BR, fa::Tile16<128>::NT);
+    return c ? one(reinterpret_cast<const void*>(&fa::fa_fwd_mfma16_kernel<T, 64, true, false, true>),
+                   fa::Tile16<64>::BR, fa::Tile16<64>::NT)
+             : one(reinterpret_cast<const void*>(&fa::fa_fwd_mfma16_kernel<T, 64, false, false, true>),
+                   fa::Tile16<64>::BR, fa::Tile16<64>::NT);
+}
+
+// the byte threshold of a drop probability: t = round(256 p); -1 outside [0, 1) or
+// beyond 255
+int drop_threshold(float p)
+{
+    if (!(p >= 0.0f) || !(p < 1.0f))
+        return -1;
+    const long t = lrintf(p * 256.0f);
+    return t > 255 ? -1 : (int)t;
+}
+
 // Workgroups of the forward kernel that one CU holds at once (register and LDS
 // budgets of the kernels above): used only by fa_split_hint.
 int wgs_per_cu(fa_dtype_t dtype, int64_t d) { return d == 64 ? 2 : 1; }
@@ -142,12 +168,23 @@ fa_status_t check_fwd(const void* q, const void* k, const void* v, void* o, floa
 // exp(x) = 2^(x * log2 e): fold log2(e) into the scale once, in double
 float scale_log2e(float scale) { return (float)((double)scale * 1.4426950408889634074); }
 
+// dropout on P: byte threshold t (drop probability t / 256) and the 64-bit seed
+struct Dropout {
+    uint32_t t;
+    uint64_t seed;
+};
+
 template <typename T>
 hipError_t launch_fwd(const Launch& L, const void* q, const void* k, const void* v, void* o,
                       float* lse, float* o_part, float* lse_part, int64_t BH, int64_t Nq,
-                      int64_t Nk, int n_splits, int split_tiles, float scale, hipStream_t stream)
+                      int64_t Nk, int n_splits, int split_tiles, float scale, hipStream_t stream,
+                      const Dropout* drop = nullptr)
 {
     fa::FwdParams<T> prm;
+    prm.drop_key0 = drop ? (uint32_t)drop->seed : 0u;
+    prm.drop_key1 = drop ? (uint32_t)(drop->seed >> 32) : 0u;
+    prm.drop_t = drop ? drop->t : 0u;
+    prm.drop_keep_scale = drop ? (float)(256.0 / (256.0 - (double)drop->t)) : 1.0f;
     prm.q = static_cast<const T*>(q);
     prm.k = static_cast<const T*>(k);
     prm.v = static_cast<const T*>(v);
@@ -170,15 +207,15 @@ hipError_t launch_fwd(const Launch& L, const void* q, const void* k, const void*
 hipError_t launch_fwd_any(fa_dtype_t dtype, const Launch& L, const void* q, const void* k,
                           const void* v, void* o, float* lse, float* o_part, float* lse_part,
                           int64_t BH, int64_t Nq, int64_t Nk, int n_splits, int split_tiles,
-                          float scale, hipStream_t stream)
+                          float scale, hipStream_t stream, const Dropout* drop = nullptr)
 {
     switch (dtype) {
     case FA_DTYPE_BF16:
         return launch_fwd<__bf16>(L, q, k, v, o, lse, o_part, lse_part, BH, Nq, Nk, n_splits,
-                                  split_tiles, scale, stream);
+                                  split_tiles, scale, stream, drop);
     case FA_DTYPE_F16:
         return launch_fwd<_Float16>(L, q, k, v, o, lse, o_part, lse_part, BH, Nq, Nk, n_splits,
-                                    split_tiles, scale, stream);
+                                    split_tiles, scale, stream, drop);
     default:
         return launch_fwd<float>(L, q, k, v, o, lse, o_part, lse_part, BH, Nq, Nk, n_splits,
                                  split_tiles, scale, stream);
@@ -224,6 +261,34 @@ extern "C" fa_status_t fa_fwd(const void* q, const void* k, const void* v, void*
         return st;
     const hipError_t err = launch_fwd_any(dtype, L, q, k, v, o, lse, nullptr, nullptr, B * H, Nq,
                                           Nk, 1, 0, scale, reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+extern "C" fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v, void* o,
+                                      float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                      int64_t d, int causal, float scale, float p_drop,
+                                      uint64_t seed, fa_dtype_t dtype, fa_stream_t stream)
+{
+    const int t = drop_threshold(p_drop);
+    if (t < 0)
+        return FA_ERR_INVALID_ARG;
+    Launch L;
+    bool empty;
+    const fa_status_t st =
+        check_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, false, &L, &empty);
+    if (st != FA_OK)
+        return st;
+    if (dtype == FA_DTYPE_F32)
+        return FA_ERR_UNSUPPORTED;
+    if (empty)
+        return FA_OK;
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    if (t > 0)
+        L = dtype == FA_DTYPE_BF16 ? mfma16_drop<__bf16>(d, causal != 0)
+                                   : mfma16_drop<_Float16>(d, causal != 0);
+    const Dropout drop{(uint32_t)t, seed};
+    const hipError_t err = launch_fwd_any(dtype, L, q, k, v, o, lse, nullptr, nullptr, B * H, Nq,
+                                          Nk, 1, 0, scale, hs, t > 0 ? &drop : nullptr);
     return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -332,11 +397,11 @@ extern "C" int fa_split_hint(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
 
 namespace {
 
-template <typename T, int D, bool C>
+template <typename T, int D, bool C, bool DR>
 hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* o,
                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
                         int64_t BH, int64_t Nq, int64_t Nk, float scale, float* delta,
-                        hipStream_t stream)
+                        hipStream_t stream, const Dropout& drop)
 {
     fa::BwdParams<T> prm;
     prm.q = static_cast<const T*>(q);
@@ -353,6 +418,10 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
     prm.Nk = (int)Nk;
     prm.c2 = scale_log2e(scale);
     prm.scale = scale;
+    prm.drop.key0 = (uint32_t)drop.seed;
+    prm.drop.key1 = (uint32_t)(drop.seed >> 32);
+    prm.drop.t = drop.t;
+    prm.drop.keep_scale = (float)(256.0 / (256.0 - (double)drop.t));
     hipError_t err;
     const int64_t rows = BH * Nq;
     if (rows > 0) {  // D = rowsum(dO o O)
@@ -369,27 +438,39 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
     void* args[] = {(void*)&prm};
     using PK = fa::DkvTile<D>;
     prm.n_tiles = (int)((Nk + PK::KEYS - 1) / PK::KEYS);  // dK, dV (zeros when Nq == 0)
-    err = hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dkv_kernel<T, D, C>),
+    err = hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dkv_kernel<T, D, C, DR>),
                           dim3((unsigned)(prm.n_tiles * BH)), dim3(PK::NT), args, 0, stream);
     if (err != hipSuccess || rows == 0)
         return err;
     using PQ = fa::DqTile<D>;
     prm.n_tiles = (int)((Nq + PQ::ROWS - 1) / PQ::ROWS);  // dQ
-    return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dq_kernel<T, D, C>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dq_kernel<T, D, C, DR>),
                            dim3((unsigned)(prm.n_tiles * BH)), dim3(PQ::NT), args, 0, stream);
+}
+
+template <typename T, bool DR>
+hipError_t launch_bwd_dr(int64_t d, int causal, const void* q, const void* k, const void* v,
+                         const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                         void* dv, int64_t BH, int64_t Nq, int64_t Nk, float scale, float* delta,
+                         hipStream_t s, const Dropout& dr)
+{
+    if (d == 128)
+        return causal ? launch_bwd_t<T, 128, true, DR>(q, k, v, o, lse, dout, dq, dk, dv, BH, Nq, Nk, scale, delta, s, dr)
+                      : launch_bwd_t<T, 128, false, DR>(q, k, v, o, lse, dout, dq, dk, dv, BH, Nq, Nk, scale, delta, s, dr);
+    return causal ? launch_bwd_t<T, 64, true, DR>(q, k, v, o, lse, dout, dq, dk, dv, BH, Nq, Nk, scale, delta, s, dr)
+                  : launch_bwd_t<T, 64, false, DR>(q, k, v, o, lse, dout, dq, dk, dv, BH, Nq, Nk, scale, delta, s, dr);
 }
 
 template <typename T>
 hipError_t launch_bwd_d(int64_t d, int causal, const void* q, const void* k, const void* v,
                         const void* o, const float* lse, const void* dout, void* dq, void* dk,
                         void* dv, int64_t BH, int64_t Nq, int64_t Nk, float scale, float* delta,
-                        hipStream_t s)
+                        hipStream_t s, const Dropout& dr)
 {
-    if (d == 128)
-        return causal ? launch_bwd_t<T, 128, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, Nq, Nk, scale, delta, s)
-                      : launch_bwd_t<T, 128, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Nq, Nk, scale, delta, s);
-    return causal ? launch_bwd_t<T, 64, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, Nq, Nk, scale, delta, s)
-                  : launch_bwd_t<T, 64, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Nq, Nk, scale, delta, s);
+    return dr.t > 0 ? launch_bwd_dr<T, true>(d, causal, q, k, v, o, lse, dout, dq, dk, dv, BH, Nq,
+                                             Nk, scale, delta, s, dr)
+                    : launch_bwd_dr<T, false>(d, causal, q, k, v, o, lse, dout, dq, dk, dv, BH,
+                                              Nq, Nk, scale, delta, s, dr);
 }
 
 }  // namespace
@@ -401,11 +482,13 @@ extern "C" int64_t fa_bwd_workspace(int64_t B, int64_t H, int64_t Nq, int64_t d)
     return round_up(B * H * Nq * 4, kAlign);
 }
 
-extern "C" fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
-                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
-                              float scale, fa_dtype_t dtype, void* workspace,
-                              int64_t workspace_bytes, fa_stream_t stream)
+namespace {
+
+fa_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                     int64_t Nq, int64_t Nk, int64_t d, int causal, float scale,
+                     fa_dtype_t dtype, void* workspace, int64_t workspace_bytes,
+                     fa_stream_t stream, const Dropout& drop)
 {
     if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
         return FA_ERR_INVALID_ARG;
@@ -441,10 +524,36 @@ extern "C" fa_status_t fa_bwd(const void* q, const void* k, const void* v, const
     const hipError_t err =
         dtype == FA_DTYPE_BF16
             ? launch_bwd_d<__bf16>(d, causal, q, k, v, o, lse, dout, dq, dk, dv, B * H, Nq, Nk,
-                                   scale, delta, hs)
+                                   scale, delta, hs, drop)
             : launch_bwd_d<_Float16>(d, causal, q, k, v, o, lse, dout, dq, dk, dv, B * H, Nq, Nk,
-                                     scale, delta, hs);
+                                     scale, delta, hs, drop);
     return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                              float scale, fa_dtype_t dtype, void* workspace,
+                              int64_t workspace_bytes, fa_stream_t stream)
+{
+    return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, causal, scale, dtype,
+                    workspace, workspace_bytes, stream, Dropout{0u, 0u});
+}
+
+extern "C" fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                                      const float* lse, const void* dout, void* dq, void* dk,
+                                      void* dv, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                      int64_t d, int causal, float scale, float p_drop,
+                                      uint64_t seed, fa_dtype_t dtype, void* workspace,
+                                      int64_t workspace_bytes, fa_stream_t stream)
+{
+    const int t = drop_threshold(p_drop);
+    if (t < 0)
+        return FA_ERR_INVALID_ARG;
+    return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, causal, scale, dtype,
+                    workspace, workspace_bytes, stream, Dropout{(uint32_t)t, seed});
 }
 
 extern "C" const char* fa_status_str(fa_status_t status)

@@ -24,6 +24,7 @@
 // and L taken in base 2.
 #pragma once
 
+#include "fa_philox.hpp"
 #include "fa_tiles.hpp"
 
 namespace fa {
@@ -44,6 +45,7 @@ struct BwdParams {
     int n_tiles;      // tiles per head of the kernel's outer dimension
     float c2;         // scale * log2(e)
     float scale;
+    DropParams drop;  // dropout on P (dropout instantiations only)
 };
 
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -125,7 +127,7 @@ __device__ __forceinline__ void store_row_block(char* dst, int kg, int dq, const
         *reinterpret_cast<u32x2*>(dst + (4 * kg + m) * RSTR + 8 * dq) = r[m];
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool DROP = false>
 __global__ __launch_bounds__(DkvTile<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_bwd_dkv_kernel(const BwdParams<T> prm)
 {
@@ -249,21 +251,30 @@ void fa_bwd_dkv_kernel(const BwdParams<T> prm)
             dp = M::mma(b, vf, dp);
         }
         // P = 2^(s c2 - L2), dS = P (dP - D); register r holds query
-        // qw + 8(r/4) + 4hh + r%4
+        // qw + 8(r/4) + 4hh + r%4.  With dropout Z: dV takes P o Z, dS takes dP o Z.
         vec pp[2], ps[2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int qo = 32 * qh + 8 * g + 4 * hh;
             const f32x4 l2 = *reinterpret_cast<const f32x4*>(sm + P::LS + qo * 4);
             const f32x4 dd = *reinterpret_cast<const f32x4*>(sm + P::DS + qo * 4);
+            uint32_t bytes = 0;
+            if (DROP)
+                bytes = drop_bytes_k(prm.drop, bh, i * P::TILE + qo, my_k);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * g + e;
                 float p = exp2_fast(fmaf(s[r], prm.c2, -l2[e]));
                 if (diag && my_k > i * P::TILE + qo + e)
                     p = 0.f;  // key after the query
-                pp[r >> 3][r & 7] = (T)p;
-                ps[r >> 3][r & 7] = (T)(p * (dp[r] - dd[e]));
+                if (DROP) {
+                    const float z = drop_keep(bytes, e, prm.drop.t) ? prm.drop.keep_scale : 0.f;
+                    pp[r >> 3][r & 7] = (T)(p * z);
+                    ps[r >> 3][r & 7] = (T)(p * (dp[r] * z - dd[e]));
+                } else {
+                    pp[r >> 3][r & 7] = (T)p;
+                    ps[r >> 3][r & 7] = (T)(p * (dp[r] - dd[e]));
+                }
             }
         }
         // dV^T += dO^T P, dK^T += Q^T dS over chunks 2qh, 2qh+1 of the tile
@@ -339,7 +350,7 @@ struct DqTile {
     static_assert(NT == 4 * D, "one 4x4 block per tensor per thread");
 };
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool DROP = false>
 __global__ __launch_bounds__(DqTile<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_bwd_dq_kernel(const BwdParams<T> prm)
 {
@@ -444,15 +455,25 @@ void fa_bwd_dq_kernel(const BwdParams<T> prm)
         const int last = CAUSAL ? min(Nk - 1, my_q) : Nk - 1;
         vec ps[4];
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
+        for (int cc = 0; cc < 4; ++cc) {
+            // chunk cc holds keys 16cc + 4hh + 0..3 (e < 4) and 16cc + 8 + 4hh + 0..3
+            uint32_t bytes[2] = {0u, 0u};
+            if (DROP) {
+                bytes[0] = drop_bytes_q(prm.drop, bh, my_q, key0 + 16 * cc + 4 * hh);
+                bytes[1] = drop_bytes_q(prm.drop, bh, my_q, key0 + 16 * cc + 8 + 4 * hh);
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int kb = cc >> 1, r = 8 * (cc & 1) + e;
                 float p = exp2_fast(fmaf(st[kb][r], prm.c2, -l2));
                 if (mask && key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3) > last)
                     p = 0.f;
-                ps[cc][e] = (T)(p * (dpt[kb][r] - dd));
+                float dpz = dpt[kb][r];
+                if (DROP)
+                    dpz *= drop_keep(bytes[e >> 2], e & 3, prm.drop.t) ? prm.drop.keep_scale : 0.f;
+                ps[cc][e] = (T)(p * (dpz - dd));
             }
+        }
         // dQ^T += K^T dS^T
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc)

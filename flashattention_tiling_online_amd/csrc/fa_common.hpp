@@ -55,6 +55,10 @@ struct FwdParams {
     float* lse_part;
     int Nq, Nk, n_qtiles, bh_count, n_splits, split_tiles;
     float c2;  // scale * log2(e)
+    // dropout on P (used by the dropout instantiations only): seed halves, byte
+    // threshold and keep scale, as in fa_philox.hpp
+    uint32_t drop_key0, drop_key1, drop_t;
+    float drop_keep_scale;
 };
 
 // -inf as a float constant usable in device code

@@ -44,6 +44,7 @@
 //     from (see update_max).
 #pragma once
 
+#include "fa_philox.hpp"
 #include "fa_tiles.hpp"
 
 namespace fa {
@@ -72,7 +73,7 @@ struct Tile16 {
     static_assert(KT % 1024 == 0, "K tiles must be whole DMA blocks");
 };
 
-template <typename T, int D, bool CAUSAL, bool SPLIT>
+template <typename T, int D, bool CAUSAL, bool SPLIT, bool DROP = false>
 __global__ __launch_bounds__(Tile16<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
 {
@@ -256,7 +257,7 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
     // T and packed in the MFMA B-operand order (chunk cc = 2kb + h holds registers
     // 8h .. 8h+7 of block kb); the rounded values summed into lr with v_dot2.  A row
     // with no visible key so far (m2 = -inf) gets p = 0.
-    auto exp_sum_pack = [&](f32x16* s, vec* pb) {
+    auto exp_sum_pack = [&](int j, f32x16* s, vec* pb) {
         const float mneg = (m2 == neg_inf()) ? 0.f : -m2;
         float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -277,6 +278,23 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
                 rr[e & 1] = M::dot_ones(w[e], rr[e & 1]);
         }
         lr += rr[0] + rr[1];
+        if (DROP) {
+            // dropout on the P that multiplies V (l and lr keep the undropped P, the
+            // keep scale is applied in the epilogue): chunk cc holds keys
+            // 16cc + 4hh + 0..3 (e < 4) and 16cc + 8 + 4hh + 0..3 (e >= 4) of the tile
+            const DropParams dp{prm.drop_key0, prm.drop_key1, prm.drop_t, prm.drop_keep_scale};
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    const int k4 = kbeg + j * P::BC + 16 * cc + 8 * g + 4 * hh;
+                    const uint32_t bytes = drop_bytes_q(dp, bh, my_q, k4);
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        if (!drop_keep(bytes, m, dp.t))
+                            pb[cc][4 * g + m] = (T)0.f;
+                }
+        }
     };
 
     // O^T += V^T P^T from the V^T buffer at vb_off
@@ -315,7 +333,7 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
             update_max(m_cur);
             scores(kn, s_nxt);
             vec pb[4];
-            exp_sum_pack(s_cur, pb);
+            exp_sum_pack(j, s_cur, pb);
             pv(pb, vc);
             m_nxt = half_max(s_nxt);
         } else if (j < n_w) {
@@ -325,7 +343,7 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
             }
             update_max(m_cur);
             vec pb[4];
-            exp_sum_pack(s_cur, pb);
+            exp_sum_pack(j, s_cur, pb);
             pv(pb, vc);
         }
         if (j + 1 < nkt)
@@ -368,7 +386,7 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
             if (hh == 0)
                 prm.lse_part[row] = lt > 0.f ? (m2 + log2_fast(lt)) * kLn2 : neg_inf();
         } else {
-            const float inv = 1.0f / lrt;
+            const float inv = (DROP ? prm.drop_keep_scale : 1.0f) / lrt;
             T* orow = prm.o + ((size_t)bh * Nq + my_q) * D;
 #pragma unroll
             for (int db = 0; db < P::DB; ++db)

@@ -195,6 +195,42 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
  * d outside {64, 128}. */
 int64_t fa_bwd_workspace(int64_t B, int64_t H, int64_t Nq, int64_t d);
 
+/*
+ * fa_fwd_dropout / fa_bwd_dropout — the forward and backward above with dropout on P.
+ * The "Flash Attention" blog page (Algorithm 2) drops entries of P after the softmax
+ * and multiplies the kept ones by 1/(1 - p): O = (P o Z) V with L unchanged (the
+ * logsumexp of the undropped scores); its Algorithm 4 regenerates the same Z from the
+ * saved generator state and uses P_dropped = P o Z for dV and dP o Z in dS:
+ *
+ *     dV = (P o Z)^T dO,  dS = P o (dP o Z - D),  D = rowsum(dO o O)
+ *
+ * The pages name no generator.  Z here: Philox4x32-10 (Salmon, Moraes, Dror, Shaw,
+ * "Parallel random numbers: as easy as 1, 2, 3", SC'11) with key (seed bits 0-31,
+ * seed bits 32-63) and counter (k / 4, q / 4, b * H + h, 0); element (q, k) of head
+ * b * H + h takes byte 4 (q % 4) + k % 4 of the output (word q % 4, bits 8 (k % 4) ..
+ * 8 (k % 4) + 7) and is dropped iff that byte is below t = round(256 p_drop); a kept
+ * element is multiplied by 256 / (256 - t).  The drop probability is thus t / 256,
+ * p_drop rounded to a multiple of 1/256.  The same (seed, p_drop) in both calls gives
+ * the same Z, independent of tile shapes and launch order.
+ *
+ * Arguments as fa_fwd / fa_bwd, plus:
+ *   p_drop  drop probability, 0 <= p_drop < 1 with round(256 p_drop) <= 255, else
+ *           FA_ERR_INVALID_ARG; p_drop that rounds to t = 0 gives fa_fwd's / fa_bwd's
+ *           result
+ *   seed    the generator key (any value)
+ * dtype must be FA_DTYPE_BF16 or FA_DTYPE_F16 (FA_DTYPE_F32: FA_ERR_UNSUPPORTED).
+ * Behaviour, ownership, limits and the workspace of fa_bwd_dropout: as fa_fwd / fa_bwd.
+ */
+fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                           float scale, float p_drop, uint64_t seed, fa_dtype_t dtype,
+                           fa_stream_t stream);
+fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                           float scale, float p_drop, uint64_t seed, fa_dtype_t dtype,
+                           void* workspace, int64_t workspace_bytes, fa_stream_t stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* fa_status_str(fa_status_t status);
 

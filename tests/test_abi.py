@@ -192,6 +192,42 @@ def test_bwd_validation_before_any_hip_call(kw, want):
     assert _bwd(**kw) == want
 
 
+def _fwd_drop(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Nq=8, Nk=8, d=64, causal=0, scale=0.125,
+             p_drop=0.1, seed=1, dtype=fa.FA_DTYPE_BF16, stream=0)
+    a.update(kw)
+    return fa.fa_fwd_dropout_raw(**a)
+
+
+def _bwd_drop(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, B=1, H=2, Nq=64, Nk=64, d=128,
+             causal=0, scale=0.1, p_drop=0.1, seed=1, dtype=fa.FA_DTYPE_BF16, workspace=P,
+             workspace_bytes=1 << 20, stream=0)
+    a.update(kw)
+    return fa.fa_bwd_dropout_raw(**a)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(p_drop=1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(p_drop=-0.01), fa.FA_ERR_INVALID_ARG),
+    (dict(p_drop=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(p_drop=0.999), fa.FA_ERR_INVALID_ARG),          # rounds to t = 256
+    (dict(dtype=fa.FA_DTYPE_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_OK),
+    (dict(Nq=0, p_drop=0.5, seed=(1 << 64) - 1), fa.FA_OK),
+])
+def test_dropout_validation_before_any_hip_call(kw, want):
+    assert _fwd_drop(**kw) == want
+    bkw = {k: v for k, v in kw.items() if k != "Nq"}
+    if "Nq" in kw:  # no queries: the backward writes zero key gradients (a GPU call)
+        bkw["B"] = 0
+    assert _bwd_drop(**bkw) == want
+
+
 def test_bwd_workspace_size():
     assert fa.fa_bwd_workspace(2, 8, 1024, 64) == 2 * 8 * 1024 * 4
     assert fa.fa_bwd_workspace(1, 1, 3, 128) == 256
