@@ -12,6 +12,7 @@
 #include "fa_bwd.hpp"
 #include "fa_fwd_f32.hpp"
 #include "fa_fwd_mfma16.hpp"
+#include "fa_fwd_pp.hpp"
 #include "fa_merge.hpp"
 
 namespace {
@@ -40,9 +41,19 @@ Launch f32()
                   fa::TileF32<D>::BR, fa::TileF32<D>::NT};
 }
 
+template <typename T, bool C>
+Launch pp()
+{
+    return Launch{reinterpret_cast<const void*>(&fa::fa_fwd_pp_kernel<T, C>), fa::TilePP::BR,
+                  fa::TilePP::NT};
+}
+
+// d = 128 without key splits: the phase-alternating kernel; otherwise fa_fwd_mfma16
 template <typename T, bool S>
 Launch mfma16_of(int64_t d, bool c)
 {
+    if (d == 128 && !S)
+        return c ? pp<T, true>() : pp<T, false>();
     return d == 128 ? (c ? mfma16<T, 128, true, S>() : mfma16<T, 128, false, S>())
                     : (c ? mfma16<T, 64, true, S>() : mfma16<T, 64, false, S>());
 }

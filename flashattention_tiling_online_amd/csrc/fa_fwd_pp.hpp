@@ -1,0 +1,370 @@
+// fa_fwd_pp.hpp — fused attention forward for bf16 / fp16 inputs and d = 128 on
+// gfx950, with the two waves of every SIMD in alternating phases.
+//
+// The arithmetic is that of fa_fwd_mfma16.hpp (the course page "05_flash_attention.py",
+// flash_attention_forward: per query tile m = -inf, l = 0, O~ = 0; per key/value tile
+// S = Q K_j^T scale, m_new = max(m, rowmax S), P = exp(S - m_new), l = alpha l +
+// rowsum P, O~ = alpha O~ + P V_j; O = O~ / l and L = m + log l at the end), with the
+// same transposed 32x32x16 MFMA formulation, lazy max reference and two row sums.
+// What differs is the schedule.
+//
+// A workgroup is 8 waves (256 query rows) and fills a CU; waves w and w + 4 share a
+// SIMD.  Waves 0-3 form group 0, waves 4-7 group 1, and the two groups run in
+// opposite phases separated by workgroup barriers:
+//   * an MFMA phase of tile j: S_{j+1} = K_{j+1} Q^T (16 MFMAs) and O~ += V_j^T P_j^T
+//     (16 MFMAs), operands read from LDS, nothing else;
+//   * a softmax phase of tile u: mask, running max, P_u = 2^(S_u c - m) rounded to
+//     T, the two row sums, plus this group's share of the K/V staging.
+// While one wave of a SIMD issues its 32 MFMAs back to back, the other wave's
+// softmax instructions take the issue slots the matrix core leaves free, instead of
+// both waves contending for the same slots in the same phase:
+//     phase 2j:    group 0 MFMA(j),     group 1 softmax(j)
+//     phase 2j+1:  group 0 softmax(j+1), group 1 MFMA(j)
+// Query rows are assigned so that the two waves of a SIMD own adjacent 32-row
+// blocks (wave w: rows 32 (2 (w % 4) + w / 4) of the tile), which keeps their
+// causal tile counts within one of each other.
+//
+// Staging (K by DMA into rows padded by 16 B, V transposed through registers into
+// V^T rows, exactly as fa_fwd_mfma16.hpp lays them out): three K buffers and two V^T
+// buffers.  Group 0 writes dims 0-63 of V^T_u and issues its K blocks of K_{u+2} in
+// its softmax phase of tile u (phase 2u-1); group 1 writes dims 64-127 of V^T_{u+1}
+// and issues its K blocks of K_{u+2} in its softmax phase of tile u (phase 2u).  A
+// group waits for its loads at the end of its following MFMA phase; the first
+// reader of K_t (group 0, phase 2t-2) and of V^T_t (group 0, phase 2t) comes after
+// both groups' waits, and no buffer is rewritten before its last reader's phase has
+// ended.
+#pragma once
+
+#include "fa_tiles.hpp"
+
+namespace fa {
+
+struct TilePP {
+    static constexpr int D = 128;
+    static constexpr int NW = 8;              // waves per workgroup
+    static constexpr int BR = 256;            // query rows per workgroup
+    static constexpr int BC = 64;             // keys per K/V tile
+    static constexpr int NT = 512;            // threads per workgroup
+    static constexpr int KSTR = 2 * D + 16;   // K row stride in LDS
+    static constexpr int VTSTR = 2 * BC + 16; // V^T row stride in LDS
+    static constexpr int KT = BC * KSTR;      // bytes of one K tile in LDS
+    static constexpr int VT = D * VTSTR;      // bytes of one V^T tile in LDS
+    static constexpr int KNB = KT / 1024;     // 1-KB DMA blocks per K tile
+    static constexpr int KPW = (KNB + NW - 1) / NW;
+    static constexpr int DC = D / 16;
+    static constexpr int DB = D / 32;
+    static constexpr int NKB = 3;             // K buffers
+    static constexpr int VOFF = NKB * KT;     // first V^T buffer
+    static constexpr int LDS = NKB * KT + 2 * VT;
+    static_assert(KT % 1024 == 0, "K tiles must be whole DMA blocks");
+    static_assert(NT == 4 * D, "V staging: one 4-key x 4-dim block per thread");
+};
+
+// s_waitcnt immediates (gfx9 encoding): LDS only, and all memory
+constexpr int kWaitLds = 0xC07F;  // lgkmcnt(0)
+constexpr int kWaitAll = 0x0070;  // vmcnt(0) lgkmcnt(0)
+
+template <typename T, bool CAUSAL>
+__global__ __launch_bounds__(TilePP::NT) __attribute__((amdgpu_waves_per_eu(2)))
+void fa_fwd_pp_kernel(const FwdParams<T> prm)
+{
+    using P = TilePP;
+    using M = Mfma16<T>;
+    using vec = typename M::vec;
+    constexpr int D = P::D;
+    typedef T T4 __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(1024))) char smem[P::LDS];
+    const char* const sm = smem;
+    const int Nq = prm.Nq, Nk = prm.Nk, n_qtiles = prm.n_qtiles;
+    const float c2 = prm.c2;
+
+    // ---- (batch*head, query tile) of this workgroup, XCD-aware, causal longest first
+    const int logical = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+    const int bh = logical / n_qtiles;
+    int qt = logical - bh * n_qtiles;
+    if (CAUSAL)
+        qt = n_qtiles - 1 - qt;
+    const int q0 = qt * P::BR;
+
+    const int tid = (int)threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;  // ping-pong group (wave-uniform)
+    const int lane = tid & 63;
+    const int ql = lane & 31;
+    const int hh = lane >> 5;
+    const int qw0 = q0 + 32 * (2 * (wave & 3) + grp);
+    const int my_q = qw0 + ql;
+
+    const T* Qh = prm.q + (size_t)bh * Nq * D;
+    const T* Kh = prm.k + (size_t)bh * Nk * D;
+    const T* Vh = prm.v + (size_t)bh * Nk * D;
+
+    // ---- key tiles: the workgroup stages nkt, this wave computes n_w
+    int nkt = (Nk + P::BC - 1) / P::BC;
+    if (CAUSAL) {
+        const int last = min(q0 + P::BR, Nq) - 1;
+        nkt = min(nkt, last / P::BC + 1);
+    }
+    const bool wave_active = qw0 < Nq;
+    int n_w = wave_active ? nkt : 0;
+    if (CAUSAL && wave_active)
+        n_w = min(nkt, min(qw0 + 31, Nq - 1) / P::BC + 1);
+
+    auto kbuf = [](int t) { return (t % P::NKB) * P::KT; };
+    auto vbuf = [](int t) { return P::VOFF + (t & 1) * P::VT; };
+
+    // ---- staging: K blocks of this wave (DMA), V block of this thread (registers;
+    // group 0 threads cover dims 0-63, group 1 threads dims 64-127)
+    int ksrc[P::KPW];
+#pragma unroll
+    for (int i = 0; i < P::KPW; ++i)
+        ksrc[i] = dma_src<D>(wave + P::NW * i, lane, P::KSTR);
+    auto stage_k = [&](int t) {
+        stage_tile<D, P::KNB, P::KPW, P::NW>(Kh, t, Nk, smem + kbuf(t), wave, ksrc);
+    };
+    const int v_dq = (tid & 3) + 4 * (tid >> 6);
+    const int v_kg = ((tid >> 2) & 3) + 4 * (((tid >> 4) & 1) + 2 * ((tid >> 5) & 1));
+    u32x2 vreg[4];
+    auto load_v = [&](int t) { load_v_block<D>(Vh, t, Nk, v_kg, v_dq, vreg); };
+    auto write_vt = [&](int t) { store_vt_block<P::VTSTR>(smem + vbuf(t), v_kg, v_dq, vreg); };
+
+    const int kbase = ql * P::KSTR + hh * 16;
+    const int vbase = ql * P::VTSTR + hh * 16;
+
+    // ---- Q fragment (B operand of S^T = K Q^T): lane supplies Q[my_q][16c + 8hh .. +8]
+    vec qf[P::DC];
+#pragma unroll
+    for (int c = 0; c < P::DC; ++c) {
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (my_q < Nq)
+            raw = *reinterpret_cast<const u32x4*>(Qh + (size_t)my_q * D + 16 * c + 8 * hh);
+        qf[c] = __builtin_bit_cast(vec, raw);
+    }
+
+    // ---- running state
+    f32x16 o[P::DB];
+#pragma unroll
+    for (int db = 0; db < P::DB; ++db)
+        o[db] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    f32x16 s[2];  // S^T of the tile whose softmax is next
+    vec pb[4];    // P of the tile whose P.V is next, rounded, B-operand order
+    float m2 = neg_inf();
+    float l = 0.f;   // this half's sum of the fp32 P (for L)
+    float lr = 0.f;  // this half's sum of the rounded P (for the normalisation of O)
+
+    // S^T of one tile from the K buffer at kb_off
+    auto scores_only = [&](int kb_off) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            s[kb] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < P::DC; ++c)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const vec a = *reinterpret_cast<const vec*>(sm + kb_off + kbase + 32 * c + kb * 32 * P::KSTR);
+                s[kb] = M::mma(a, qf[c], s[kb]);
+            }
+    };
+    // both, interleaved: S^T of tile j+1 and P.V of tile j; the operand reads run
+    // four MFMAs ahead (a fixed DS-read / MFMA order keeps the operands in flight,
+    // and their registers, bounded)
+    auto scores_pv = [&](int kb_off, int vb_off) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            s[kb] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int c = i >> 1, kb = i & 1;
+            const vec a = *reinterpret_cast<const vec*>(sm + kb_off + kbase + 32 * c + kb * 32 * P::KSTR);
+            s[kb] = M::mma(a, qf[c], s[kb]);
+            const int cc = i >> 2, db = i & 3;
+            const vec b = *reinterpret_cast<const vec*>(sm + vb_off + vbase + 32 * db * P::VTSTR + 32 * cc);
+            o[db] = M::mma(b, pb[cc], o[db]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 28; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    };
+
+    // Mask of tile j (keys past the end, or after the query): only a wave's last
+    // tile can need it (its first query is a multiple of 32, tiles are 64 keys).
+    auto needs_mask = [&](int j) {
+        const int key0 = j * P::BC;
+        return (key0 + P::BC > Nk) || (CAUSAL && key0 + P::BC - 1 > qw0);
+    };
+    auto mask_tile = [&](int j) {
+        const int key0 = j * P::BC;
+        const int last = CAUSAL ? min(Nk - 1, my_q) : Nk - 1;
+        const int lim = last - key0 - 4 * hh;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+                if (off > lim)
+                    s[kb][r] = neg_inf();
+            }
+    };
+
+    // Lazy running max (as in fa_fwd_mfma16.hpp): the reference m2 moves, with the
+    // rescale of O~, l and lr by 2^(m2 - m_new), only when some row exceeds it by
+    // more than kSlack; O is divided by the sum of the same rounded P that entered
+    // the P.V MFMAs, L uses the fp32 sum.  The rescale of O~ is applied by the next
+    // MFMA phase (O~ is touched by MFMA phases only): `rescale` marks it pending,
+    // alpha holds the factor.
+    constexpr float kSlack = 8.0f;
+    bool rescale = false;
+    float alpha = 1.f;
+    auto update_max = [&]() {
+        float mx = s[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                mx = fmaxf(mx, s[kb][r]);
+        const float mh = mx * c2;  // c2 > 0: max commutes with the scale
+        if (__builtin_amdgcn_ballot_w64(mh > m2 + kSlack) != 0) {
+            const float m_new = fmaxf(m2, fmaxf(mh, swap_halves(mh)));
+            alpha = exp2_fast(m2 - m_new);  // 0 on a wave's first tile (m2 = -inf)
+            rescale = true;
+            l *= alpha;
+            lr *= alpha;
+            m2 = m_new;
+        }
+    };
+    // P = 2^(s c2 - m2) in fp32, summed into l; rounded to T in the MFMA B-operand
+    // order (chunk cc = 2kb + h holds registers 8h .. 8h+7 of block kb); the rounded
+    // values summed into lr with v_dot2.  A row with no visible key so far
+    // (m2 = -inf) gets p = 0.
+    auto exp_sum_pack = [&]() {
+        const float mneg = (m2 == neg_inf()) ? 0.f : -m2;
+        float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float p = exp2_fast(fmaf(s[cc >> 1][8 * (cc & 1) + e], c2, mneg));
+                rs[e & 3] += p;
+                pb[cc][e] = (T)p;
+            }
+        l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+        float rr[2] = {0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            const u32x4 w = __builtin_bit_cast(u32x4, pb[cc]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                rr[e & 1] = M::dot_ones(w[e], rr[e & 1]);
+        }
+        lr += rr[0] + rr[1];
+    };
+    auto softmax = [&](int u) {
+        if (u < n_w) {
+            if (needs_mask(u))
+                mask_tile(u);
+            update_max();
+            exp_sum_pack();
+        }
+    };
+    // MFMA phase of tile j: S^T of tile j+1 (if this wave has it) and P.V of tile j
+    // (j = -1: only S^T of tile 0)
+    auto mfma = [&](int j) {
+        if (rescale) {
+#pragma unroll
+            for (int db = 0; db < P::DB; ++db)
+                o[db] *= alpha;
+            rescale = false;
+        }
+        // on a wave's last tile the S^T MFMAs read a K buffer that holds no tile of
+        // this wave (stale but allocated LDS) and their result is never used: one
+        // code path keeps O~ in the same registers throughout the loop
+        if (j < n_w)
+            scores_pv(kbuf(j + 1), vbuf(j));
+    };
+    // this group's staging in its softmax phase of tile u: group 0 writes V^T_u (dims
+    // 0-63) and loads V_{u+1}, group 1 writes V^T_{u+1} (dims 64-127) and loads
+    // V_{u+2}; both issue their K blocks of K_{u+2}
+    auto stage = [&](int u) {
+        const int tw = u + grp;
+        if (tw >= 0 && tw < nkt)
+            write_vt(tw);
+        if (tw + 1 < nkt)
+            load_v(tw + 1);
+        if (u + 2 < nkt)
+            stage_k(u + 2);
+    };
+    // end of a phase: this wave's LDS traffic (and, after an MFMA phase, its loads)
+    // complete, then the workgroup barrier
+    auto barrier = [&](bool loads) {
+        __asm__ volatile("" ::: "memory");
+        if (loads)
+            __builtin_amdgcn_s_waitcnt(kWaitAll);
+        else
+            __builtin_amdgcn_s_waitcnt(kWaitLds);
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+    };
+
+    // ---- prologue: K_0 (and group 0's blocks of K_1) by DMA; V_0 into registers,
+    // both halves
+    if (0 < nkt)
+        stage_k(0);
+    if (grp == 0 && 1 < nkt)
+        stage_k(1);
+    if (0 < nkt)
+        load_v(0);
+    barrier(true);
+
+    // ---- phases: group 0 runs MFMA(j) in phase 2j and softmax(u) in phase 2u - 1,
+    // group 1 softmax(u) in phase 2u and MFMA(j) in phase 2j + 1.  Both groups run
+    // the same code, one MFMA and one softmax phase per iteration; group 1 enters
+    // one phase later (it stages in phase -2, while group 0 computes S_0) and group
+    // 0 closes with one barrier more, so both pass the same barriers.
+    if (grp == 1) {
+        stage(-1);
+        barrier(false);
+    }
+    if (0 < n_w)
+        scores_only(kbuf(0));
+    barrier(true);
+    stage(0);
+    softmax(0);
+    barrier(false);
+    for (int j = 0; j < nkt; ++j) {
+        mfma(j);
+        barrier(true);
+        stage(j + 1);
+        softmax(j + 1);
+        barrier(false);
+    }
+    if (grp == 0)
+        barrier(false);
+
+    if (!wave_active)
+        return;  // no barrier follows
+    // ---- epilogue: O = O~ / lr (rounded to T), L = ln2 (m2 + log2 l)
+    const float lt = l + swap_halves(l);
+    const float lrt = lr + swap_halves(lr);
+    if (my_q >= Nq)
+        return;
+    const float inv = 1.0f / lrt;
+    T* orow = prm.o + ((size_t)bh * Nq + my_q) * D;
+#pragma unroll
+    for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            T4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                w[e] = (T)(o[db][4 * a + e] * inv);
+            *reinterpret_cast<T4*>(orow + 32 * db + 8 * a + 4 * hh) = w;
+        }
+    if (hh == 0)
+        prm.lse[(size_t)bh * Nq + my_q] = (m2 + log2_fast(lt)) * kLn2;
+}
+
+}  // namespace fa
