@@ -50,7 +50,8 @@ def log(msg: str) -> None:
 
 # the sources the forward kernels are built from (the profiles in profiles/ that
 # bench.py reads belong to the forward kernel)
-FWD_SOURCES = ("fa_common.hpp", "fa_tiles.hpp", "fa_fwd_mfma16.hpp", "fa_fwd_f32.hpp")
+FWD_SOURCES = ("fa_common.hpp", "fa_tiles.hpp", "fa_fwd_mfma16.hpp", "fa_fwd_pp.hpp",
+               "fa_fwd_f32.hpp")
 
 
 def kernel_source_hash() -> str:
