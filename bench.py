@@ -211,6 +211,9 @@ def main() -> int:
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (fa_bwd: D, dK/dV and dQ kernels) after one "
                          "forward that supplies O and L; counted flops 2.5x the forward's")
+    ap.add_argument("--dropout", type=float, default=None, metavar="P",
+                    help="time fa_fwd_dropout (with --bwd: fa_bwd_dropout) with drop "
+                         "probability P and a fixed seed instead of fa_fwd / fa_bwd")
     ap.add_argument("--no-clocks", action="store_true",
                     help="skip the sclk readings and the GEMM ceiling run")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -248,11 +251,20 @@ def main() -> int:
     lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     splits = None
+    p_drop = args.dropout
+    seed = 0x5EEDF00D
+    if p_drop is not None and (args.splits is not None or w.dtype == "f32"):
+        print("bench.py --dropout: bf16/fp16 workloads without --splits only", file=sys.stderr)
+        return 2
     if args.bwd:
         if w.dtype == "f32":
             print("bench.py --bwd: the backward pass takes bf16/fp16 inputs", file=sys.stderr)
             return 2
-        fa.fa_fwd(tq, tk, tv, causal=w.causal, scale=w.scale, o=o, lse=lse, stream=stream)
+        if p_drop is None:
+            fa.fa_fwd(tq, tk, tv, causal=w.causal, scale=w.scale, o=o, lse=lse, stream=stream)
+        else:
+            fa.fa_fwd_dropout(tq, tk, tv, p_drop, seed, causal=w.causal, scale=w.scale, o=o,
+                              lse=lse, stream=stream)
         tdo = to_device(inputs.make_do(w), w.dtype, dev)
         dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
         bws = torch.empty(max(16, fa.fa_bwd_workspace(w.B, w.H, w.Nq, w.d)), dtype=torch.uint8,
@@ -260,8 +272,13 @@ def main() -> int:
         log("[bench] timing fa_bwd (gradients of sum(dO o O)); counted flops = 2.5 x forward")
 
         def step():
-            fa.fa_bwd(tq, tk, tv, o, lse, tdo, causal=w.causal, scale=w.scale, dq=dq, dk=dk,
-                      dv=dv, workspace=bws, stream=stream)
+            if p_drop is None:
+                fa.fa_bwd(tq, tk, tv, o, lse, tdo, causal=w.causal, scale=w.scale, dq=dq,
+                          dk=dk, dv=dv, workspace=bws, stream=stream)
+            else:
+                fa.fa_bwd_dropout(tq, tk, tv, o, lse, tdo, p_drop, seed, causal=w.causal,
+                                  scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=bws,
+                                  stream=stream)
     elif args.splits is not None:
         code = {"bf16": fa.FA_DTYPE_BF16, "f16": fa.FA_DTYPE_F16, "f32": fa.FA_DTYPE_F32}[w.dtype]
         splits = args.splits or max(1, fa.fa_split_hint(w.B, w.H, w.Nq, w.Nk, w.d, w.causal, code))
@@ -272,6 +289,12 @@ def main() -> int:
         def step():
             fa.fa_fwd_split(tq, tk, tv, causal=w.causal, scale=w.scale, n_splits=splits, o=o,
                             lse=lse, workspace=ws, stream=stream)
+    elif p_drop is not None:
+        log(f"[bench] timing fa_fwd_dropout, p = {p_drop}")
+
+        def step():
+            fa.fa_fwd_dropout(tq, tk, tv, p_drop, seed, causal=w.causal, scale=w.scale, o=o,
+                              lse=lse, stream=stream)
     else:
         def step():
             fa.fa_fwd(tq, tk, tv, causal=w.causal, scale=w.scale, o=o, lse=lse, stream=stream)
@@ -303,7 +326,8 @@ def main() -> int:
     log(f"[bench] {ms:.4f} ms/step ({t_wall / args.steps * 1e3:.4f} ms wall), {tflops:.1f} TFLOP/s")
 
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = None if (args.bwd or splits is not None) else committed_traffic(w.name)
+    traffic = (None if (args.bwd or splits is not None or p_drop is not None)
+               else committed_traffic(w.name))
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic}
     if not args.no_clocks:
@@ -323,7 +347,7 @@ def main() -> int:
                 f"at {ceil['sclk_mhz']} MHz")
 
     cpu = None
-    if not args.no_cpu_baseline and not args.bwd:
+    if not args.no_cpu_baseline and not args.bwd and p_drop is None:
         log(f"[bench] cpu baseline (~{args.cpu_budget:.0f} s)")
         cpu = cpu_baseline(w, q, k, v, args.cpu_budget)
         log(f"[bench] cpu baseline: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} cores")
@@ -344,8 +368,10 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
                    "causal": w.causal, "scale": "1/sqrt(d)",
-                   "entry": ("fa_bwd" if args.bwd else "fa_fwd" if splits is None
-                             else f"fa_fwd_split(n_splits={splits})"),
+                   "entry": (("fa_bwd" if args.bwd else "fa_fwd" if splits is None
+                              else f"fa_fwd_split(n_splits={splits})")
+                             + ("" if p_drop is None else "_dropout")),
+                   **({} if p_drop is None else {"p_drop": p_drop}),
                    "inputs": f"N(0,{w.sigma_q:g}^2) Q, N(0,{w.sigma_k:g}^2) K, "
                              f"N(0,{w.sigma_v:g}^2) V, seeded"},
         "roofline": roofline,

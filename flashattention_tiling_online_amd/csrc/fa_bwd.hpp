@@ -253,6 +253,9 @@ void fa_bwd_dkv_kernel(const BwdParams<T> prm)
         // P = 2^(s c2 - L2), dS = P (dP - D); register r holds query
         // qw + 8(r/4) + 4hh + r%4.  With dropout Z: dV takes P o Z, dS takes dP o Z.
         vec pp[2], ps[2];
+        uint32_t dw[4];  // group g: queries i TILE + 32qh + 8g + 4hh + 0..3
+        if (DROP)
+            drop_words_k4(prm.drop, bh, i * P::TILE + 32 * qh + 4 * hh, my_k, dw);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int qo = 32 * qh + 8 * g + 4 * hh;
@@ -260,7 +263,7 @@ void fa_bwd_dkv_kernel(const BwdParams<T> prm)
             const f32x4 dd = *reinterpret_cast<const f32x4*>(sm + P::DS + qo * 4);
             uint32_t bytes = 0;
             if (DROP)
-                bytes = drop_bytes_k(prm.drop, bh, i * P::TILE + qo, my_k);
+                bytes = dw[g];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * g + e;
@@ -454,13 +457,16 @@ void fa_bwd_dq_kernel(const BwdParams<T> prm)
         const bool mask = (key0 + P::TILE > Nk) || (CAUSAL && key0 + P::TILE - 1 > qw0);
         const int last = CAUSAL ? min(Nk - 1, my_q) : Nk - 1;
         vec ps[4];
+        uint32_t dw[8];  // group 2cc + g: keys key0 + 16cc + 8g + 4hh + 0..3
+        if (DROP)
+            drop_words_q8(prm.drop, bh, my_q, key0 + 4 * hh, dw);
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
             // chunk cc holds keys 16cc + 4hh + 0..3 (e < 4) and 16cc + 8 + 4hh + 0..3
             uint32_t bytes[2] = {0u, 0u};
             if (DROP) {
-                bytes[0] = drop_bytes_q(prm.drop, bh, my_q, key0 + 16 * cc + 4 * hh);
-                bytes[1] = drop_bytes_q(prm.drop, bh, my_q, key0 + 16 * cc + 8 + 4 * hh);
+                bytes[0] = dw[2 * cc];
+                bytes[1] = dw[2 * cc + 1];
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {

@@ -283,17 +283,16 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
             // keep scale is applied in the epilogue): chunk cc holds keys
             // 16cc + 4hh + 0..3 (e < 4) and 16cc + 8 + 4hh + 0..3 (e >= 4) of the tile
             const DropParams dp{prm.drop_key0, prm.drop_key1, prm.drop_t, prm.drop_keep_scale};
+            uint32_t words[8];  // group 2cc + g: keys kbase + 16cc + 8g + 0..3
+            drop_words_q8(dp, bh, my_q, kbeg + j * P::BC + 4 * hh, words);
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    const int k4 = kbeg + j * P::BC + 16 * cc + 8 * g + 4 * hh;
-                    const uint32_t bytes = drop_bytes_q(dp, bh, my_q, k4);
+                for (int g = 0; g < 2; ++g)
 #pragma unroll
                     for (int m = 0; m < 4; ++m)
-                        if (!drop_keep(bytes, m, dp.t))
+                        if (!drop_keep(words[2 * cc + g], m, dp.t))
                             pb[cc][4 * g + m] = (T)0.f;
-                }
         }
     };
 

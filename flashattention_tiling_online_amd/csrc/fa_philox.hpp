@@ -37,9 +37,11 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
             k0 += W0;
             k1 += W1;
         }
-        const uint32_t hi0 = __umulhi(M0, c[0]), lo0 = M0 * c[0];
-        const uint32_t hi1 = __umulhi(M1, c[2]), lo1 = M1 * c[2];
-        c = u32x4{hi1 ^ c[1] ^ k0, lo1, hi0 ^ c[3] ^ k1, lo0};
+        // both halves of each 32 x 32 -> 64-bit product from one multiply
+        const uint64_t p0 = (uint64_t)M0 * c[0];
+        const uint64_t p1 = (uint64_t)M1 * c[2];
+        c = u32x4{(uint32_t)(p1 >> 32) ^ c[1] ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c[3] ^ k1,
+                  (uint32_t)p0};
     }
     return c;
 }
@@ -62,6 +64,87 @@ __device__ __forceinline__ uint32_t drop_bytes_k(const DropParams& dp, int bh, i
     const int sh = 8 * (k & 3);
     return ((w[0] >> sh) & 0xFFu) | (((w[1] >> sh) & 0xFFu) << 8) |
            (((w[2] >> sh) & 0xFFu) << 16) | (((w[3] >> sh) & 0xFFu) << 24);
+}
+
+// ---- sharing one call between the four lanes of a quad.  A call covers 4 queries x
+// 4 keys; when the four lanes of a quad (lanes 4a .. 4a+3, all active) own four
+// consecutive queries (or keys), each lane computes one call of four and the quad
+// exchanges the words with DPP, instead of every lane computing all four calls.
+
+// value of lane s ^ 1 / s ^ 2 of the quad
+__device__ __forceinline__ uint32_t quad_xor1(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+}
+__device__ __forceinline__ uint32_t quad_xor2(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+}
+
+// 4 x 4 transpose across a quad: lane s holds a[i] = M[s][i] and ends with a[i] = M[i][s]
+// (two butterfly stages; in each, a lane trades the entries whose index bit differs
+// from its own lane bit for its partner's mirrored entries).
+__device__ __forceinline__ void quad_transpose(uint32_t* a, int s)
+{
+    const bool odd = (s & 1) != 0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t r = quad_xor1(odd ? a[2 * k] : a[2 * k + 1]);
+        if (odd)
+            a[2 * k] = r;
+        else
+            a[2 * k + 1] = r;
+    }
+    const bool up = (s & 2) != 0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t r = quad_xor2(up ? a[k] : a[k + 2]);
+        if (up)
+            a[k] = r;
+        else
+            a[k + 2] = r;
+    }
+}
+
+// Lane = query q (queries 4(q/4) + 0..3 on the lanes of the quad): words[G] (G = 0..7)
+// = the bytes of keys kbase + 8G + 0..3 for q, as drop_bytes_q(dp, bh, q, kbase + 8G);
+// kbase a multiple of 4.  Two calls per lane.
+__device__ __forceinline__ void drop_words_q8(const DropParams& dp, int bh, int q, int kbase,
+                                              uint32_t* words)
+{
+    const int s = q & 3;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int g = s + 4 * half;
+        const u32x4 w = philox4x32_10(
+            u32x4{(uint32_t)((kbase + 8 * g) >> 2), (uint32_t)(q >> 2), (uint32_t)bh, 0u}, dp.key0,
+            dp.key1);
+        uint32_t a[4] = {w[0], w[1], w[2], w[3]};
+        quad_transpose(a, s);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            words[4 * half + i] = a[i];
+    }
+}
+
+// Lane = key k (keys 4(k/4) + 0..3 on the lanes of the quad): words[g] (g = 0..3) =
+// the byte of key k for queries qbase + 8g + 0..3 (byte m for query qbase + 8g + m),
+// as drop_bytes_k(dp, bh, qbase + 8g, k); qbase a multiple of 4.  One call per lane.
+__device__ __forceinline__ void drop_words_k4(const DropParams& dp, int bh, int qbase, int k,
+                                              uint32_t* words)
+{
+    const int s = k & 3;
+    const u32x4 w = philox4x32_10(
+        u32x4{(uint32_t)(k >> 2), (uint32_t)((qbase + 8 * s) >> 2), (uint32_t)bh, 0u}, dp.key0,
+        dp.key1);
+    // byte transpose inside the lane: a[b] = byte b (key 4(k/4) + b) of words 0..3
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        words[b] = ((w[0] >> (8 * b)) & 0xFFu) | (((w[1] >> (8 * b)) & 0xFFu) << 8) |
+                   (((w[2] >> (8 * b)) & 0xFFu) << 16) | (((w[3] >> (8 * b)) & 0xFFu) << 24);
+    // words[b] now belongs to (group s, key b); the quad transpose hands lane s' the
+    // words of (group g, key s') for g = 0..3
+    quad_transpose(words, s);
 }
 
 // keep test of byte m of a word of four bytes
