@@ -35,6 +35,8 @@
 // ended.
 #pragma once
 
+#include <type_traits>
+
 #include "fa_tiles.hpp"
 
 namespace fa {
@@ -119,14 +121,14 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
 #pragma unroll
     for (int i = 0; i < P::KPW; ++i)
         ksrc[i] = dma_src<D>(wave + P::NW * i, lane, P::KSTR);
-    auto stage_k = [&](int t) {
-        stage_tile<D, P::KNB, P::KPW, P::NW>(Kh, t, Nk, smem + kbuf(t), wave, ksrc);
+    auto stage_k = [&](int t, int lds_off) {
+        stage_tile<D, P::KNB, P::KPW, P::NW>(Kh, t, Nk, smem + lds_off, wave, ksrc);
     };
     const int v_dq = (tid & 3) + 4 * (tid >> 6);
     const int v_kg = ((tid >> 2) & 3) + 4 * (((tid >> 4) & 1) + 2 * ((tid >> 5) & 1));
     u32x2 vreg[4];
     auto load_v = [&](int t) { load_v_block<D>(Vh, t, Nk, v_kg, v_dq, vreg); };
-    auto write_vt = [&](int t) { store_vt_block<P::VTSTR>(smem + vbuf(t), v_kg, v_dq, vreg); };
+    auto write_vt = [&](int lds_off) { store_vt_block<P::VTSTR>(smem + lds_off, v_kg, v_dq, vreg); };
 
     const int kbase = ql * P::KSTR + hh * 16;
     const int vbase = ql * P::VTSTR + hh * 16;
@@ -272,7 +274,8 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     };
     // MFMA phase of tile j: S^T of tile j+1 (if this wave has it) and P.V of tile j
     // (j = -1: only S^T of tile 0)
-    auto mfma = [&](int j) {
+    // (kb_off: K buffer of tile j+1, vb_off: V^T buffer of tile j)
+    auto mfma = [&](int j, int kb_off, int vb_off) {
         if (rescale) {
 #pragma unroll
             for (int db = 0; db < P::DB; ++db)
@@ -283,7 +286,7 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
         // this wave (stale but allocated LDS) and their result is never used: one
         // code path keeps O~ in the same registers throughout the loop
         if (j < n_w)
-            scores_pv(kbuf(j + 1), vbuf(j));
+            scores_pv(kb_off, vb_off);
     };
     // this group's staging in its softmax phase of tile u: group 0 writes V^T_u (dims
     // 0-63) and loads V_{u+1}, group 1 writes V^T_{u+1} (dims 64-127) and loads
@@ -291,11 +294,22 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     auto stage = [&](int u) {
         const int tw = u + grp;
         if (tw >= 0 && tw < nkt)
-            write_vt(tw);
+            write_vt(vbuf(tw));
         if (tw + 1 < nkt)
             load_v(tw + 1);
         if (u + 2 < nkt)
-            stage_k(u + 2);
+            stage_k(u + 2, kbuf(u + 2));
+    };
+    // the same with the buffers of a known residue r of u (mod 6)
+    auto stage_r = [&](int u, auto R) {
+        constexpr int r = decltype(R)::value;
+        const int tw = u + grp;
+        if (tw < nkt)
+            write_vt(grp == 0 ? P::VOFF + (r & 1) * P::VT : P::VOFF + ((r + 1) & 1) * P::VT);
+        if (tw + 1 < nkt)
+            load_v(tw + 1);
+        if (u + 2 < nkt)
+            stage_k(u + 2, ((r + 2) % P::NKB) * P::KT);
     };
     // end of a phase: this wave's LDS traffic (and, after an MFMA phase, its loads)
     // complete, then the workgroup barrier
@@ -312,9 +326,9 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     // ---- prologue: K_0 (and group 0's blocks of K_1) by DMA; V_0 into registers,
     // both halves
     if (0 < nkt)
-        stage_k(0);
+        stage_k(0, kbuf(0));
     if (grp == 0 && 1 < nkt)
-        stage_k(1);
+        stage_k(1, kbuf(1));
     if (0 < nkt)
         load_v(0);
     barrier(true);
@@ -334,12 +348,28 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     stage(0);
     softmax(0);
     barrier(false);
-    for (int j = 0; j < nkt; ++j) {
-        mfma(j);
+    // unrolled by 6 = lcm(3 K buffers, 2 V^T buffers), so that every buffer offset
+    // is a constant of the code
+    auto iter = [&](int j, auto R) {  // j = R (mod 6)
+        constexpr int r = decltype(R)::value;
+        mfma(j, ((r + 1) % P::NKB) * P::KT, P::VOFF + (r & 1) * P::VT);
         barrier(true);
-        stage(j + 1);
+        stage_r(j + 1, std::integral_constant<int, (r + 1) % 6>{});
         softmax(j + 1);
         barrier(false);
+    };
+    for (int j = 0; j < nkt; j += 6) {
+        iter(j, std::integral_constant<int, 0>{});
+        if (j + 1 < nkt)
+            iter(j + 1, std::integral_constant<int, 1>{});
+        if (j + 2 < nkt)
+            iter(j + 2, std::integral_constant<int, 2>{});
+        if (j + 3 < nkt)
+            iter(j + 3, std::integral_constant<int, 3>{});
+        if (j + 4 < nkt)
+            iter(j + 4, std::integral_constant<int, 4>{});
+        if (j + 5 < nkt)
+            iter(j + 5, std::integral_constant<int, 5>{});
     }
     if (grp == 0)
         barrier(false);

@@ -56,36 +56,45 @@ struct Mfma16<_Float16> {
     }
 };
 
+// Records of a buffer resource are capped at kRsrcCap bytes: every access through
+// one lies within 128 rows of its base (at most 64 KB), and the cap keeps the byte
+// count inside 32 bits for any head.  kDmaSkip is beyond every resource's records.
+constexpr int kRsrcCap = 1 << 30;
+constexpr int kDmaSkip = 0x7FFFFFF0;
+
 // Byte offset, inside a tile of the [rows, D] matrix in memory, that lane `lane` of
 // the 1-KB DMA block `blk` fetches for an LDS tile with row stride `str`: the LDS
-// byte it lands on is blk*1024 + 16*lane.  -1 for lanes that land on row padding
-// (they are masked off and fetch nothing).
+// byte it lands on is blk*1024 + 16*lane.  kDmaSkip for lanes that land on row
+// padding: out of range, they read zero (and write it into the padding, which is
+// never read), so every lane of a block issues the same instruction unmasked.
 template <int D>
 __device__ __forceinline__ int dma_src(int blk, int lane, int str)
 {
     const int pos = blk * 1024 + 16 * lane;
     const int row = pos / str;
     const int ch = (pos - row * str) / 16;
-    return ch < (2 * D) / 16 ? row * (2 * D) + ch * 16 : -1;
+    return ch < (2 * D) / 16 ? row * (2 * D) + ch * 16 : kDmaSkip;
 }
 
 // Word 3 of a gfx9 buffer resource for untyped (raw) loads: 32-bit data format.
 constexpr int kRsrcWord3 = 0x00020000;
 
 // Buffer resource over rows [row0, nrows) of a [nrows, D] matrix: offsets past the
-// end read as zero.
+// end (or past kRsrcCap) read as zero.
 template <int D, typename T>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const T* base, int row0, int nrows)
 {
-    const int n = nrows > row0 ? nrows - row0 : 0;
+    const int64_t n = nrows > row0 ? nrows - row0 : 0;
+    const int64_t bytes = n * D * (int64_t)sizeof(T);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base) + (size_t)row0 * D, 0,
-                                             n * D * (int)sizeof(T), kRsrcWord3);
+                                             bytes < kRsrcCap ? (int)bytes : kRsrcCap,
+                                             kRsrcWord3);
 }
 
 // DMA one K or V tile (rows [tile*BC, tile*BC + BC) of a head) into the LDS tile at
 // `dst`: this wave's blocks wave, wave+NW, ... (< NB); src[i] is the lane's source
-// offset for its i-th block (-1: padding, lane masked off).  A device function (not
-// a lambda) so that the host pass never sees the builtin.
+// offset for its i-th block (kDmaSkip: padding).  A device function (not a lambda)
+// so that the host pass never sees the builtin.
 template <int D, int NB, int PW, int NW, typename T>
 __device__ __forceinline__ void stage_tile(const T* head, int tile, int nrows, char* dst,
                                            int wave, const int* src)
@@ -94,7 +103,7 @@ __device__ __forceinline__ void stage_tile(const T* head, int tile, int nrows, c
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
         const int blk = wave + NW * i;
-        if (blk < NB && src[i] >= 0)
+        if (blk < NB)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + blk * 1024), 16, src[i],
                                                      0, 0, 0);
     }
