@@ -112,8 +112,6 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     if (CAUSAL && wave_active)
         n_w = min(nkt, min(qw0 + 31, Nq - 1) / P::BC + 1);
 
-    auto kbuf = [](int t) { return (t % P::NKB) * P::KT; };
-    auto vbuf = [](int t) { return P::VOFF + (t & 1) * P::VT; };
 
     // ---- staging: K blocks of this wave (DMA), V block of this thread (registers;
     // group 0 threads cover dims 0-63, group 1 threads dims 64-127)
@@ -126,9 +124,11 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     };
     const int v_dq = (tid & 3) + 4 * (tid >> 6);
     const int v_kg = ((tid >> 2) & 3) + 4 * (((tid >> 4) & 1) + 2 * ((tid >> 5) & 1));
-    u32x2 vreg[4];
-    auto load_v = [&](int t) { load_v_block<D>(Vh, t, Nk, v_kg, v_dq, vreg); };
-    auto write_vt = [&](int lds_off) { store_vt_block<P::VTSTR>(smem + lds_off, v_kg, v_dq, vreg); };
+    u32x2 vreg[2][4];  // V_t in vreg[t % 2] from its load to its V^T write
+    auto load_v = [&](int t, int slot) { load_v_block<D>(Vh, t, Nk, v_kg, v_dq, vreg[slot]); };
+    auto write_vt = [&](int lds_off, int slot) {
+        store_vt_block<P::VTSTR>(smem + lds_off, v_kg, v_dq, vreg[slot]);
+    };
 
     const int kbase = ql * P::KSTR + hh * 16;
     const int vbase = ql * P::VTSTR + hh * 16;
@@ -272,46 +272,33 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
             exp_sum_pack();
         }
     };
-    // MFMA phase of tile j: S^T of tile j+1 (if this wave has it) and P.V of tile j
-    // (j = -1: only S^T of tile 0)
-    // (kb_off: K buffer of tile j+1, vb_off: V^T buffer of tile j)
-    auto mfma = [&](int j, int kb_off, int vb_off) {
+    // MFMA phase of tile j (j = R mod 6): this group's half of V^T_{j+1} written from
+    // registers, then S^T of tile j+1 and P.V of tile j (K buffer of tile j+1, V^T
+    // buffer of tile j).  On a wave's last tile the S^T MFMAs read a K buffer that
+    // holds no tile of this wave (stale but allocated LDS) and their result is never
+    // used: one code path keeps O~ in the same registers throughout the loop.
+    auto mfma = [&](int j, auto R) {
+        constexpr int r = decltype(R)::value;
+        if (j + 1 < nkt)
+            write_vt(P::VOFF + ((r + 1) & 1) * P::VT, (r + 1) & 1);
         if (rescale) {
 #pragma unroll
             for (int db = 0; db < P::DB; ++db)
                 o[db] *= alpha;
             rescale = false;
         }
-        // on a wave's last tile the S^T MFMAs read a K buffer that holds no tile of
-        // this wave (stale but allocated LDS) and their result is never used: one
-        // code path keeps O~ in the same registers throughout the loop
         if (j < n_w)
-            scores_pv(kb_off, vb_off);
+            scores_pv(((r + 1) % P::NKB) * P::KT, P::VOFF + (r & 1) * P::VT);
     };
-    // this group's staging in its softmax phase of tile u: group 0 writes V^T_u (dims
-    // 0-63) and loads V_{u+1}, group 1 writes V^T_{u+1} (dims 64-127) and loads
-    // V_{u+2}; both issue their K blocks of K_{u+2}
-    auto stage = [&](int u) {
-        const int tw = u + grp;
-        if (tw >= 0 && tw < nkt)
-            write_vt(vbuf(tw));
-        if (tw + 1 < nkt)
-            load_v(tw + 1);
-        if (u + 2 < nkt)
-            stage_k(u + 2, kbuf(u + 2));
-    };
-    // the same with the buffers of a known residue r of u (mod 6)
-    auto stage_r = [&](int u, auto R) {
+    // staging in the softmax phase of tile u (u = R mod 6): V_{u+2} into registers and
+    // this wave's DMA blocks of K_{u+2}
+    auto stage = [&](int u, auto R) {
         constexpr int r = decltype(R)::value;
-        const int tw = u + grp;
-        if (tw < nkt)
-            write_vt(grp == 0 ? P::VOFF + (r & 1) * P::VT : P::VOFF + ((r + 1) & 1) * P::VT);
-        if (tw + 1 < nkt)
-            load_v(tw + 1);
-        if (u + 2 < nkt)
+        if (u + 2 < nkt) {
+            load_v(u + 2, r & 1);
             stage_k(u + 2, ((r + 2) % P::NKB) * P::KT);
-    };
-    // end of a phase: this wave's LDS traffic (and, after an MFMA phase, its loads)
+        }
+    };    // end of a phase: this wave's LDS traffic (and, after an MFMA phase, its loads)
     // complete, then the workgroup barrier
     auto barrier = [&](bool loads) {
         __asm__ volatile("" ::: "memory");
@@ -323,38 +310,44 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
         __asm__ volatile("" ::: "memory");
     };
 
-    // ---- prologue: K_0 (and group 0's blocks of K_1) by DMA; V_0 into registers,
-    // both halves
-    if (0 < nkt)
-        stage_k(0, kbuf(0));
-    if (grp == 0 && 1 < nkt)
-        stage_k(1, kbuf(1));
-    if (0 < nkt)
-        load_v(0);
+    // ---- prologue: K_0 (and group 0's blocks of K_1) by DMA; V_0 and V_1 into
+    // registers, this group's dims
+    if (0 < nkt) {
+        stage_k(0, 0);
+        load_v(0, 0);
+    }
+    if (1 < nkt) {
+        if (grp == 0)
+            stage_k(1, P::KT);
+        load_v(1, 1);
+    }
     barrier(true);
 
     // ---- phases: group 0 runs MFMA(j) in phase 2j and softmax(u) in phase 2u - 1,
     // group 1 softmax(u) in phase 2u and MFMA(j) in phase 2j + 1.  Both groups run
     // the same code, one MFMA and one softmax phase per iteration; group 1 enters
-    // one phase later (it stages in phase -2, while group 0 computes S_0) and group
-    // 0 closes with one barrier more, so both pass the same barriers.
+    // one phase later (it issues its K_1 blocks in phase -2, while group 0 computes
+    // S_0) and group 0 closes with one barrier more, so both pass the same barriers.
+    // The MFMA phase of tile j writes V^T_{j+1}, the one before tile 0 writes V^T_0.
     if (grp == 1) {
-        stage(-1);
+        if (1 < nkt)
+            stage_k(1, P::KT);
         barrier(false);
     }
+    write_vt(P::VOFF, 0);
     if (0 < n_w)
-        scores_only(kbuf(0));
+        scores_only(0);
     barrier(true);
-    stage(0);
+    stage(0, std::integral_constant<int, 0>{});
     softmax(0);
     barrier(false);
     // unrolled by 6 = lcm(3 K buffers, 2 V^T buffers), so that every buffer offset
-    // is a constant of the code
+    // and register slot is a constant of the code
     auto iter = [&](int j, auto R) {  // j = R (mod 6)
         constexpr int r = decltype(R)::value;
-        mfma(j, ((r + 1) % P::NKB) * P::KT, P::VOFF + (r & 1) * P::VT);
+        mfma(j, R);
         barrier(true);
-        stage_r(j + 1, std::integral_constant<int, (r + 1) % 6>{});
+        stage(j + 1, std::integral_constant<int, (r + 1) % 6>{});
         softmax(j + 1);
         barrier(false);
     };
