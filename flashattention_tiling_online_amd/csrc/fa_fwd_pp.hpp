@@ -272,15 +272,18 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
             exp_sum_pack();
         }
     };
-    // MFMA phase of tile j (j = R mod 6): this group's half of V^T_{j+1} written from
-    // registers, then S^T of tile j+1 and P.V of tile j (K buffer of tile j+1, V^T
-    // buffer of tile j).  On a wave's last tile the S^T MFMAs read a K buffer that
-    // holds no tile of this wave (stale but allocated LDS) and their result is never
-    // used: one code path keeps O~ in the same registers throughout the loop.
+    // MFMA phase of tile j (j = R mod 6): S^T of tile j+1 and P.V of tile j (K buffer
+    // of tile j+1, V^T buffer of tile j), then this group's half of V^T_{j+1} written
+    // from registers.  The write goes last: its transposing VALU work runs under the
+    // last MFMAs and its LDS stores queue behind the operand reads (placed first, or
+    // among the MFMAs, it delays the first operand reads).  On a wave's last tile the
+    // S^T MFMAs read a K buffer that holds no tile of this wave (stale but allocated
+    // LDS) and their result is never used: one code path keeps O~ in the same
+    // registers throughout the loop.  The phase runs at raised wave priority, so the
+    // SIMD's arbiter issues this wave's MFMAs ahead of the other group's VALU work.
     auto mfma = [&](int j, auto R) {
         constexpr int r = decltype(R)::value;
-        if (j + 1 < nkt)
-            write_vt(P::VOFF + ((r + 1) & 1) * P::VT, (r + 1) & 1);
+        __builtin_amdgcn_s_setprio(3);
         if (rescale) {
 #pragma unroll
             for (int db = 0; db < P::DB; ++db)
@@ -289,11 +292,14 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
         }
         if (j < n_w)
             scores_pv(((r + 1) % P::NKB) * P::KT, P::VOFF + (r & 1) * P::VT);
+        if (j + 1 < nkt)
+            write_vt(P::VOFF + ((r + 1) & 1) * P::VT, (r + 1) & 1);
     };
     // staging in the softmax phase of tile u (u = R mod 6): V_{u+2} into registers and
-    // this wave's DMA blocks of K_{u+2}
+    // this wave's DMA blocks of K_{u+2}; the phase runs at normal priority
     auto stage = [&](int u, auto R) {
         constexpr int r = decltype(R)::value;
+        __builtin_amdgcn_s_setprio(0);
         if (u + 2 < nkt) {
             load_v(u + 2, r & 1);
             stage_k(u + 2, ((r + 2) % P::NKB) * P::KT);
