@@ -41,21 +41,21 @@ Launch f32()
                   fa::TileF32<D>::BR, fa::TileF32<D>::NT};
 }
 
-template <typename T, bool C>
+template <typename T, bool C, bool S>
 Launch pp()
 {
-    return Launch{reinterpret_cast<const void*>(&fa::fa_fwd_pp_kernel<T, C>), fa::TilePP::BR,
+    return Launch{reinterpret_cast<const void*>(&fa::fa_fwd_pp_kernel<T, C, S>), fa::TilePP::BR,
                   fa::TilePP::NT};
 }
 
-// d = 128 without key splits: the phase-alternating kernel; otherwise fa_fwd_mfma16
+// d = 128: the phase-alternating kernel (with or without key splits); d = 64:
+// fa_fwd_mfma16
 template <typename T, bool S>
 Launch mfma16_of(int64_t d, bool c)
 {
-    if (d == 128 && !S)
-        return c ? pp<T, true>() : pp<T, false>();
-    return d == 128 ? (c ? mfma16<T, 128, true, S>() : mfma16<T, 128, false, S>())
-                    : (c ? mfma16<T, 64, true, S>() : mfma16<T, 64, false, S>());
+    if (d == 128)
+        return c ? pp<T, true, S>() : pp<T, false, S>();
+    return c ? mfma16<T, 64, true, S>() : mfma16<T, 64, false, S>();
 }
 
 template <bool S>

@@ -66,7 +66,7 @@ struct TilePP {
 constexpr int kWaitLds = 0xC07F;  // lgkmcnt(0)
 constexpr int kWaitAll = 0x0070;  // vmcnt(0) lgkmcnt(0)
 
-template <typename T, bool CAUSAL>
+template <typename T, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(TilePP::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_fwd_pp_kernel(const FwdParams<T> prm)
 {
@@ -80,10 +80,13 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     const int Nq = prm.Nq, Nk = prm.Nk, n_qtiles = prm.n_qtiles;
     const float c2 = prm.c2;
 
-    // ---- (batch*head, query tile) of this workgroup, XCD-aware, causal longest first
+    // ---- (batch*head, key split, query tile) of this workgroup, XCD-aware, causal
+    // longest first; the query tiles of one (head, split) are consecutive
     const int logical = xcd_remap((int)blockIdx.x, (int)gridDim.x);
-    const int bh = logical / n_qtiles;
-    int qt = logical - bh * n_qtiles;
+    const int rest = logical / n_qtiles;
+    int qt = logical - rest * n_qtiles;
+    const int split = SPLIT ? rest % prm.n_splits : 0;
+    const int bh = SPLIT ? rest / prm.n_splits : rest;
     if (CAUSAL)
         qt = n_qtiles - 1 - qt;
     const int q0 = qt * P::BR;
@@ -97,20 +100,28 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     const int qw0 = q0 + 32 * (2 * (wave & 3) + grp);
     const int my_q = qw0 + ql;
 
+    // ---- key range: keys [kbeg, kbeg + Nks) of the head (all of them unless split);
+    // key tiles and positions below are relative to kbeg, so a query's causal limit is
+    // its index minus kbeg.  kbeg is a multiple of 64, so a wave's 32 rows either all
+    // see key kbeg or see no key of the range.
+    const int kbeg = SPLIT ? split * prm.split_tiles * P::BC : 0;
+    const int Nks = SPLIT ? min(Nk - kbeg, prm.split_tiles * P::BC) : Nk;
     const T* Qh = prm.q + (size_t)bh * Nq * D;
-    const T* Kh = prm.k + (size_t)bh * Nk * D;
-    const T* Vh = prm.v + (size_t)bh * Nk * D;
+    const T* Kh = prm.k + ((size_t)bh * Nk + kbeg) * D;
+    const T* Vh = prm.v + ((size_t)bh * Nk + kbeg) * D;
 
     // ---- key tiles: the workgroup stages nkt, this wave computes n_w
-    int nkt = (Nk + P::BC - 1) / P::BC;
+    int nkt = (Nks + P::BC - 1) / P::BC;
     if (CAUSAL) {
-        const int last = min(q0 + P::BR, Nq) - 1;
-        nkt = min(nkt, last / P::BC + 1);
+        const int last = min(q0 + P::BR, Nq) - 1 - kbeg;
+        nkt = last < 0 ? 0 : min(nkt, last / P::BC + 1);
     }
     const bool wave_active = qw0 < Nq;
     int n_w = wave_active ? nkt : 0;
-    if (CAUSAL && wave_active)
-        n_w = min(nkt, min(qw0 + 31, Nq - 1) / P::BC + 1);
+    if (CAUSAL && wave_active) {
+        const int last = min(qw0 + 31, Nq - 1) - kbeg;
+        n_w = last < 0 ? 0 : min(nkt, last / P::BC + 1);
+    }
 
 
     // ---- staging: K blocks of this wave (DMA), V block of this thread (registers;
@@ -120,12 +131,12 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     for (int i = 0; i < P::KPW; ++i)
         ksrc[i] = dma_src<D>(wave + P::NW * i, lane, P::KSTR);
     auto stage_k = [&](int t, int lds_off) {
-        stage_tile<D, P::KNB, P::KPW, P::NW>(Kh, t, Nk, smem + lds_off, wave, ksrc);
+        stage_tile<D, P::KNB, P::KPW, P::NW>(Kh, t, Nks, smem + lds_off, wave, ksrc);
     };
     const int v_dq = (tid & 3) + 4 * (tid >> 6);
     const int v_kg = ((tid >> 2) & 3) + 4 * (((tid >> 4) & 1) + 2 * ((tid >> 5) & 1));
     u32x2 vreg[2][4];  // V_t in vreg[t % 2] from its load to its V^T write
-    auto load_v = [&](int t, int slot) { load_v_block<D>(Vh, t, Nk, v_kg, v_dq, vreg[slot]); };
+    auto load_v = [&](int t, int slot) { load_v_block<D>(Vh, t, Nks, v_kg, v_dq, vreg[slot]); };
     auto write_vt = [&](int lds_off, int slot) {
         store_vt_block<P::VTSTR>(smem + lds_off, v_kg, v_dq, vreg[slot]);
     };
@@ -196,11 +207,11 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     // tile can need it (its first query is a multiple of 32, tiles are 64 keys).
     auto needs_mask = [&](int j) {
         const int key0 = j * P::BC;
-        return (key0 + P::BC > Nk) || (CAUSAL && key0 + P::BC - 1 > qw0);
+        return (key0 + P::BC > Nks) || (CAUSAL && key0 + P::BC - 1 > qw0 - kbeg);
     };
     auto mask_tile = [&](int j) {
         const int key0 = j * P::BC;
-        const int last = CAUSAL ? min(Nk - 1, my_q) : Nk - 1;
+        const int last = CAUSAL ? min(Nks - 1, my_q - kbeg) : Nks - 1;
         const int lim = last - key0 - 4 * hh;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -375,11 +386,31 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
 
     if (!wave_active)
         return;  // no barrier follows
-    // ---- epilogue: O = O~ / lr (rounded to T), L = ln2 (m2 + log2 l)
+    // ---- epilogue: O = O~ / lr (rounded to T), L = ln2 (m2 + log2 l); split: O~ / lr
+    // and L in fp32 into the partial buffers, and for a row that saw no key of its
+    // range the identity of the merge, L = -inf with O = 0
     const float lt = l + swap_halves(l);
     const float lrt = lr + swap_halves(lr);
     if (my_q >= Nq)
         return;
+    if (SPLIT) {
+        const size_t row = ((size_t)split * prm.bh_count + bh) * Nq + my_q;
+        const float inv = lrt > 0.f ? 1.0f / lrt : 0.f;
+        float* orow = prm.o_part + row * D;
+#pragma unroll
+        for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                f32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = o[db][4 * a + e] * inv;
+                *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * a + 4 * hh) = w;
+            }
+        if (hh == 0)
+            prm.lse_part[row] = lt > 0.f ? (m2 + log2_fast(lt)) * kLn2 : neg_inf();
+        return;
+    }
     const float inv = 1.0f / lrt;
     T* orow = prm.o + ((size_t)bh * Nq + my_q) * D;
 #pragma unroll
