@@ -51,7 +51,7 @@ Launch pp()
 // d = 128: the phase-alternating kernel (with or without key splits); d = 64:
 // fa_fwd_mfma16
 template <typename T, bool S>
-Launch mfma16_of(int64_t d, bool c)
+Launch fwd16_of(int64_t d, bool c)
 {
     if (d == 128)
         return c ? pp<T, true, S>() : pp<T, false, S>();
@@ -72,10 +72,10 @@ bool pick(fa_dtype_t dtype, int64_t d, int causal, bool split, Launch* out)
         return false;
     switch (dtype) {
     case FA_DTYPE_BF16:
-        *out = split ? mfma16_of<__bf16, true>(d, c) : mfma16_of<__bf16, false>(d, c);
+        *out = split ? fwd16_of<__bf16, true>(d, c) : fwd16_of<__bf16, false>(d, c);
         return true;
     case FA_DTYPE_F16:
-        *out = split ? mfma16_of<_Float16, true>(d, c) : mfma16_of<_Float16, false>(d, c);
+        *out = split ? fwd16_of<_Float16, true>(d, c) : fwd16_of<_Float16, false>(d, c);
         return true;
     case FA_DTYPE_F32:
         *out = split ? f32_of<true>(d, c) : f32_of<false>(d, c);

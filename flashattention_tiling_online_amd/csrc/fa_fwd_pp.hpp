@@ -11,10 +11,12 @@
 // A workgroup is 8 waves (256 query rows) and fills a CU; waves w and w + 4 share a
 // SIMD.  Waves 0-3 form group 0, waves 4-7 group 1, and the two groups run in
 // opposite phases separated by workgroup barriers:
-//   * an MFMA phase of tile j: S_{j+1} = K_{j+1} Q^T (16 MFMAs) and O~ += V_j^T P_j^T
-//     (16 MFMAs), operands read from LDS, nothing else;
+//   * an MFMA phase of tile j, at raised wave priority: S_{j+1} = K_{j+1} Q^T (16
+//     MFMAs) and O~ += V_j^T P_j^T (16 MFMAs), operands read from LDS, then this
+//     group's half of V^T_{j+1} written to LDS from registers;
 //   * a softmax phase of tile u: mask, running max, P_u = 2^(S_u c - m) rounded to
-//     T, the two row sums, plus this group's share of the K/V staging.
+//     T, the two row sums, plus this group's share of the staging: V_{u+2} into
+//     registers (its half of the dims) and its DMA blocks of K_{u+2}.
 // While one wave of a SIMD issues its 32 MFMAs back to back, the other wave's
 // softmax instructions take the issue slots the matrix core leaves free, instead of
 // both waves contending for the same slots in the same phase:
@@ -25,14 +27,18 @@
 // causal tile counts within one of each other.
 //
 // Staging (K by DMA into rows padded by 16 B, V transposed through registers into
-// V^T rows, exactly as fa_fwd_mfma16.hpp lays them out): three K buffers and two V^T
-// buffers.  Group 0 writes dims 0-63 of V^T_u and issues its K blocks of K_{u+2} in
-// its softmax phase of tile u (phase 2u-1); group 1 writes dims 64-127 of V^T_{u+1}
-// and issues its K blocks of K_{u+2} in its softmax phase of tile u (phase 2u).  A
-// group waits for its loads at the end of its following MFMA phase; the first
-// reader of K_t (group 0, phase 2t-2) and of V^T_t (group 0, phase 2t) comes after
-// both groups' waits, and no buffer is rewritten before its last reader's phase has
-// ended.
+// V^T rows, exactly as fa_fwd_mfma16.hpp lays them out): three K buffers, two V^T
+// buffers and two V register slots.  K_t and V_t are issued in the softmax phase of
+// tile t-2 (group 0: phase 2t-5, group 1: phase 2t-4), and a group waits for its
+// loads at the end of its following MFMA phase (phases 2t-4 and 2t-3).  V^T_t is
+// written at the end of the MFMA phases of tile t-1 (group 0 dims 0-63 in phase
+// 2t-2, group 1 dims 64-127 in phase 2t-1).  The first reader of K_t (group 0,
+// phase 2t-2) and of V^T_t (group 0, phase 2t) comes after both groups' waits and
+// writes, and no buffer or register slot is rewritten before its last reader's
+// phase has ended.
+//
+// With key splits a workgroup stages one range of whole key tiles and writes fp32
+// partial states, as fa_fwd_mfma16.hpp does.
 #pragma once
 
 #include <type_traits>
