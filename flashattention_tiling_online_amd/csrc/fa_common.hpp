@@ -21,6 +21,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.693147180559945309417f;
+// key tiles per block of the forward kernels' row sums (a power of two)
+constexpr int kSumBlock = 64;
 
 // Number of XCDs (accelerator complex dies) on gfx950.  Consecutive workgroup ids
 // are dispatched round-robin over them, and each has its own L2.

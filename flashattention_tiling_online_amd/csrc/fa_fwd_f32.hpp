@@ -88,7 +88,8 @@ void fa_fwd_f32_kernel(const FwdParams<float> prm)
     for (int db = 0; db < P::DB; ++db)
         o[db] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     float m2 = neg_inf();
-    float l = 0.f;
+    float l = 0.f;       // this half's row sum, current block of kSumBlock tiles
+    float l_done = 0.f;  // completed blocks (bounds the drift of the fp32 sum)
 
     for (int j = 0; j < nkt; ++j) {
         const int key0 = j * P::BC;
@@ -157,6 +158,11 @@ void fa_fwd_f32_kernel(const FwdParams<float> prm)
                 rs += p;
             }
         l = l * alpha + rs;
+        l_done *= alpha;
+        if ((j & (kSumBlock - 1)) == kSumBlock - 1) {
+            l_done += l;
+            l = 0.f;
+        }
         m2 = m_new;
 #pragma unroll
         for (int db = 0; db < P::DB; ++db)
@@ -178,7 +184,8 @@ void fa_fwd_f32_kernel(const FwdParams<float> prm)
         return;
     // split: a row that saw no key of its range leaves the merge identity
     // (L = -inf, O = 0)
-    const float lt = l + swap_halves(l);
+    const float lsum = l_done + l;
+    const float lt = lsum + swap_halves(lsum);
     if (my_q < Nq) {
         const size_t row = SPLIT ? ((size_t)split * prm.bh_count + bh) * Nq + my_q
                                  : (size_t)bh * Nq + my_q;

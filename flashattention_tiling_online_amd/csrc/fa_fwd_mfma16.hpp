@@ -68,7 +68,8 @@ struct Tile16 {
     static_assert(NT == 4 * D, "V staging: one 4-key x 4-dim block per thread");
     static constexpr int DC = D / 16;            // 16-wide d chunks of the S contraction
     static constexpr int DB = D / 32;            // 32-wide d blocks of O
-    static constexpr int LDS = 2 * KT + 2 * VT;  // K[2] and V^T[2]
+    static constexpr int SUMS = 2 * KT + 2 * VT;  // per thread: completed row-sum blocks
+    static constexpr int LDS = SUMS + 8 * NT;      // K[2], V^T[2], sums
     static constexpr int K0 = 0, K1 = KT, V0 = 2 * KT, V1 = 2 * KT + VT;
     static_assert(KT % 1024 == 0, "K tiles must be whole DMA blocks");
 };
@@ -195,8 +196,17 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
     for (int db = 0; db < P::DB; ++db)
         o[db] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     float m2 = neg_inf();
-    float l = 0.f;   // this half's sum of the fp32 P (for L)
-    float lr = 0.f;  // this half's sum of the rounded P (for the normalisation of O)
+    float l = 0.f;   // this half's sum of the fp32 P (for L), current block of tiles
+    float lr = 0.f;  // this half's sum of the rounded P (for the normalisation of O), same
+    // The row sums run per block of kSumBlock key tiles and are folded into this
+    // thread's LDS slot (l, lr of the completed blocks) when a block ends: a sequential
+    // fp32 sum over T tiles can drift by up to about T 2^-24 of its value (when the
+    // tile sums are alike), blocks bound the drift by about (kSumBlock + T / kSumBlock)
+    // 2^-24.  The slot is in LDS because the dropout instantiations have no register
+    // to spare; it is touched once per block and on the rare rescale only.
+    float* const done = reinterpret_cast<float*>(smem + P::SUMS) + 2 * tid;
+    done[0] = 0.f;
+    done[1] = 0.f;
 
     // Mask tile j: keys key0 + 4hh + off (off = 32kb + 8(r/4) + r%4) past the end of
     // the keys or (causal) after the query become -inf.  Only a wave's last tile can
@@ -249,6 +259,8 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
                 o[db] *= alpha;
             l *= alpha;
             lr *= alpha;
+            done[0] *= alpha;
+            done[1] *= alpha;
             m2 = m_new;
         }
     };
@@ -278,6 +290,12 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
                 rr[e & 1] = M::dot_ones(w[e], rr[e & 1]);
         }
         lr += rr[0] + rr[1];
+        if ((j & (kSumBlock - 1)) == kSumBlock - 1) {
+            done[0] += l;
+            done[1] += lr;
+            l = 0.f;
+            lr = 0.f;
+        }
         if (DROP) {
             // dropout on the P that multiplies V (l and lr keep the undropped P, the
             // keep scale is applied in the epilogue): chunk cc holds keys
@@ -365,8 +383,9 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
     // ---- epilogue: O = O~ / l (rounded to T, nearest-even), L = ln2 * (m2 + log2 l);
     // split: O~ / l and L in fp32 into the partial buffers, and for a row that saw
     // no key of its range the identity of the merge, L = -inf with O = 0
-    const float lt = l + swap_halves(l);
-    const float lrt = lr + swap_halves(lr);
+    const float lsum = done[0] + l, lrsum = done[1] + lr;
+    const float lt = lsum + swap_halves(lsum);
+    const float lrt = lrsum + swap_halves(lrsum);
     if (my_q < Nq) {
         if (SPLIT) {
             const size_t row = ((size_t)split * prm.bh_count + bh) * Nq + my_q;

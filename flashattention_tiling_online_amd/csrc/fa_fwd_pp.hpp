@@ -168,8 +168,13 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     f32x16 s[2];  // S^T of the tile whose softmax is next
     vec pb[4];    // P of the tile whose P.V is next, rounded, B-operand order
     float m2 = neg_inf();
-    float l = 0.f;   // this half's sum of the fp32 P (for L)
-    float lr = 0.f;  // this half's sum of the rounded P (for the normalisation of O)
+    float l = 0.f;   // this half's sum of the fp32 P (for L), current block of tiles
+    float lr = 0.f;  // this half's sum of the rounded P (for the normalisation of O), same
+    // The row sums run per block of kSumBlock key tiles and are folded into l_done /
+    // lr_done when a block ends: a sequential fp32 sum over T tiles can drift by up to
+    // about T 2^-24 of its value (when the tile sums are alike), blocks bound the drift
+    // by about (kSumBlock + T / kSumBlock) 2^-24.
+    float l_done = 0.f, lr_done = 0.f;
 
     // S^T of one tile from the K buffer at kb_off
     auto scores_only = [&](int kb_off) {
@@ -252,6 +257,8 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
             rescale = true;
             l *= alpha;
             lr *= alpha;
+            l_done *= alpha;
+            lr_done *= alpha;
             m2 = m_new;
         }
     };
@@ -287,6 +294,12 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
                 mask_tile(u);
             update_max();
             exp_sum_pack();
+            if ((u & (kSumBlock - 1)) == kSumBlock - 1) {
+                l_done += l;
+                lr_done += lr;
+                l = 0.f;
+                lr = 0.f;
+            }
         }
     };
     // MFMA phase of tile j (j = R mod 6): S^T of tile j+1 and P.V of tile j (K buffer
@@ -395,8 +408,9 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     // ---- epilogue: O = O~ / lr (rounded to T), L = ln2 (m2 + log2 l); split: O~ / lr
     // and L in fp32 into the partial buffers, and for a row that saw no key of its
     // range the identity of the merge, L = -inf with O = 0
-    const float lt = l + swap_halves(l);
-    const float lrt = lr + swap_halves(lr);
+    const float lsum = l_done + l, lrsum = lr_done + lr;
+    const float lt = lsum + swap_halves(lsum);
+    const float lrt = lrsum + swap_halves(lrsum);
     if (my_q >= Nq)
         return;
     if (SPLIT) {
