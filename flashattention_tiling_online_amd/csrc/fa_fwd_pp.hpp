@@ -129,7 +129,6 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
         n_w = last < 0 ? 0 : min(nkt, last / P::BC + 1);
     }
 
-
     // ---- staging: K blocks of this wave (DMA), V block of this thread (registers;
     // group 0 threads cover dims 0-63, group 1 threads dims 64-127)
     int ksrc[P::KPW];
@@ -168,12 +167,13 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     f32x16 s[2];  // S^T of the tile whose softmax is next
     vec pb[4];    // P of the tile whose P.V is next, rounded, B-operand order
     float m2 = neg_inf();
-    float l = 0.f;   // this half's sum of the fp32 P (for L), current block of tiles
-    float lr = 0.f;  // this half's sum of the rounded P (for the normalisation of O), same
-    // The row sums run per block of kSumBlock key tiles and are folded into l_done /
-    // lr_done when a block ends: a sequential fp32 sum over T tiles can drift by up to
-    // about T 2^-24 of its value (when the tile sums are alike), blocks bound the drift
-    // by about (kSumBlock + T / kSumBlock) 2^-24.
+    // Row sums of this half: ls0, ls1 of the fp32 P (for L) and lrs0, lrs1 of the rounded P
+    // (for the normalisation of O), independent chains that run across the tiles of
+    // a block of kSumBlock key tiles and are folded into l_done / lr_done when the
+    // block ends.  A sequential fp32 sum over T tiles can drift by up to about
+    // T 2^-24 of its value (when the tile sums are alike); blocks bound the drift by
+    // about (kSumBlock + T / kSumBlock) 2^-24.
+    float ls0 = 0.f, ls1 = 0.f, lrs0 = 0.f, lrs1 = 0.f;
     float l_done = 0.f, lr_done = 0.f;
 
     // S^T of one tile from the K buffer at kb_off
@@ -235,14 +235,18 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     };
 
     // Lazy running max (as in fa_fwd_mfma16.hpp): the reference m2 moves, with the
-    // rescale of O~, l and lr by 2^(m2 - m_new), only when some row exceeds it by
-    // more than kSlack; O is divided by the sum of the same rounded P that entered
+    // rescale of O~ and the row sums by 2^(m2 - m_new), only when some row exceeds it
+    // by more than kSlack; O is divided by the sum of the same rounded P that entered
     // the P.V MFMAs, L uses the fp32 sum.  The rescale of O~ is applied by the next
     // MFMA phase (O~ is touched by MFMA phases only): `rescale` marks it pending,
-    // alpha holds the factor.
+    // alpha holds the factor.  What the per-tile work needs of m2 is kept ready:
+    // mneg = -m2 (0 while m2 = -inf, so that a row with no visible key gets p = 0) and
+    // the raw-score threshold thr = (m2 + kSlack) / c2 of the move test (c2 > 0).
     constexpr float kSlack = 8.0f;
+    const float inv_c2 = 1.0f / c2;
     bool rescale = false;
     float alpha = 1.f;
+    float mneg = 0.f, thr = neg_inf();
     auto update_max = [&]() {
         float mx = s[0][0];
 #pragma unroll
@@ -250,35 +254,38 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 mx = fmaxf(mx, s[kb][r]);
-        const float mh = mx * c2;  // c2 > 0: max commutes with the scale
-        if (__builtin_amdgcn_ballot_w64(mh > m2 + kSlack) != 0) {
+        if (__builtin_amdgcn_ballot_w64(mx > thr) != 0) {
+            const float mh = mx * c2;  // c2 > 0: max commutes with the scale
             const float m_new = fmaxf(m2, fmaxf(mh, swap_halves(mh)));
             alpha = exp2_fast(m2 - m_new);  // 0 on a wave's first tile (m2 = -inf)
             rescale = true;
-            l *= alpha;
-            lr *= alpha;
+            ls0 *= alpha;
+            ls1 *= alpha;
+            lrs0 *= alpha;
+            lrs1 *= alpha;
             l_done *= alpha;
             lr_done *= alpha;
             m2 = m_new;
+            mneg = (m_new == neg_inf()) ? 0.f : -m_new;
+            thr = (m_new + kSlack) * inv_c2;
         }
     };
-    // P = 2^(s c2 - m2) in fp32, summed into l; rounded to T in the MFMA B-operand
+    // P = 2^(s c2 - m2) in fp32, summed into ls; rounded to T in the MFMA B-operand
     // order (chunk cc = 2kb + h holds registers 8h .. 8h+7 of block kb); the rounded
-    // values summed into lr with v_dot2.  A row with no visible key so far
-    // (m2 = -inf) gets p = 0.
+    // values summed into lrs with v_dot2.
     auto exp_sum_pack = [&]() {
-        const float mneg = (m2 == neg_inf()) ? 0.f : -m2;
-        float rs[4] = {0.f, 0.f, 0.f, 0.f};
+        float rs[2] = {ls0, ls1};
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float p = exp2_fast(fmaf(s[cc >> 1][8 * (cc & 1) + e], c2, mneg));
-                rs[e & 3] += p;
+                rs[e & 1] += p;
                 pb[cc][e] = (T)p;
             }
-        l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-        float rr[2] = {0.f, 0.f};
+        ls0 = rs[0];
+        ls1 = rs[1];
+        float rr[2] = {lrs0, lrs1};
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
             const u32x4 w = __builtin_bit_cast(u32x4, pb[cc]);
@@ -286,7 +293,8 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
             for (int e = 0; e < 4; ++e)
                 rr[e & 1] = M::dot_ones(w[e], rr[e & 1]);
         }
-        lr += rr[0] + rr[1];
+        lrs0 = rr[0];
+        lrs1 = rr[1];
     };
     auto softmax = [&](int u) {
         if (u < n_w) {
@@ -295,10 +303,10 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
             update_max();
             exp_sum_pack();
             if ((u & (kSumBlock - 1)) == kSumBlock - 1) {
-                l_done += l;
-                lr_done += lr;
-                l = 0.f;
-                lr = 0.f;
+                l_done += ls0 + ls1;
+                lr_done += lrs0 + lrs1;
+                ls0 = ls1 = 0.f;
+                lrs0 = lrs1 = 0.f;
             }
         }
     };
@@ -408,7 +416,8 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     // ---- epilogue: O = O~ / lr (rounded to T), L = ln2 (m2 + log2 l); split: O~ / lr
     // and L in fp32 into the partial buffers, and for a row that saw no key of its
     // range the identity of the merge, L = -inf with O = 0
-    const float lsum = l_done + l, lrsum = lr_done + lr;
+    const float lsum = l_done + (ls0 + ls1);
+    const float lrsum = lr_done + (lrs0 + lrs1);
     const float lt = lsum + swap_halves(lsum);
     const float lrt = lrsum + swap_halves(lrsum);
     if (my_q >= Nq)
