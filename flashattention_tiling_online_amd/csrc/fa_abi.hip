@@ -84,16 +84,17 @@ bool pick(fa_dtype_t dtype, int64_t d, int causal, bool split, Launch* out)
     return false;
 }
 
-// the forward kernel with dropout on P (16-bit inputs, unsplit)
+// the forward kernel with dropout on P (16-bit inputs, unsplit): d = 128 on the
+// phase-alternating kernel, d = 64 on fa_fwd_mfma16
 template <typename T>
-Launch mfma16_drop(int64_t d, bool c)
+Launch fwd16_drop(int64_t d, bool c)
 {
     auto one = [](const void* fn, int rows, int threads) { return Launch{fn, rows, threads}; };
     if (d == 128)
-        return c ? one(reinterpret_cast<const void*>(&fa::fa_fwd_mfma16_kernel<T, 128, true, false, true>),
-                       fa::Tile16<128>::BR, fa::Tile16<128>::NT)
-                 : one(reinterpret_cast<const void*>(&fa::fa_fwd_mfma16_kernel<T, 128, false, false, true>),
-                       fa::Tile16<128>::BR, fa::Tile16<128>::NT);
+        return c ? one(reinterpret_cast<const void*>(&fa::fa_fwd_pp_kernel<T, true, false, true>),
+                       fa::TilePP::BR, fa::TilePP::NT)
+                 : one(reinterpret_cast<const void*>(&fa::fa_fwd_pp_kernel<T, false, false, true>),
+                       fa::TilePP::BR, fa::TilePP::NT);
     return c ? one(reinterpret_cast<const void*>(&fa::fa_fwd_mfma16_kernel<T, 64, true, false, true>),
                    fa::Tile16<64>::BR, fa::Tile16<64>::NT)
              : one(reinterpret_cast<const void*>(&fa::fa_fwd_mfma16_kernel<T, 64, false, false, true>),
@@ -295,8 +296,8 @@ extern "C" fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* 
         return FA_OK;
     const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     if (t > 0)
-        L = dtype == FA_DTYPE_BF16 ? mfma16_drop<__bf16>(d, causal != 0)
-                                   : mfma16_drop<_Float16>(d, causal != 0);
+        L = dtype == FA_DTYPE_BF16 ? fwd16_drop<__bf16>(d, causal != 0)
+                                   : fwd16_drop<_Float16>(d, causal != 0);
     const Dropout drop{(uint32_t)t, seed};
     const hipError_t err = launch_fwd_any(dtype, L, q, k, v, o, lse, nullptr, nullptr, B * H, Nq,
                                           Nk, 1, 0, scale, hs, t > 0 ? &drop : nullptr);

@@ -43,6 +43,7 @@
 
 #include <type_traits>
 
+#include "fa_philox.hpp"
 #include "fa_tiles.hpp"
 
 namespace fa {
@@ -72,7 +73,7 @@ struct TilePP {
 constexpr int kWaitLds = 0xC07F;  // lgkmcnt(0)
 constexpr int kWaitAll = 0x0070;  // vmcnt(0) lgkmcnt(0)
 
-template <typename T, bool CAUSAL, bool SPLIT>
+template <typename T, bool CAUSAL, bool SPLIT, bool DROP = false>
 __global__ __launch_bounds__(TilePP::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_fwd_pp_kernel(const FwdParams<T> prm)
 {
@@ -296,12 +297,30 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
         lrs0 = rr[0];
         lrs1 = rr[1];
     };
-    auto softmax = [&](int u) {
+    // softmax phase of tile u; forced inline, since with dropout the compiler would
+    // otherwise emit it as a function and keep the captured state in scratch memory
+    auto softmax = [&](int u) __attribute__((always_inline)) {
         if (u < n_w) {
             if (needs_mask(u))
                 mask_tile(u);
             update_max();
             exp_sum_pack();
+            if (DROP) {
+                // dropout on the P that multiplies V (the row sums keep the undropped P,
+                // the keep scale is applied in the epilogue): chunk cc holds keys
+                // 16cc + 4hh + 0..3 (e < 4) and 16cc + 8 + 4hh + 0..3 (e >= 4) of the tile
+                const DropParams dp{prm.drop_key0, prm.drop_key1, prm.drop_t, prm.drop_keep_scale};
+                uint32_t words[8];  // group 2cc + g: keys 16cc + 8g + 4hh + 0..3 of the tile
+                drop_words_q8(dp, bh, my_q, kbeg + u * P::BC + 4 * hh, words);
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+                    for (int g = 0; g < 2; ++g)
+#pragma unroll
+                        for (int m = 0; m < 4; ++m)
+                            if (!drop_keep(words[2 * cc + g], m, dp.t))
+                                pb[cc][4 * g + m] = (T)0.f;
+            }
             if ((u & (kSumBlock - 1)) == kSumBlock - 1) {
                 l_done += ls0 + ls1;
                 lr_done += lrs0 + lrs1;
@@ -440,7 +459,7 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
             prm.lse_part[row] = lt > 0.f ? (m2 + log2_fast(lt)) * kLn2 : neg_inf();
         return;
     }
-    const float inv = 1.0f / lrt;
+    const float inv = (DROP ? prm.drop_keep_scale : 1.0f) / lrt;
     T* orow = prm.o + ((size_t)bh * Nq + my_q) * D;
 #pragma unroll
     for (int db = 0; db < P::DB; ++db)
