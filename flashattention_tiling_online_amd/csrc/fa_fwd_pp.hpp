@@ -38,7 +38,8 @@
 // phase has ended.
 //
 // With key splits a workgroup stages one range of whole key tiles and writes fp32
-// partial states, as fa_fwd_mfma16.hpp does.
+// partial states, as fa_fwd_mfma16.hpp does; with dropout the softmax phase zeroes
+// the dropped entries of the rounded P (the Philox words of fa_philox.hpp).
 #pragma once
 
 #include <type_traits>
@@ -432,7 +433,8 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
 
     if (!wave_active)
         return;  // no barrier follows
-    // ---- epilogue: O = O~ / lr (rounded to T), L = ln2 (m2 + log2 l); split: O~ / lr
+    // ---- epilogue: O = O~ / lr (times the keep scale with dropout, rounded to T),
+    // L = ln2 (m2 + log2 l); split: O~ / lr
     // and L in fp32 into the partial buffers, and for a row that saw no key of its
     // range the identity of the merge, L = -inf with O = 0
     const float lsum = l_done + (ls0 + ls1);
