@@ -139,9 +139,9 @@ void fa_bwd_dkv_kernel(const BwdParams<T> prm)
     const char* const sm = smem;
     const int Nq = prm.Nq, Nk = prm.Nk;
 
-    const int logical = xcd_remap((int)blockIdx.x, (int)gridDim.x);
-    const int bh = logical / prm.n_tiles;
-    const int kt = logical - bh * prm.n_tiles;  // key tile: heaviest (causal) first
+    const WorkItem wi = work_item((int)blockIdx.x, (int)gridDim.x, prm.n_tiles, CAUSAL);
+    const int bh = wi.head;
+    const int kt = wi.rank;  // key tile: heaviest (causal) first
     const int k0 = kt * P::KEYS;
 
     const int tid = (int)threadIdx.x;
@@ -365,11 +365,9 @@ void fa_bwd_dq_kernel(const BwdParams<T> prm)
     const char* const sm = smem;
     const int Nq = prm.Nq, Nk = prm.Nk;
 
-    const int logical = xcd_remap((int)blockIdx.x, (int)gridDim.x);
-    const int bh = logical / prm.n_tiles;
-    int qt = logical - bh * prm.n_tiles;
-    if (CAUSAL)
-        qt = prm.n_tiles - 1 - qt;  // longest rows first
+    const WorkItem wi = work_item((int)blockIdx.x, (int)gridDim.x, prm.n_tiles, CAUSAL);
+    const int bh = wi.head;
+    const int qt = CAUSAL ? prm.n_tiles - 1 - wi.rank : wi.rank;  // longest rows first
     const int q0 = qt * P::ROWS;
 
     const int tid = (int)threadIdx.x;

@@ -42,13 +42,11 @@ void fa_fwd_f32_kernel(const FwdParams<float> prm)
     const int Nq = prm.Nq, Nk = prm.Nk, n_qtiles = prm.n_qtiles;
     const float c2 = prm.c2;
 
-    const int logical = xcd_remap((int)blockIdx.x, (int)gridDim.x);
-    const int rest = logical / n_qtiles;
-    int qt = logical - rest * n_qtiles;
+    const WorkItem wi = work_item((int)blockIdx.x, (int)gridDim.x, n_qtiles, CAUSAL && !SPLIT);
+    const int rest = wi.head;
+    const int qt = CAUSAL ? n_qtiles - 1 - wi.rank : wi.rank;
     const int split = SPLIT ? rest % prm.n_splits : 0;
     const int bh = SPLIT ? rest / prm.n_splits : rest;
-    if (CAUSAL)
-        qt = n_qtiles - 1 - qt;
     const int q0 = qt * P::BR;
 
     const int tid = (int)threadIdx.x;

@@ -89,13 +89,11 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
 
     // ---- which (batch*head, key split, query tile) this workgroup owns; the
     // query tiles of one (head, split) are consecutive, so they share an XCD's L2
-    const int logical = xcd_remap((int)blockIdx.x, (int)gridDim.x);
-    const int rest = logical / n_qtiles;
-    int qt = logical - rest * n_qtiles;
+    const WorkItem wi = work_item((int)blockIdx.x, (int)gridDim.x, n_qtiles, CAUSAL && !SPLIT);
+    const int rest = wi.head;
+    const int qt = CAUSAL ? n_qtiles - 1 - wi.rank : wi.rank;  // longest rows (most key tiles) first
     const int split = SPLIT ? rest % prm.n_splits : 0;
     const int bh = SPLIT ? rest / prm.n_splits : rest;
-    if (CAUSAL)
-        qt = n_qtiles - 1 - qt;  // longest rows (most key tiles) are dispatched first
     const int q0 = qt * P::BR;
 
     const int tid = (int)threadIdx.x;

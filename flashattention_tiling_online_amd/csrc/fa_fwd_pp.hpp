@@ -88,15 +88,13 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     const int Nq = prm.Nq, Nk = prm.Nk, n_qtiles = prm.n_qtiles;
     const float c2 = prm.c2;
 
-    // ---- (batch*head, key split, query tile) of this workgroup, XCD-aware, causal
-    // longest first; the query tiles of one (head, split) are consecutive
-    const int logical = xcd_remap((int)blockIdx.x, (int)gridDim.x);
-    const int rest = logical / n_qtiles;
-    int qt = logical - rest * n_qtiles;
+    // ---- (batch*head, key split, query tile) of this workgroup: the query tiles of
+    // one (head, split) share an XCD; causal: the longest rows (most key tiles) first
+    const WorkItem wi = work_item((int)blockIdx.x, (int)gridDim.x, n_qtiles, CAUSAL && !SPLIT);
+    const int rest = wi.head;
+    const int qt = CAUSAL ? n_qtiles - 1 - wi.rank : wi.rank;
     const int split = SPLIT ? rest % prm.n_splits : 0;
     const int bh = SPLIT ? rest / prm.n_splits : rest;
-    if (CAUSAL)
-        qt = n_qtiles - 1 - qt;
     const int q0 = qt * P::BR;
 
     const int tid = (int)threadIdx.x;

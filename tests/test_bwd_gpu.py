@@ -94,6 +94,10 @@ SMALL = [
     ("bwd_nq_gt_nk_causal", 1, 2, 300, 100, 128, "bf16", True, 56),
     ("bwd_f16_causal_d64", 1, 3, 321, 321, 64, "f16", True, 57),
     ("bwd_large_logits", 1, 2, 256, 512, 128, "bf16", True, 58, 3.0),
+    # causal grids of whole heads per XCD (16 heads: items listed by weight across the
+    # XCD's heads) and of split heads (12 heads: head-major order kept)
+    ("bwd_16h_causal_order", 2, 8, 300, 300, 128, "bf16", True, 59),
+    ("bwd_12h_causal_order", 1, 12, 260, 260, 128, "f16", True, 60),
 ]
 
 

@@ -109,6 +109,14 @@ EXTRA = [
     (1, 1, 100, 70, 64, "f32", True, 1.0),
     (1, 3, 640, 640, 128, "bf16", True, 3.0),    # large logits: many rescales
     (1, 2, 1000, 1000, 64, "bf16", True, 3.0),
+    # causal grids whose workgroup order lists the tiles by weight across the heads of
+    # each XCD (whole heads per XCD: 16, 8 and 24 heads), and one that keeps the
+    # head-major order (12 heads split over the XCDs)
+    (2, 8, 600, 600, 128, "bf16", True, 1.0),
+    (1, 8, 1100, 1100, 128, "bf16", True, 1.0),
+    (3, 8, 520, 520, 128, "f16", True, 1.0),
+    (1, 12, 600, 600, 128, "bf16", True, 1.0),
+    (2, 8, 700, 700, 64, "bf16", True, 1.0),
 ]
 
 
