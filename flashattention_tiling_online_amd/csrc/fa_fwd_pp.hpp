@@ -66,6 +66,8 @@ struct TilePP {
     static constexpr int NKB = 3;             // K buffers
     static constexpr int VOFF = NKB * KT;     // first V^T buffer
     static constexpr int LDS = NKB * KT + 2 * VT;
+    static constexpr int OSTR = 2 * D + 16;   // bytes per row of a wave's O in LDS (epilogue)
+    static_assert(NW * 32 * OSTR <= LDS, "the epilogue's O rows must fit the K and V^T buffers");
     static_assert(KT % 1024 == 0, "K tiles must be whole DMA blocks");
     static_assert(NT == 4 * D, "V staging: one 4-key x 4-dim block per thread");
 };
@@ -439,9 +441,9 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     const float lrsum = lr_done + (lrs0 + lrs1);
     const float lt = lsum + swap_halves(lsum);
     const float lrt = lrsum + swap_halves(lrsum);
-    if (my_q >= Nq)
-        return;
     if (SPLIT) {
+        if (my_q >= Nq)
+            return;
         const size_t row = ((size_t)split * prm.bh_count + bh) * Nq + my_q;
         const float inv = lrt > 0.f ? 1.0f / lrt : 0.f;
         float* orow = prm.o_part + row * D;
@@ -459,8 +461,11 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
             prm.lse_part[row] = lt > 0.f ? (m2 + log2_fast(lt)) * kLn2 : neg_inf();
         return;
     }
+    // O rounded to T goes through this wave's own LDS rows (the K and V^T buffers are
+    // free after the last barrier), so that each store writes four whole rows of O
+    // rather than 16-byte pieces of 32 rows
     const float inv = (DROP ? prm.drop_keep_scale : 1.0f) / lrt;
-    T* orow = prm.o + ((size_t)bh * Nq + my_q) * D;
+    char* const ost = smem + wave * 32 * P::OSTR;
 #pragma unroll
     for (int db = 0; db < P::DB; ++db)
 #pragma unroll
@@ -469,9 +474,18 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 w[e] = (T)(o[db][4 * a + e] * inv);
-            *reinterpret_cast<T4*>(orow + 32 * db + 8 * a + 4 * hh) = w;
+            *reinterpret_cast<T4*>(ost + ql * P::OSTR + 2 * (32 * db + 8 * a + 4 * hh)) = w;
         }
-    if (hh == 0)
+    T* const ohead = prm.o + (size_t)bh * Nq * D;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + (lane >> 4);
+        const int ch = lane & 15;
+        const u32x4 piece = *reinterpret_cast<const u32x4*>(ost + r * P::OSTR + 16 * ch);
+        if (qw0 + r < Nq)
+            *reinterpret_cast<u32x4*>(ohead + (size_t)(qw0 + r) * D + 8 * ch) = piece;
+    }
+    if (hh == 0 && my_q < Nq)
         prm.lse[(size_t)bh * Nq + my_q] = (m2 + log2_fast(lt)) * kLn2;
 }
 
