@@ -68,6 +68,7 @@ struct TilePP {
     static constexpr int LDS = NKB * KT + 2 * VT;
     static constexpr int OSTR = 2 * D + 16;   // bytes per row of a wave's O in LDS (epilogue)
     static_assert(NW * 32 * OSTR <= LDS, "the epilogue's O rows must fit the K and V^T buffers");
+    static_assert(KT + BR * KSTR <= LDS, "the prologue's Q rows must fit past K buffer 0");
     static_assert(KT % 1024 == 0, "K tiles must be whole DMA blocks");
     static_assert(NT == 4 * D, "V staging: one 4-key x 4-dim block per thread");
 };
@@ -151,15 +152,9 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     const int kbase = ql * P::KSTR + hh * 16;
     const int vbase = ql * P::VTSTR + hh * 16;
 
-    // ---- Q fragment (B operand of S^T = K Q^T): lane supplies Q[my_q][16c + 8hh .. +8]
+    // ---- Q fragment (B operand of S^T = K Q^T): lane supplies Q[my_q][16c + 8hh .. +8],
+    // read in the prologue from the workgroup's Q rows staged in LDS (rows past Nq are 0)
     vec qf[P::DC];
-#pragma unroll
-    for (int c = 0; c < P::DC; ++c) {
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (my_q < Nq)
-            raw = *reinterpret_cast<const u32x4*>(Qh + (size_t)my_q * D + 16 * c + 8 * hh);
-        qf[c] = __builtin_bit_cast(vec, raw);
-    }
 
     // ---- running state
     f32x16 o[P::DB];
@@ -374,18 +369,30 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
         __asm__ volatile("" ::: "memory");
     };
 
-    // ---- prologue: K_0 (and group 0's blocks of K_1) by DMA; V_0 and V_1 into
-    // registers, this group's dims
-    if (0 < nkt) {
+    // ---- prologue: K_0 and the workgroup's 256 Q rows by DMA (Q into K buffers 1-2
+    // and the V^T buffers, free until K_1 and V^T_0 arrive; whole rows per DMA block,
+    // where loading the fragments straight from memory would touch 32 rows per
+    // load); V_0 and V_1 into registers, this group's dims.  Then every wave reads
+    // its Q fragments, and a barrier frees the staging area for K_1.
+    if (0 < nkt)
         stage_k(0, 0);
+#pragma unroll
+    for (int t = 0; t < P::BR / P::BC; ++t)
+        stage_tile<D, P::KNB, P::KPW, P::NW>(Qh, q0 / P::BC + t, Nq, smem + P::KT * (1 + t), wave, ksrc);
+    if (0 < nkt)
         load_v(0, 0);
-    }
-    if (1 < nkt) {
-        if (grp == 0)
-            stage_k(1, P::KT);
+    if (1 < nkt)
         load_v(1, 1);
-    }
     barrier(true);
+    {
+        const char* const qrow = sm + P::KT + (qw0 - q0 + ql) * P::KSTR + hh * 16;
+#pragma unroll
+        for (int c = 0; c < P::DC; ++c)
+            qf[c] = *reinterpret_cast<const vec*>(qrow + 32 * c);
+    }
+    barrier(false);
+    if (1 < nkt && grp == 0)
+        stage_k(1, P::KT);
 
     // ---- phases: group 0 runs MFMA(j) in phase 2j and softmax(u) in phase 2u - 1,
     // group 1 softmax(u) in phase 2u and MFMA(j) in phase 2j + 1.  Both groups run
