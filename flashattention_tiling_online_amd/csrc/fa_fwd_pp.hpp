@@ -449,23 +449,35 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     const float lt = lsum + swap_halves(lsum);
     const float lrt = lrsum + swap_halves(lrsum);
     if (SPLIT) {
-        if (my_q >= Nq)
-            return;
-        const size_t row = ((size_t)split * prm.bh_count + bh) * Nq + my_q;
+        // fp32 partial O through this wave's LDS rows as below, in two halves of 64
+        // columns (256 bytes a row, like a row of T)
         const float inv = lrt > 0.f ? 1.0f / lrt : 0.f;
-        float* orow = prm.o_part + row * D;
+        char* const ost = smem + wave * 32 * P::OSTR;
+        float* const phead = prm.o_part + ((size_t)split * prm.bh_count + bh) * Nq * D;
 #pragma unroll
-        for (int db = 0; db < P::DB; ++db)
+        for (int half = 0; half < 2; ++half) {
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                f32x4 w;
+            for (int db = 2 * half; db < 2 * half + 2; ++db)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    w[e] = o[db][4 * a + e] * inv;
-                *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * a + 4 * hh) = w;
+                for (int a = 0; a < 4; ++a) {
+                    f32x4 w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        w[e] = o[db][4 * a + e] * inv;
+                    *reinterpret_cast<f32x4*>(ost + ql * P::OSTR + 4 * (32 * (db - 2 * half) + 8 * a + 4 * hh)) = w;
+                }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = 4 * i + (lane >> 4);
+                const int ch = lane & 15;
+                const f32x4 piece = *reinterpret_cast<const f32x4*>(ost + r * P::OSTR + 16 * ch);
+                if (qw0 + r < Nq)
+                    *reinterpret_cast<f32x4*>(phead + (size_t)(qw0 + r) * D + 64 * half + 4 * ch) = piece;
             }
-        if (hh == 0)
-            prm.lse_part[row] = lt > 0.f ? (m2 + log2_fast(lt)) * kLn2 : neg_inf();
+        }
+        if (hh == 0 && my_q < Nq)
+            prm.lse_part[((size_t)split * prm.bh_count + bh) * Nq + my_q] =
+                lt > 0.f ? (m2 + log2_fast(lt)) * kLn2 : neg_inf();
         return;
     }
     // O rounded to T goes through this wave's own LDS rows (the K and V^T buffers are

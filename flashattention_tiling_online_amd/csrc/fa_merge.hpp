@@ -39,18 +39,39 @@ void fa_merge_kernel(const float* __restrict__ o_part, const float* __restrict__
     if (row >= rows)
         return;
 
+    // parts in groups of NG, each group's loads issued together (the fold is a
+    // memory-bound stream: the loads, not the arithmetic, set its time)
+    constexpr int NG = 8;
     float mx = neg_inf();
-    for (int s = 0; s < n_parts; ++s)
-        mx = fmaxf(mx, lse_part[(int64_t)s * rows + row]);
+    for (int s0 = 0; s0 < n_parts; s0 += NG) {
+        float l[NG];
+#pragma unroll
+        for (int u = 0; u < NG; ++u)
+            l[u] = s0 + u < n_parts ? lse_part[(int64_t)(s0 + u) * rows + row] : neg_inf();
+#pragma unroll
+        for (int u = 0; u < NG; ++u)
+            mx = fmaxf(mx, l[u]);
+    }
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
     if (mx != neg_inf()) {
-        for (int s = 0; s < n_parts; ++s) {
-            const float w = expf(lse_part[(int64_t)s * rows + row] - mx);  // 0 for an empty part
-            const f32x4 v = *reinterpret_cast<const f32x4*>(o_part + ((int64_t)s * rows + row) * D + 4 * t);
-            wsum += w;
-            acc += w * v;
+        for (int s0 = 0; s0 < n_parts; s0 += NG) {
+            float l[NG];
+            f32x4 v[NG];
+#pragma unroll
+            for (int u = 0; u < NG; ++u) {
+                const bool in = s0 + u < n_parts;
+                l[u] = in ? lse_part[(int64_t)(s0 + u) * rows + row] : neg_inf();
+                v[u] = in ? *reinterpret_cast<const f32x4*>(o_part + ((int64_t)(s0 + u) * rows + row) * D + 4 * t)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int u = 0; u < NG; ++u) {
+                const float w = expf(l[u] - mx);  // 0 for an empty part or a missing one
+                wsum += w;
+                acc += w * v[u];
+            }
         }
         acc *= 1.0f / wsum;
     }
