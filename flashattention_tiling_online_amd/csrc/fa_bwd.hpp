@@ -108,6 +108,8 @@ struct DkvTile {
     // partial accumulators of the second query half, exchanged at the end
     static constexpr int XCH = 4 * 2 * DB * 16 * 64 * 4;
     static_assert(XCH <= LDS, "reduction buffer must fit the staging space");
+    static constexpr int OSTR = 2 * 64 + 16;     // bytes per staged row of 64 dK or dV columns
+    static_assert(4 * 2 * 32 * OSTR <= LDS, "the staged dK and dV rows must fit");
 };
 
 // The 4-row x 4-column block b of a [64, D] tile (rows 4kg.., columns 4dq..): the
@@ -307,27 +309,53 @@ void fa_bwd_dkv_kernel(const BwdParams<T> prm)
             }
     }
     __syncthreads();
-    if (qh == 1 || my_k >= Nk)
-        return;
-    // epilogue: accumulator register r of block db holds d = 32db + 8(r/4) + 4hh + r%4
-    T* dkrow = prm.dk + ((size_t)bh * Nk + my_k) * D;
-    T* dvrow = prm.dv + ((size_t)bh * Nk + my_k) * D;
+    if (qh == 0) {
 #pragma unroll
-    for (int db = 0; db < P::DB; ++db)
+        for (int db = 0; db < P::DB; ++db)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            T4 wk, wv;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * a + e;
-                const float sk = dkt[db][r] + xch[(((kblk * 2 + 0) * P::DB + db) * 16 + r) * 64 + lane];
-                const float sv = dvt[db][r] + xch[(((kblk * 2 + 1) * P::DB + db) * 16 + r) * 64 + lane];
-                wk[e] = (T)(sk * prm.scale);
-                wv[e] = (T)sv;
+            for (int r = 0; r < 16; ++r) {
+                dkt[db][r] += xch[(((kblk * 2 + 0) * P::DB + db) * 16 + r) * 64 + lane];
+                dvt[db][r] += xch[(((kblk * 2 + 1) * P::DB + db) * 16 + r) * 64 + lane];
             }
-            *reinterpret_cast<T4*>(dkrow + 32 * db + 8 * a + 4 * hh) = wk;
-            *reinterpret_cast<T4*>(dvrow + 32 * db + 8 * a + 4 * hh) = wv;
+    }
+    __syncthreads();  // the exchange is read: its space takes the rows of dK and dV
+    if (qh == 1)
+        return;
+    // epilogue: accumulator register r of block db holds d = 32db + 8(r/4) + 4hh + r%4.
+    // The rows go through this wave's LDS rows, 64 columns at a time, so that each
+    // store writes 128 bytes of 8 rows rather than 8 bytes of 32 rows.
+    char* const kst = smem + kblk * 2 * 32 * P::OSTR;
+    char* const vst = kst + 32 * P::OSTR;
+    T* const dkh = prm.dk + (size_t)bh * Nk * D;
+    T* const dvh = prm.dv + (size_t)bh * Nk * D;
+#pragma unroll
+    for (int half = 0; half < D / 64; ++half) {
+#pragma unroll
+        for (int db = 2 * half; db < 2 * half + 2; ++db)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                T4 wk, wv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    wk[e] = (T)(dkt[db][4 * a + e] * prm.scale);
+                    wv[e] = (T)dvt[db][4 * a + e];
+                }
+                const int off = kl * P::OSTR + 2 * (32 * (db - 2 * half) + 8 * a + 4 * hh);
+                *reinterpret_cast<T4*>(kst + off) = wk;
+                *reinterpret_cast<T4*>(vst + off) = wv;
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 8 * i + (lane >> 3);
+            const int ch = lane & 7;
+            const u32x4 pk = *reinterpret_cast<const u32x4*>(kst + r * P::OSTR + 16 * ch);
+            const u32x4 pv = *reinterpret_cast<const u32x4*>(vst + r * P::OSTR + 16 * ch);
+            if (kw0 + r < Nk) {
+                *reinterpret_cast<u32x4*>(dkh + (size_t)(kw0 + r) * D + 64 * half + 8 * ch) = pk;
+                *reinterpret_cast<u32x4*>(dvh + (size_t)(kw0 + r) * D + 64 * half + 8 * ch) = pv;
+            }
         }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -350,6 +378,8 @@ struct DqTile {
     static constexpr int VR = TILE * RSTR;             // V row tile
     static constexpr int KT = 2 * TILE * RSTR;         // K transposed tile
     static constexpr int LDS = KT + D * TSTR;
+    static constexpr int OSTR = 2 * 64 + 16;     // bytes per staged row of 64 dQ columns
+    static_assert(NW * 32 * OSTR <= LDS, "the staged dQ rows must fit the tiles");
     static_assert(NT == 4 * D, "one 4x4 block per tensor per thread");
 };
 
@@ -488,18 +518,31 @@ void fa_bwd_dq_kernel(const BwdParams<T> prm)
             }
     }
 
-    if (my_q < Nq) {
-        T* row = prm.dq + ((size_t)bh * Nq + my_q) * D;
+    // dQ rows through this wave's LDS rows, 64 columns at a time (the K and V tiles
+    // are consumed after the barrier), so that each store writes 128 bytes of 8 rows
+    __syncthreads();
+    char* const ost = smem + wave * 32 * P::OSTR;
+    T* const dqh = prm.dq + (size_t)bh * Nq * D;
 #pragma unroll
-        for (int db = 0; db < P::DB; ++db)
+    for (int half = 0; half < D / 64; ++half) {
+#pragma unroll
+        for (int db = 2 * half; db < 2 * half + 2; ++db)
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 T4 w;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     w[e] = (T)(dqt[db][4 * a + e] * prm.scale);
-                *reinterpret_cast<T4*>(row + 32 * db + 8 * a + 4 * hh) = w;
+                *reinterpret_cast<T4*>(ost + ql * P::OSTR + 2 * (32 * (db - 2 * half) + 8 * a + 4 * hh)) = w;
             }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 8 * i + (lane >> 3);
+            const int ch = lane & 7;
+            const u32x4 piece = *reinterpret_cast<const u32x4*>(ost + r * P::OSTR + 16 * ch);
+            if (qw0 + r < Nq)
+                *reinterpret_cast<u32x4*>(dqh + (size_t)(qw0 + r) * D + 64 * half + 8 * ch) = piece;
+        }
     }
 }
 
