@@ -71,6 +71,10 @@ struct Tile16 {
     static constexpr int SUMS = 2 * KT + 2 * VT;  // per thread: completed row-sum blocks
     static constexpr int LDS = SUMS + 8 * NT;      // K[2], V^T[2], sums
     static constexpr int K0 = 0, K1 = KT, V0 = 2 * KT, V1 = 2 * KT + VT;
+    // epilogue: a wave's 32 rows of O (2D bytes each) or of 64 fp32 partial columns
+    // (256 bytes), staged in LDS with 16 bytes of padding
+    static constexpr int OSTR = (2 * D > 256 ? 2 * D : 256) + 16;
+    static_assert(NW * 32 * OSTR <= SUMS, "the epilogue's rows must fit the tile buffers");
     static_assert(KT % 1024 == 0, "K tiles must be whole DMA blocks");
 };
 
@@ -384,39 +388,62 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
     const float lsum = done[0] + l, lrsum = done[1] + lr;
     const float lt = lsum + swap_halves(lsum);
     const float lrt = lrsum + swap_halves(lrsum);
-    if (my_q < Nq) {
-        if (SPLIT) {
-            const size_t row = ((size_t)split * prm.bh_count + bh) * Nq + my_q;
-            const float inv = lrt > 0.f ? 1.0f / lrt : 0.f;
-            float* orow = prm.o_part + row * D;
+    // O goes through this wave's own LDS rows (the tile buffers are free after the
+    // last barrier; the row sums lie past them), so that each store writes whole
+    // rows rather than 8 or 16 bytes of 32 rows; fp32 partials 64 columns at a time
+    char* const ost = smem + wave * 32 * P::OSTR;
+    if (SPLIT) {
+        const float inv = lrt > 0.f ? 1.0f / lrt : 0.f;
+        float* const phead = prm.o_part + ((size_t)split * prm.bh_count + bh) * Nq * D;
 #pragma unroll
-            for (int db = 0; db < P::DB; ++db)
+        for (int half = 0; half < D / 64; ++half) {
+#pragma unroll
+            for (int db = 2 * half; db < 2 * half + 2; ++db)
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
                     f32x4 w;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         w[e] = o[db][4 * a + e] * inv;
-                    *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * a + 4 * hh) = w;
+                    *reinterpret_cast<f32x4*>(ost + ql * P::OSTR + 4 * (32 * (db - 2 * half) + 8 * a + 4 * hh)) = w;
                 }
-            if (hh == 0)
-                prm.lse_part[row] = lt > 0.f ? (m2 + log2_fast(lt)) * kLn2 : neg_inf();
-        } else {
-            const float inv = (DROP ? prm.drop_keep_scale : 1.0f) / lrt;
-            T* orow = prm.o + ((size_t)bh * Nq + my_q) * D;
 #pragma unroll
-            for (int db = 0; db < P::DB; ++db)
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    T4 w;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        w[e] = (T)(o[db][4 * a + e] * inv);
-                    *reinterpret_cast<T4*>(orow + 32 * db + 8 * a + 4 * hh) = w;
-                }
-            if (hh == 0)
-                prm.lse[(size_t)bh * Nq + my_q] = (m2 + log2_fast(lt)) * kLn2;
+            for (int i = 0; i < 8; ++i) {
+                const int r = 4 * i + (lane >> 4);
+                const int ch = lane & 15;
+                const f32x4 piece = *reinterpret_cast<const f32x4*>(ost + r * P::OSTR + 16 * ch);
+                if (qw0 + r < Nq)
+                    *reinterpret_cast<f32x4*>(phead + (size_t)(qw0 + r) * D + 64 * half + 4 * ch) = piece;
+            }
         }
+        if (hh == 0 && my_q < Nq)
+            prm.lse_part[((size_t)split * prm.bh_count + bh) * Nq + my_q] =
+                lt > 0.f ? (m2 + log2_fast(lt)) * kLn2 : neg_inf();
+    } else {
+        const float inv = (DROP ? prm.drop_keep_scale : 1.0f) / lrt;
+#pragma unroll
+        for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                T4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = (T)(o[db][4 * a + e] * inv);
+                *reinterpret_cast<T4*>(ost + ql * P::OSTR + 2 * (32 * db + 8 * a + 4 * hh)) = w;
+            }
+        constexpr int LPR = 2 * D / 16;  // lanes per row of T, 16 bytes each
+        constexpr int RPI = 64 / LPR;    // rows per store
+        T* const ohead = prm.o + (size_t)bh * Nq * D;
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+            const int r = RPI * i + lane / LPR;
+            const int ch = lane % LPR;
+            const u32x4 piece = *reinterpret_cast<const u32x4*>(ost + r * P::OSTR + 16 * ch);
+            if (qw0 + r < Nq)
+                *reinterpret_cast<u32x4*>(ohead + (size_t)(qw0 + r) * D + 8 * ch) = piece;
+        }
+        if (hh == 0 && my_q < Nq)
+            prm.lse[(size_t)bh * Nq + my_q] = (m2 + log2_fast(lt)) * kLn2;
     }
 }
 
