@@ -37,6 +37,11 @@
 // writes, and no buffer or register slot is rewritten before its last reader's
 // phase has ended.
 //
+// Q and O move as whole rows: the prologue stages the workgroup's 256 Q rows by DMA
+// into buffers not yet in use and each wave reads its fragments from there; the
+// epilogue writes O (or the fp32 partials) through each wave's own LDS rows.  The
+// workgroup's (head, query tile) comes from work_item (fa_common.hpp).
+//
 // With key splits a workgroup stages one range of whole key tiles and writes fp32
 // partial states, as fa_fwd_mfma16.hpp does; with dropout the softmax phase zeroes
 // the dropped entries of the rounded P (the Philox words of fa_philox.hpp).
