@@ -5,8 +5,9 @@ The shapes are drawn once from a fixed seed: batch and head counts (so that the
 workgroup orders for whole and split heads per XCD both occur), query and key
 lengths up to 1500 (ragged tiles, Nq != Nk, single rows), d in {64, 128}, bf16 /
 fp16 / fp32, causal or not, and logit scales sigma 1 or 3.  Forward (fa_fwd), key
-split (fa_fwd_split with 2 to 8 ranges) and backward (fa_bwd, bf16/fp16) each get
-their own draw.
+split (fa_fwd_split with 2 to 8 ranges), backward (fa_bwd, bf16/fp16) and dropout
+(fa_fwd_dropout / fa_bwd_dropout, bf16/fp16, drop probabilities 0.1 to 0.9, the
+bounds of test_dropout_gpu.py) each get their own draw.
 """
 import numpy as np
 import pytest
@@ -23,6 +24,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 import flashattention_tiling_online_amd as fa  # noqa: E402
 from parity_util import compare, say, to_dev, to_host  # noqa: E402
 from test_bwd_gpu import check_all_rows as bwd_check_all_rows  # noqa: E402
+from test_dropout_gpu import check_grad, compare_fwd, run_fwd, threshold  # noqa: E402
 
 
 def draw(seed, n, dtypes, max_n, max_h):
@@ -44,6 +46,9 @@ def draw(seed, n, dtypes, max_n, max_h):
 FWD = draw(7, 60, ["bf16", "bf16", "f16", "f32"], 1500, 7)
 SPLIT = draw(8, 30, ["bf16", "f16", "f32"], 1500, 7)
 BWD = draw(9, 20, ["bf16", "f16"], 600, 4)
+DROP_FWD = draw(10, 20, ["bf16", "f16"], 1000, 7)
+DROP_BWD = draw(11, 8, ["bf16", "f16"], 400, 4)
+P_DROP = (0.1, 0.3, 0.5, 0.9)
 
 
 def workload(spec):
@@ -85,3 +90,39 @@ def test_sweep_split(spec):
 @pytest.mark.parametrize("spec", BWD, ids=[s[0] for s in BWD])
 def test_sweep_bwd(spec):
     bwd_check_all_rows(workload(spec))
+
+
+@pytest.mark.parametrize("spec", DROP_FWD, ids=[s[0] for s in DROP_FWD])
+def test_sweep_dropout_fwd(spec):
+    w = workload(spec)
+    p = P_DROP[spec[-1] % 4]
+    rng_seed = 0x5EED0000 + spec[-1]
+    say(f"[sweep dropout fwd] {w.describe()} p={p}")
+    q, k, v = inputs.make_qkv(w)
+    o, lse = run_fwd(w, q, k, v, p, rng_seed)
+    sel_bh, sel_row = all_rows(w)
+    o64, l64 = oracle.ref_rows_dropout_f64(q, k, v, w.causal, w.scale, w.dtype, threshold(p),
+                                           rng_seed, sel_bh, sel_row)
+    compare_fwd(w, p, to_host(o, w.dtype), lse.cpu().numpy(), sel_bh, sel_row, o64, l64)
+
+
+@pytest.mark.parametrize("spec", DROP_BWD, ids=[s[0] for s in DROP_BWD])
+def test_sweep_dropout_bwd(spec):
+    w = workload(spec)
+    p = P_DROP[spec[-1] % 2]
+    rng_seed = 0xABCDEF + spec[-1]
+    say(f"[sweep dropout bwd] {w.describe()} p={p}")
+    q, k, v = inputs.make_qkv(w)
+    dout = inputs.make_do(w)
+    tq, tk, tv, tdo = (to_dev(a, w.dtype) for a in (q, k, v, dout))
+    o, lse = fa.fa_fwd_dropout(tq, tk, tv, p, rng_seed, causal=w.causal, scale=w.scale)
+    dq, dk, dv = fa.fa_bwd_dropout(tq, tk, tv, o, lse, tdo, p, rng_seed, causal=w.causal,
+                                   scale=w.scale)
+    torch.cuda.synchronize()
+    g = [oracle.widen(to_host(t, w.dtype), w.dtype).reshape(w.B * w.H, -1, w.d)
+         for t in (dq, dk, dv)]
+    for bh in range(w.B * w.H):
+        ref = oracle.bwd_head_dropout_f64(q, k, v, dout, w.causal, w.scale, w.dtype,
+                                          threshold(p), rng_seed, bh)
+        for nm, a, b in zip(("dq", "dk", "dv"), g, ref):
+            check_grad(f"{nm} head {bh}", a[bh], b, w.dtype)
