@@ -52,7 +52,7 @@ constexpr int kSortedMax = 128;
 struct WorkItem {
     int head, rank;
 };
-__device__ __forceinline__ WorkItem work_item(int wg, int n, int n_tiles, bool heavy_first)
+__host__ __device__ __forceinline__ WorkItem work_item(int wg, int n, int n_tiles, bool heavy_first)
 {
     const int per = n / kXcds;
     const int rem = n % kXcds;
