@@ -365,7 +365,7 @@ void fa_bwd_dkv_kernel(const BwdParams<T> prm)
 template <int D>
 struct DqTile {
     // d = 128: 8 waves (256 queries) per workgroup, one per CU; d = 64: 4 waves (128
-    // queries), two per CU; either way each thread stages one 4x4 block per tensor
+    // queries), two per CU; either way each thread stages one 4x4 block of K
     static constexpr int NW = D == 128 ? 8 : 4;
     static constexpr int NT = 64 * NW;
     static constexpr int ROWS = 32 * NW;        // queries per workgroup
@@ -377,10 +377,14 @@ struct DqTile {
     static constexpr int KR = 0;                       // K row tile
     static constexpr int VR = TILE * RSTR;             // V row tile
     static constexpr int KT = 2 * TILE * RSTR;         // K transposed tile
-    static constexpr int LDS = KT + D * TSTR;
+    static constexpr int VR1 = KT + D * TSTR;          // second V row tile (DMA, double-buffered)
+    static constexpr int LDS = VR1 + TILE * RSTR;
+    static constexpr int VNB = TILE * RSTR / 1024;     // 1-KB DMA blocks per V tile
+    static constexpr int VPW = (VNB + NW - 1) / NW;
+    static_assert(TILE * RSTR % 1024 == 0, "V tiles must be whole DMA blocks");
     static constexpr int OSTR = 2 * 64 + 16;     // bytes per staged row of 64 dQ columns
     static_assert(NW * 32 * OSTR <= LDS, "the staged dQ rows must fit the tiles");
-    static_assert(NT == 4 * D, "one 4x4 block per tensor per thread");
+    static_assert(NT == 4 * D, "one 4x4 block of K per thread");
 };
 
 template <typename T, int D, bool CAUSAL, bool DROP = false>
@@ -421,13 +425,18 @@ void fa_bwd_dq_kernel(const BwdParams<T> prm)
     if (CAUSAL && wave_active)
         n_w = min(nkt, min(qw0 + 31, Nq - 1) / P::TILE + 1);
 
-    // staging: this thread's 4x4 block of K and of V, loaded one tile ahead; K is
-    // written as a row tile and transposed, V as a row tile
+    // staging: this thread's 4x4 block of K, loaded one tile ahead and written as a row
+    // tile and transposed; V's row tile by DMA straight into LDS, a tile ahead into
+    // the other of two buffers
     const int s_kg = blk_kg(tid), s_dq = blk_dq(tid);
-    u32x2 kreg[4], vreg[4];
+    u32x2 kreg[4];
+    int vsrc[P::VPW];
+#pragma unroll
+    for (int i = 0; i < P::VPW; ++i)
+        vsrc[i] = dma_src<D>(wave + P::NW * i, lane, P::RSTR);
     if (0 < nkt) {
         load_v_block<D>(Kh, 0, Nk, s_kg, s_dq, kreg);
-        load_v_block<D>(Vh, 0, Nk, s_kg, s_dq, vreg);
+        stage_tile<D, P::VNB, P::VPW, P::NW>(Vh, 0, Nk, smem + P::VR, wave, vsrc);
     }
 
     // Q and dO rows of this lane's query as the B operands
@@ -458,11 +467,13 @@ void fa_bwd_dq_kernel(const BwdParams<T> prm)
         __syncthreads();  // the previous tile is consumed
         store_row_block<P::RSTR>(smem + P::KR, s_kg, s_dq, kreg);
         store_vt_block<P::TSTR>(smem + P::KT, s_kg, s_dq, kreg);
-        store_row_block<P::RSTR>(smem + P::VR, s_kg, s_dq, vreg);
+        __builtin_amdgcn_s_waitcnt(0x0070);  // this wave's DMA blocks of V_j have landed
         __syncthreads();
+        const int vr = (j & 1) ? P::VR1 : P::VR;
         if (j + 1 < nkt) {  // in flight while this tile is computed
             load_v_block<D>(Kh, j + 1, Nk, s_kg, s_dq, kreg);
-            load_v_block<D>(Vh, j + 1, Nk, s_kg, s_dq, vreg);
+            stage_tile<D, P::VNB, P::VPW, P::NW>(Vh, j + 1, Nk, smem + ((j & 1) ? P::VR : P::VR1),
+                                                 wave, vsrc);
         }
         if (j >= n_w)
             continue;
@@ -477,7 +488,7 @@ void fa_bwd_dq_kernel(const BwdParams<T> prm)
             for (int c = 0; c < P::DC; ++c) {
                 const vec a = *reinterpret_cast<const vec*>(sm + P::KR + rbase + 32 * kb * P::RSTR + 32 * c);
                 st[kb] = M::mma(a, qf[c], st[kb]);
-                const vec b = *reinterpret_cast<const vec*>(sm + P::VR + rbase + 32 * kb * P::RSTR + 32 * c);
+                const vec b = *reinterpret_cast<const vec*>(sm + vr + rbase + 32 * kb * P::RSTR + 32 * c);
                 dpt[kb] = M::mma(b, df[c], dpt[kb]);
             }
         }
