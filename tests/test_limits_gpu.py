@@ -1,4 +1,4 @@
-"""GPU parity at the largest offsets the forward accepts.
+"""GPU parity at the largest offsets the forward (and the backward, last test) accepts.
 
 fa_fwd limits a head to Nq*d < 2^31 elements (in-head offsets are 32-bit) and lets
 the whole tensor exceed 2^31 (head offsets are 64-bit).  Shape: B=1, H=2,
@@ -141,4 +141,44 @@ def test_largest_key_offsets(entry):
     say(f"  weight of the placed keys: min {np.exp(l_s - l64).min():.3f}, median {np.median(np.exp(l_s - l64)):.3f}")
     compare(small, to_host(o, "bf16"), lse.cpu().numpy(), sel_bh, sel_row, o64, l64)
     del tk, tv
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_largest_offsets(causal):
+    """fa_bwd at Nq = 2^24 - 256 (Q, dO, O and dQ 8 GiB each), Nk = 64: Q and dO are zero
+    except the 64 seeded rows per head placed as above.  A zero dO row has dP = 0 and
+    D = 0, so dS = 0: it adds nothing to dK and dV and its dQ row is exactly 0.  So dK,
+    dV and the placed dQ rows equal the fp64 oracle's gradients of the small problem
+    made of the placed rows (all 64 keys visible to each), within the backward's
+    bounds, and the other dQ rows are exactly zero."""
+    from test_bwd_gpu import check_close  # noqa: E402
+    small = inputs.custom("limits_bwd", 1, H, N_PLACED, NK, D, "bf16", False, seed=63)
+    say(f"[limits bwd] B=1 H={H} Nq={NQ} Nk={NK} d={D} bf16 causal={causal}; rows from {small.describe()}")
+    q_s, k, v = inputs.make_qkv(small)
+    do_s = inputs.make_do(small)
+    rows = placed_rows()
+    idx = torch.from_numpy(rows).to(DEV)
+    tq = torch.zeros((1, H, NQ, D), dtype=torch.bfloat16, device=DEV)
+    tdo = torch.zeros((1, H, NQ, D), dtype=torch.bfloat16, device=DEV)
+    tq_s, tdo_s = to_dev(q_s, "bf16"), to_dev(do_s, "bf16")
+    for h in range(H):
+        tq[0, h].index_copy_(0, idx, tq_s[0, h])
+        tdo[0, h].index_copy_(0, idx, tdo_s[0, h])
+    tk, tv = to_dev(k, "bf16"), to_dev(v, "bf16")
+    o, lse = fa.fa_fwd(tq, tk, tv, causal=causal, scale=small.scale)
+    dq, dk, dv = fa.fa_bwd(tq, tk, tv, o, lse, tdo, causal=causal, scale=small.scale)
+    torch.cuda.synchronize()
+    zero_rows = torch.from_numpy(np.array([0, 1, NK + 7, (1 << 23) + 3, NQ - 40], dtype=np.int64)).to(DEV)
+    for h in range(H):
+        ref_dq, ref_dk, ref_dv = oracle.bwd_head_f64(q_s, k, v, do_s, False, small.scale, "bf16", h)
+        got_dq = oracle.widen(to_host(dq[0, h].index_select(0, idx), "bf16"), "bf16")
+        got_dk = oracle.widen(to_host(dk[0, h], "bf16"), "bf16")
+        got_dv = oracle.widen(to_host(dv[0, h], "bf16"), "bf16")
+        say(f"  head {h}")
+        check_close("dq (placed rows)", got_dq, ref_dq, "bf16")
+        check_close("dk", got_dk, ref_dk, "bf16")
+        check_close("dv", got_dv, ref_dv, "bf16")
+        assert bool((dq[0, h].index_select(0, zero_rows) == 0).all())
+    del tq, tdo, o, lse, dq
     torch.cuda.empty_cache()
