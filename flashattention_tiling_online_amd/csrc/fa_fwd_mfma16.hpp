@@ -39,9 +39,10 @@
 //     run, the S MFMAs of tile j+1 are issued; K and V have separate double
 //     buffers with the next loads issued one tile ahead; one barrier per tile;
 //   * exp is exp2 with scale*log2(e) folded into one FMA; the running-max reference
-//     moves (with the O~ rescale) only when a row's max exceeds it by more than 2^8;
-//     L takes the fp32 row sum of P, O the row sum of the rounded P it was built
-//     from (see update_max).
+//     moves (with the O~ rescale) on a new row maximum while the row's sum is small,
+//     and once it is large only when a key would weigh more than 1/5 of the row
+//     (P never exceeds 2^8); L takes the fp32 row sum of P, O the row sum of the
+//     rounded P it was built from (see update_max).
 #pragma once
 
 #include "fa_philox.hpp"
@@ -233,15 +234,25 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
         return (key0 + P::BC > Nks) || (CAUSAL && key0 + P::BC - 1 > qkw0);
     };
 
-    // Running-max update with a lazy reference: m2 (and with it O~, l, lr, rescaled
-    // by alpha = 2^(m2 - m_new)) only moves when some lane of the wave sees its half
-    // of a row exceed m2 by more than kSlack, so P <= 2^kSlack and the 64-multiply
-    // rescale is rare.  The halves' maxima are exchanged only then: m2 is the same in
-    // both halves of a row because it is only ever set from the whole row's max.
-    // Any reference gives the same softmax: L = m2 + log2(sum P) uses the fp32 sum,
-    // and O is divided by the sum of the SAME rounded P that went into the P.V MFMAs,
-    // which keeps a row dominated by one key exact whatever that key's P is.
+    // Running-max update with a reference that moves only when it matters: m2 (and
+    // with it O~, l, lr, rescaled by alpha = 2^(m2 - m_new)) moves to the rows' maxima
+    // when some lane of the wave sees its half of a row exceed m2 + g, where
+    // g = clamp(e - kShift, 0, kSlack) and e is the binary exponent of a lower bound
+    // of the row's running sum (l >= 2^(e-1)): this half's sum over the current block
+    // of tiles, from an earlier tile (sums only grow between moves).  A key that does
+    // not move the reference has P <= 2^g <= l / 4: it weighs at most 1/5 of its row,
+    // and P <= 2^kSlack.  A key that does gets P = 1 exactly, as in the pages'
+    // recurrence (which moves on every new maximum), so the weight of a row's dominant
+    // key is not rounded; while l is small (peaked rows, the first tiles of a row)
+    // every new maximum moves it, and once l is large the 32-multiply rescale is rare.
+    // The halves' maxima are exchanged only on a move: m2 is the same in both halves
+    // of a row because it is only ever set from the whole row's max.  Any reference
+    // gives the same softmax: L = m2 + log2(sum P) uses the fp32 sum, and O is divided
+    // by the sum of the SAME rounded P that went into the P.V MFMAs.  thr2 = m2 + g:
+    // g = 0 after a move, recomputed after every second tile's sums.
     constexpr float kSlack = 8.0f;
+    constexpr int kShift = 3;
+    float thr2 = neg_inf();
     auto half_max = [&](const f32x16* s) {
         float mx = s[0][0];
 #pragma unroll
@@ -253,7 +264,7 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
     };
     auto update_max = [&](float mx) {
         const float mh = mx * c2;  // c2 > 0: max commutes with the scale
-        if (__builtin_amdgcn_ballot_w64(mh > m2 + kSlack) != 0) {
+        if (__builtin_amdgcn_ballot_w64(mh > thr2) != 0) {
             const float m_new = fmaxf(m2, fmaxf(mh, swap_halves(mh)));
             const float alpha = exp2_fast(m2 - m_new);  // 0 on the first tile (m2 = -inf)
 #pragma unroll
@@ -264,6 +275,7 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
             done[0] *= alpha;
             done[1] *= alpha;
             m2 = m_new;
+            thr2 = m_new;
         }
     };
 
@@ -292,6 +304,8 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
                 rr[e & 1] = M::dot_ones(w[e], rr[e & 1]);
         }
         lr += rr[0] + rr[1];
+        if (j & 1)
+            thr2 = m2 + (float)min(max(__builtin_amdgcn_frexp_expf(l) - kShift, 0), (int)kSlack);
         if ((j & (kSumBlock - 1)) == kSumBlock - 1) {
             done[0] += l;
             done[1] += lr;

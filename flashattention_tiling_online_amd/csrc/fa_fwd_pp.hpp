@@ -5,7 +5,7 @@
 // flash_attention_forward: per query tile m = -inf, l = 0, O~ = 0; per key/value tile
 // S = Q K_j^T scale, m_new = max(m, rowmax S), P = exp(S - m_new), l = alpha l +
 // rowsum P, O~ = alpha O~ + P V_j; O = O~ / l and L = m + log l at the end), with the
-// same transposed 32x32x16 MFMA formulation, lazy max reference and two row sums.
+// same transposed 32x32x16 MFMA formulation, reference-max rule and two row sums.
 // What differs is the schedule.
 //
 // A workgroup is 8 waves (256 query rows) and fills a CU; waves w and w + 4 share a
@@ -177,6 +177,8 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     // about (kSumBlock + T / kSumBlock) 2^-24.
     float ls0 = 0.f, ls1 = 0.f, lrs0 = 0.f, lrs1 = 0.f;
     float l_done = 0.f, lr_done = 0.f;
+    bool rescale = false;  // a rescale of O~ by alpha is pending (see update_max)
+    float alpha = 1.f;
 
     // S^T of one tile from the K buffer at kb_off
     auto scores_only = [&](int kb_off) {
@@ -236,18 +238,26 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
             }
     };
 
-    // Lazy running max (as in fa_fwd_mfma16.hpp): the reference m2 moves, with the
-    // rescale of O~ and the row sums by 2^(m2 - m_new), only when some row exceeds it
-    // by more than kSlack; O is divided by the sum of the same rounded P that entered
-    // the P.V MFMAs, L uses the fp32 sum.  The rescale of O~ is applied by the next
-    // MFMA phase (O~ is touched by MFMA phases only): `rescale` marks it pending,
+    // Running max with a reference that moves only when it matters (as in
+    // fa_fwd_mfma16.hpp): the reference m2 moves to the rows' maxima, with the rescale
+    // of O~ and the row sums by 2^(m2 - m_new), when some row's tile max exceeds
+    // m2 + g, g = clamp(e - kShift, 0, kSlack), where e is the binary exponent of a
+    // lower bound of the row's running sum l (l >= 2^(e-1)): this half's part of it,
+    // from an earlier tile (l only grows between moves).  A key that does not move the
+    // reference has P <= 2^g <= l / 4, so it weighs at most 1/5 of its row, and
+    // P <= 2^kSlack.  A key that does gets P = 1 exactly, as in the pages' recurrence
+    // (which moves on every new maximum): the weight of a row's dominant key is not
+    // rounded, and while l is small (peaked rows, a row's first tiles) every new
+    // maximum moves the reference.  O is divided by the sum of the same rounded P that
+    // entered the P.V MFMAs, L uses the fp32 sum.  The rescale of O~ is applied by the
+    // next MFMA phase (O~ is touched by MFMA phases only): `rescale` marks it pending,
     // alpha holds the factor.  What the per-tile work needs of m2 is kept ready:
     // mneg = -m2 (0 while m2 = -inf, so that a row with no visible key gets p = 0) and
-    // the raw-score threshold thr = (m2 + kSlack) / c2 of the move test (c2 > 0).
+    // the raw-score threshold thr = (m2 + g) / c2 of the move test (c2 > 0): g = 0
+    // after a move, recomputed every second tile.
     constexpr float kSlack = 8.0f;
+    constexpr int kShift = 3;
     const float inv_c2 = 1.0f / c2;
-    bool rescale = false;
-    float alpha = 1.f;
     float mneg = 0.f, thr = neg_inf();
     auto update_max = [&]() {
         float mx = s[0][0];
@@ -269,8 +279,13 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
             lr_done *= alpha;
             m2 = m_new;
             mneg = (m_new == neg_inf()) ? 0.f : -m_new;
-            thr = (m_new + kSlack) * inv_c2;
+            thr = m_new * inv_c2;
         }
+    };
+    // threshold of the move test from the current sums (m2 = -inf keeps it at -inf)
+    auto update_thr = [&]() {
+        const int e = __builtin_amdgcn_frexp_expf(l_done + (ls0 + ls1));
+        thr = (m2 + (float)min(max(e - kShift, 0), (int)kSlack)) * inv_c2;
     };
     // P = 2^(s c2 - m2) in fp32, summed into ls; rounded to T in the MFMA B-operand
     // order (chunk cc = 2kb + h holds registers 8h .. 8h+7 of block kb); the rounded
@@ -300,12 +315,14 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     };
     // softmax phase of tile u; forced inline, since with dropout the compiler would
     // otherwise emit it as a function and keep the captured state in scratch memory
-    auto softmax = [&](int u) __attribute__((always_inline)) {
+    auto softmax = [&](int u, auto UPD) __attribute__((always_inline)) {
         if (u < n_w) {
             if (needs_mask(u))
                 mask_tile(u);
             update_max();
             exp_sum_pack();
+            if (decltype(UPD)::value)
+                update_thr();
             if (DROP) {
                 // dropout on the P that multiplies V (the row sums keep the undropped P,
                 // the keep scale is applied in the epilogue): chunk cc holds keys
@@ -415,7 +432,7 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
         scores_only(0);
     barrier(true);
     stage(0, std::integral_constant<int, 0>{});
-    softmax(0);
+    softmax(0, std::false_type{});
     barrier(false);
     // unrolled by 6 = lcm(3 K buffers, 2 V^T buffers), so that every buffer offset
     // and register slot is a constant of the code
@@ -424,7 +441,7 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
         mfma(j, R);
         barrier(true);
         stage(j + 1, std::integral_constant<int, (r + 1) % 6>{});
-        softmax(j + 1);
+        softmax(j + 1, std::integral_constant<bool, (r & 1) == 0>{});  // odd tiles
         barrier(false);
     };
     for (int j = 0; j < nkt; j += 6) {

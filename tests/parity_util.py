@@ -4,12 +4,13 @@ and the comparison against the fp64 oracle with the stated bounds.
 Bounds (stated for the fused forward): bf16/fp16 inputs — max |dO| <= 1e-2,
 mean |dO| <= 1e-3, max |dL| <= 1e-3; fp32 inputs — max |dO| <= 1e-4 (and
 |dL| <= 1e-3).  dO is the GPU output widened to fp64 minus the oracle's fp64 O.
-Where |O_ref| >= 2 an element passes the max bound if it is one of the two bf16
-neighbours of O_ref (faithful rounding): there one bf16 step is 2^-6 or more, its half
-(the error of correct rounding alone) leaves at most 0.0022 of the 1e-2 for the
-arithmetic, and the rounding of P to bf16 that the method prescribes moves O by about
-2^-9 of the weight differences, enough to land on the other neighbour.
+Where |O_ref| >= 4 an element passes the max bound if it is one of the two bf16
+neighbours of O_ref (faithful rounding): there one bf16 step is 2^-5 or more, so
+correct rounding of the output alone can miss O_ref by more than 1e-2.  Below 4 the
+literal bound holds for every element.
 """
+import json
+import os
 import sys
 
 import numpy as np
@@ -38,6 +39,20 @@ def to_host(t, dtype: str) -> np.ndarray:
     return t.cpu().numpy()
 
 
+def record(w, **figures):
+    """Append one JSON line of parity figures to $FA_PARITY_LOG (when set)."""
+    path = os.environ.get("FA_PARITY_LOG")
+    if not path:
+        return
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    row = {"test": test, "workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+           "dtype": w.dtype, "causal": bool(w.causal), "sigma_qk": w.sigma_q}
+    row.update({k: (float(v) if isinstance(v, (float, np.floating)) else v)
+                for k, v in figures.items()})
+    with open(path, "a") as f:
+        f.write(json.dumps(row) + "\n")
+
+
 def bf16_neighbours_ok(o_gpu64, o_ref):
     """True where o_gpu is the bf16 value just below or just above o_ref in magnitude."""
     e = np.frexp(np.abs(o_ref))[1].astype(np.int32)    # |o_ref| in [2^(e-1), 2^e)
@@ -57,14 +72,20 @@ def compare(w, o_gpu_np, lse_gpu, sel_bh, sel_row, o64, l64):
     if w.dtype == "f32":
         say(f"  {w.name}: max|dO|={err.max():.3e} mean|dO|={err.mean():.3e} "
             f"max|dL|={derr_l.max():.3e}")
+        record(w, rows=len(sel_row), max_do=err.max(), mean_do=err.mean(), max_dl=derr_l.max())
         assert err.max() <= 1e-4
         assert derr_l.max() <= 1e-3
         return
-    big = np.abs(o64) >= 2.0
+    big = np.abs(o64) >= 4.0
     over = err > 1e-2
     faithful = over & big & (bf16_neighbours_ok(o_sel, o64) if w.dtype == "bf16" else False)
+    band = (np.abs(o64) >= 2.0) & ~big
     say(f"  {w.name}: max|dO|={err.max():.3e} mean|dO|={err.mean():.3e} "
         f"max|dL|={derr_l.max():.3e} faithful-rounding exceptions={int(faithful.sum())}")
+    record(w, rows=len(sel_row), max_do=err.max(), mean_do=err.mean(), max_dl=derr_l.max(),
+           over_lt2=int((over & (np.abs(o64) < 2.0)).sum()), over_2_4=int((over & band).sum()),
+           over_ge4=int((over & big).sum()), faithful_ge4=int(faithful.sum()),
+           max_abs_oref=float(np.abs(o64).max()))
     assert not (over & ~faithful).any(), f"max|dO| {err[over & ~faithful].max():.3e} > 1e-2"
     assert err.mean() <= 1e-3
     assert derr_l.max() <= 1e-3

@@ -23,37 +23,12 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 
 import flashattention_tiling_online_amd as fa  # noqa: E402
 from parity_util import compare, say, to_dev, to_host  # noqa: E402
+from sweep_specs import BWD, DROP_BWD, DROP_FWD, FWD, SPLIT, workload  # noqa: E402
 from test_bwd_gpu import check_all_rows as bwd_check_all_rows  # noqa: E402
 from test_dropout_gpu import check_grad, compare_fwd, run_fwd, threshold  # noqa: E402
 
 
-def draw(seed, n, dtypes, max_n, max_h):
-    rs = np.random.RandomState(seed)
-    out = []
-    for i in range(n):
-        B = int(rs.randint(1, 3))
-        H = int(rs.choice([1, 2, 3, 4, 5, 8, 9][: max(1, max_h)]))
-        Nq = int(rs.choice([1, 31, 33, 64, 127, 255, 257]) if rs.rand() < 0.3 else rs.randint(1, max_n + 1))
-        Nk = int(rs.choice([1, 63, 65, 128, 200]) if rs.rand() < 0.3 else rs.randint(1, max_n + 1))
-        d = int(rs.choice([64, 128]))
-        dt = str(rs.choice(dtypes))
-        causal = bool(rs.rand() < 0.5)
-        sig = float(rs.choice([1.0, 3.0]))
-        out.append((f"s{seed}_{i}", B, H, Nq, Nk, d, dt, causal, sig, 1000 * seed + i))
-    return out
-
-
-FWD = draw(7, 60, ["bf16", "bf16", "f16", "f32"], 1500, 7)
-SPLIT = draw(8, 30, ["bf16", "f16", "f32"], 1500, 7)
-BWD = draw(9, 20, ["bf16", "f16"], 600, 4)
-DROP_FWD = draw(10, 20, ["bf16", "f16"], 1000, 7)
-DROP_BWD = draw(11, 8, ["bf16", "f16"], 400, 4)
 P_DROP = (0.1, 0.3, 0.5, 0.9)
-
-
-def workload(spec):
-    name, B, H, Nq, Nk, d, dt, causal, sig, seed = spec
-    return inputs.custom(name, B, H, Nq, Nk, d, dt, causal, seed, sigma_q=sig, sigma_k=sig)
 
 
 def all_rows(w):
