@@ -153,6 +153,8 @@ def _check_qkv(q, k, v):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
             raise ValueError(f"{name} must be a contiguous 4-D GPU tensor [B,H,N,d]")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on the same GPU")
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
     if k.shape != (B, H, Nk, d) or v.shape != (B, H, Nk, d):
@@ -162,13 +164,62 @@ def _check_qkv(q, k, v):
     return B, H, Nq, Nk, d
 
 
+def _check_buf(name, t, shape, dtype, device):
+    """A caller-supplied buffer: a contiguous tensor of `shape` and `dtype` on `device`
+    (the library sees only its address, so a wrong one would send the kernels out of
+    bounds or to host memory)."""
+    if not hasattr(t, "is_cuda") or not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a GPU tensor on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _check_workspace(t, need, device):
+    """A caller-supplied workspace: a contiguous GPU buffer of at least `need` bytes."""
+    if not hasattr(t, "is_cuda") or not t.is_cuda or t.device != device:
+        raise ValueError(f"workspace must be a GPU tensor on {device}")
+    if not t.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if t.numel() * t.element_size() < need:
+        raise ValueError(f"workspace must hold at least {need} bytes")
+    return t
+
+
+def _outputs_fwd(q, B, H, Nq, o, lse):
+    """o [B,H,Nq,d] in q's dtype and lse [B,H,Nq] fp32: checked if given, else allocated
+    (on the current stream, which the caller has made the launch stream)."""
+    import torch
+    if o is None:
+        o = torch.empty_like(q)
+    else:
+        _check_buf("o", o, q.shape, q.dtype, q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        _check_buf("lse", lse, (B, H, Nq), torch.float32, q.device)
+    return o, lse
+
+
+def _launch_stream(stream, device):
+    """The stream to enqueue on (default: torch's current stream on `device`)."""
+    import torch
+    return torch.cuda.current_stream(device) if stream is None else stream
+
+
 def fa_fwd_split(q, k, v, causal: bool = False, scale: float | None = None, n_splits=None,
                  o=None, lse=None, workspace=None, stream=None):
     """fa_fwd computed over key ranges and merged (fa_fwd_split).
 
     n_splits defaults to fa_split_hint(...).  The fp32 workspace for the partial
     states is allocated with torch when not given (a uint8 GPU tensor of at least
-    fa_fwd_split_workspace(...) bytes may be passed instead).
+    fa_fwd_split_workspace(...) bytes may be passed instead).  Buffers the binding
+    allocates are allocated on the launch stream, so that torch does not hand their
+    memory to other work before the kernels on that stream are done with it.
     """
     import torch
     B, H, Nq, Nk, d = _check_qkv(q, k, v)
@@ -177,15 +228,14 @@ def fa_fwd_split(q, k, v, causal: bool = False, scale: float | None = None, n_sp
         scale = 1.0 / math.sqrt(d)
     if n_splits is None:
         n_splits = max(1, fa_split_hint(B, H, Nq, Nk, d, causal, code))
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    stream = _launch_stream(stream, q.device)
     need = fa_fwd_split_workspace(B, H, Nq, d, n_splits)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.stream(stream):
+        o, lse = _outputs_fwd(q, B, H, Nq, o, lse)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        else:
+            _check_workspace(workspace, max(need, 0), q.device)
     st = fa_fwd_split_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                           B, H, Nq, Nk, d, int(bool(causal)), scale, code, n_splits,
                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -203,16 +253,23 @@ def fa_merge(o_parts, lse_parts, dtype=None, o=None, lse=None, stream=None):
         raise TypeError("o_parts and lse_parts must be float32")
     if not (o_parts.is_cuda and lse_parts.is_cuda and o_parts.is_contiguous()
             and lse_parts.is_contiguous() and o_parts.dim() == 5
-            and lse_parts.shape == o_parts.shape[:4]):
-        raise ValueError("o_parts must be [P,B,H,Nq,d] and lse_parts [P,B,H,Nq], contiguous GPU")
+            and lse_parts.shape == o_parts.shape[:4] and lse_parts.device == o_parts.device):
+        raise ValueError("o_parts must be [P,B,H,Nq,d] and lse_parts [P,B,H,Nq], contiguous, "
+                         "on one GPU")
     P, B, H, Nq, d = o_parts.shape
-    dtype = dtype or torch.bfloat16
-    if o is None:
-        o = torch.empty((B, H, Nq, d), dtype=dtype, device=o_parts.device)
-    if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=o_parts.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(o_parts.device)
+    dev = o_parts.device
+    if dtype is None:
+        dtype = o.dtype if o is not None else torch.bfloat16
+    stream = _launch_stream(stream, dev)
+    with torch.cuda.stream(stream):
+        if o is None:
+            o = torch.empty((B, H, Nq, d), dtype=dtype, device=dev)
+        else:
+            _check_buf("o", o, (B, H, Nq, d), dtype, dev)
+        if lse is None:
+            lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+        else:
+            _check_buf("lse", lse, (B, H, Nq), torch.float32, dev)
     st = fa_merge_raw(o_parts.data_ptr(), lse_parts.data_ptr(), P, B, H, Nq, d, o.data_ptr(),
                       lse.data_ptr(), _dtype_code(o), stream.cuda_stream)
     if st != FA_OK:
@@ -220,27 +277,37 @@ def fa_merge(o_parts, lse_parts, dtype=None, o=None, lse=None, stream=None):
     return o, lse
 
 
+def _bwd_buffers(q, k, v, o, lse, dout, dq, dk, dv, workspace, stream):
+    """Checks and allocations shared by fa_bwd and fa_bwd_dropout."""
+    import torch
+    B, H, Nq, Nk, d = _check_qkv(q, k, v)
+    dev = q.device
+    _check_buf("o", o, q.shape, q.dtype, dev)
+    _check_buf("dout", dout, q.shape, q.dtype, dev)
+    _check_buf("lse", lse, (B, H, Nq), torch.float32, dev)
+    stream = _launch_stream(stream, dev)
+    need = fa_bwd_workspace(B, H, Nq, d)
+    with torch.cuda.stream(stream):
+        dq = torch.empty_like(q) if dq is None else _check_buf("dq", dq, q.shape, q.dtype, dev)
+        dk = torch.empty_like(k) if dk is None else _check_buf("dk", dk, k.shape, k.dtype, dev)
+        dv = torch.empty_like(v) if dv is None else _check_buf("dv", dv, v.shape, v.dtype, dev)
+        if workspace is None:
+            workspace = torch.empty(max(16, need), dtype=torch.uint8, device=dev)
+        else:
+            _check_workspace(workspace, max(need, 0), dev)
+    return (B, H, Nq, Nk, d), dq, dk, dv, workspace, stream
+
+
 def fa_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, dq=None,
            dk=None, dv=None, workspace=None, stream=None):
     """dQ, dK, dV of the attention forward (fa_bwd) from the forward's o and lse and the
     output gradient dout; the fp32 workspace for D = rowsum(dO o O) is allocated with
-    torch when not given."""
-    import torch
-    B, H, Nq, Nk, d = _check_qkv(q, k, v)
-    for name, t in (("o", o), ("dout", dout)):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous tensor shaped and typed like q")
+    torch (on the launch stream) when not given."""
+    (B, H, Nq, Nk, d), dq, dk, dv, workspace, stream = _bwd_buffers(
+        q, k, v, o, lse, dout, dq, dk, dv, workspace, stream)
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    if workspace is None:
-        workspace = torch.empty(max(16, fa_bwd_workspace(B, H, Nq, d)), dtype=torch.uint8,
-                                device=q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
     st = fa_bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                     dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Nq, Nk, d,
                     int(bool(causal)), scale, code, workspace.data_ptr(),
@@ -254,20 +321,18 @@ def fa_fwd(q, k, v, causal: bool = False, scale: float | None = None, o=None, ls
            stream=None):
     """O, L = attention forward of torch tensors q [B,H,Nq,d], k, v [B,H,Nk,d] on the GPU.
 
-    o and lse are allocated (torch) when not given.  The kernel is enqueued on
-    ``stream`` (default: torch's current stream) and the call returns at once.
+    o and lse are allocated (torch, on the launch stream) when not given.  The kernel
+    is enqueued on ``stream`` (default: torch's current stream) and the call returns
+    at once.
     """
     import torch
     B, H, Nq, Nk, d = _check_qkv(q, k, v)
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
+    stream = _launch_stream(stream, q.device)
+    with torch.cuda.stream(stream):
+        o, lse = _outputs_fwd(q, B, H, Nq, o, lse)
     st = fa_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H,
                     Nq, Nk, d, int(bool(causal)), scale, code, stream.cuda_stream)
     if st != FA_OK:
@@ -283,12 +348,9 @@ def fa_fwd_dropout(q, k, v, p_drop: float, seed: int, causal: bool = False,
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
+    stream = _launch_stream(stream, q.device)
+    with torch.cuda.stream(stream):
+        o, lse = _outputs_fwd(q, B, H, Nq, o, lse)
     st = fa_fwd_dropout_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                             lse.data_ptr(), B, H, Nq, Nk, d, bool(causal), scale, p_drop, seed,
                             code, stream.cuda_stream)
@@ -301,22 +363,11 @@ def fa_bwd_dropout(q, k, v, o, lse, dout, p_drop: float, seed: int, causal: bool
                    scale: float | None = None, dq=None, dk=None, dv=None, workspace=None,
                    stream=None):
     """fa_bwd with the dropout of fa_fwd_dropout (same p_drop and seed)."""
-    import torch
-    B, H, Nq, Nk, d = _check_qkv(q, k, v)
-    for name, t in (("o", o), ("dout", dout)):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous tensor shaped and typed like q")
+    (B, H, Nq, Nk, d), dq, dk, dv, workspace, stream = _bwd_buffers(
+        q, k, v, o, lse, dout, dq, dk, dv, workspace, stream)
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    if workspace is None:
-        workspace = torch.empty(max(16, fa_bwd_workspace(B, H, Nq, d)), dtype=torch.uint8,
-                                device=q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
     st = fa_bwd_dropout_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                             lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                             dv.data_ptr(), B, H, Nq, Nk, d, bool(causal), scale, p_drop, seed,

@@ -125,3 +125,33 @@ def test_concurrent_streams_match_serial():
         for outs in per_rep:
             for a, b in zip(outs, serial):
                 assert torch.equal(a, b)
+
+
+def test_explicit_stream_temporaries_are_not_reused_early():
+    """fa_fwd_split and fa_bwd given a stream other than torch's current one, with no
+    workspace: the binding allocates the workspace (and the outputs) on that stream, so
+    memory that the current stream allocates and overwrites right after the calls
+    return is never the workspace the kernels are still using.  Results must equal the
+    serial calls bit for bit."""
+    w = inputs.custom("side_stream", 2, 8, 1500, 3000, 128, "bf16", True, seed=93)
+    say(f"[side stream] {w.describe()}")
+    q, k, v = (to_dev(a, "bf16") for a in inputs.make_qkv(w))
+    gen = torch.Generator(device="cpu").manual_seed(94)
+    do = torch.randn(q.shape, generator=gen).to(torch.bfloat16).to(DEV)
+    o0, l0 = fa.fa_fwd(q, k, v, causal=True, scale=w.scale)
+    ref_split = fa.fa_fwd_split(q, k, v, causal=True, scale=w.scale, n_splits=4)
+    ref_bwd = fa.fa_bwd(q, k, v, o0, l0, do, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    ws_bytes = max(fa.fa_fwd_split_workspace(2, 8, 1500, 128, 4), fa.fa_bwd_workspace(2, 8, 1500, 128))
+    side = torch.cuda.Stream()
+    for rep in range(3):
+        side.wait_stream(torch.cuda.current_stream())
+        got_split = fa.fa_fwd_split(q, k, v, causal=True, scale=w.scale, n_splits=4, stream=side)
+        got_bwd = fa.fa_bwd(q, k, v, o0, l0, do, causal=True, scale=w.scale, stream=side)
+        # the current stream grabs and scribbles over freshly freed memory at once
+        junk = [torch.full((ws_bytes // 4 + 1,), float("nan"), device=DEV) for _ in range(4)]
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        del junk
+        for a, b in zip((*got_split, *got_bwd), (*ref_split, *ref_bwd)):
+            assert torch.equal(a, b), f"repeat {rep}: result differs from the serial call"
