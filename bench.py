@@ -187,7 +187,9 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         done = sel.stop
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "seconds": round(dt, 2),
+            "seconds": round(dt, 2), "threads_used": cores, "os_cpu_count": os.cpu_count(),
+            "affinity_cores": (len(os.sched_getaffinity(0))
+                               if hasattr(os, "sched_getaffinity") else None),
             "sample": (f"{done} of the {bh.size} rows of {w.name} (all heads), taken in a "
                        f"seeded random order until the {budget_s:g} s budget ran out; fp64 "
                        f"three-step oracle on {cores} threads; rate = 4*d*visible_keys per "

@@ -5,12 +5,12 @@ orders reach the plain definition for EVERY way of cutting queries and keys into
 contiguous blocks.  They are written from the algorithms' descriptions, in fp64
 numpy, one head at a time:
 
-* :func:`q_outer` — "05_flash_attention.py" course file, ``flash_attention_forward``:
-  per query block, state O~ = 0, m = -inf, l = 0; per key block (left to right,
-  skipping blocks wholly in the causal future), S = Q_i K_j^T * scale, mask,
-  m_new = max(m, rowmax S), P = exp(S - m_new), c = exp(m - m_new),
-  l = c l + rowsum P, O~ = c O~ + P V_j, m = m_new; finally O = O~ / l and
-  L = m + log l.
+* :func:`q_outer` — the order of the "05_flash_attention.py" course file's
+  ``flash_attention_forward``: per query block an empty running state, which absorbs
+  the key blocks left to right (skipping those wholly in the causal future) by the
+  running-softmax recurrence — the new maximum, the old sums carried over by
+  exp(old max - new max), the block's exponentials added — and finally O = o~ / d and
+  L = m + log d.  The state is the blog page's (m, d, o~) triple, one row per query.
 * :func:`kv_outer` — "Flash Attention" blog page, Algorithm 1: keys outside, queries
   inside; O, l, m live in "HBM" arrays and O is kept normalised after every step:
   m~ = rowmax S, P~ = exp(S - m~), l~ = rowsum P~, m_new = max(m, m~),
@@ -27,6 +27,7 @@ being visible to every query; Algorithm 1 with a mask needs the same guard).
 """
 from __future__ import annotations
 
+import functools
 import math
 
 import numpy as np
@@ -46,31 +47,51 @@ def _mask(s: np.ndarray, qs: int, ks: int, causal: bool) -> np.ndarray:
     return np.where(kj > qi, -np.inf, s)
 
 
+def _absorb(state: np.ndarray, s: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """One step of the running-softmax recurrence for a block of query rows.
+
+    state [rows, 2 + dim] holds (m, d, o~) per row: the largest score seen, the sum of
+    exp(score - m) and the value rows weighted by the same exponentials.  s [rows, keys]
+    are the block's scaled scores (-inf where masked), v [keys, dim] its value rows.
+    The new largest score m' = max(m, max s); the old sums are carried over by the
+    factor exp(m - m') and the block adds exp(s - m') and exp(s - m') v.  A row that
+    sees no key of the block keeps its state (so (-inf) - (-inf) never occurs)."""
+    m_old, d_old, o_old = state[:, 0], state[:, 1], state[:, 2:]
+    seen = np.isfinite(s).any(axis=1)
+    m_new = np.where(seen, np.maximum(m_old, s.max(axis=1)), m_old)
+    carry = np.where(np.isfinite(m_old), np.exp(m_old - np.where(seen, m_new, 0.0)), 0.0)
+    carry = np.where(seen, carry, 1.0)
+    w = np.where(seen[:, None], np.exp(s - np.where(seen, m_new, 0.0)[:, None]), 0.0)
+    out = np.empty_like(state)
+    out[:, 0] = m_new
+    out[:, 1] = carry * d_old + w.sum(axis=1)
+    out[:, 2:] = carry[:, None] * o_old + w @ v
+    return out
+
+
 def q_outer(Q, K, V, causal: bool, scale: float, q_cuts=(), k_cuts=()):
-    """Course-file order: query blocks outside, key blocks inside, state on chip."""
+    """Course-file order: query blocks outside, key blocks inside, state on chip.
+
+    Each query block starts from the empty state (m = -inf, d = 0, o~ = 0) and absorbs
+    the key blocks left to right (:func:`_absorb`); with the causal mask, key blocks
+    that start after the block's last query hold no visible key and are not visited.
+    At the end O = o~ / d and L = m + log d."""
     Q, K, V = (np.asarray(a, dtype=np.float64) for a in (Q, K, V))
-    n, d = Q.shape
-    m_total = K.shape[0]
-    O = np.zeros((n, d))
-    L = np.zeros(n)
-    for qs, qe in _bounds(n, q_cuts):
-        Oi = np.zeros((qe - qs, d))
-        mi = np.full(qe - qs, -np.inf)
-        li = np.zeros(qe - qs)
-        for ks, ke in _bounds(m_total, k_cuts):
-            if causal and ks > qe - 1:
-                break  # the whole key block lies in the future of every query here
-            S = _mask(Q[qs:qe] @ K[ks:ke].T * scale, qs, ks, causal)
-            live = np.isfinite(S.max(axis=1))  # rows with at least one visible key
-            m_new = np.where(live, np.maximum(mi, S.max(axis=1)), mi)
-            P = np.where(live[:, None], np.exp(S - m_new[:, None]), 0.0)
-            c = np.where(live & np.isfinite(mi), np.exp(mi - m_new), np.where(live, 0.0, 1.0))
-            li = c * li + P.sum(axis=1)
-            Oi = c[:, None] * Oi + P @ V[ks:ke]
-            mi = m_new
-        O[qs:qe] = Oi / li[:, None]
-        L[qs:qe] = mi + np.log(li)
-    return O, L
+    n, dim = Q.shape
+    key_blocks = _bounds(K.shape[0], k_cuts)
+    out = np.empty((n, dim))
+    lse = np.empty(n)
+    for lo, hi in _bounds(n, q_cuts):
+        state = np.zeros((hi - lo, 2 + dim))
+        state[:, 0] = -np.inf
+        todo = [(a, b) for a, b in key_blocks if not (causal and a >= hi)]
+        state = functools.reduce(
+            lambda st, kb: _absorb(st, _mask(Q[lo:hi] @ K[kb[0]:kb[1]].T * scale, lo, kb[0],
+                                             causal), V[kb[0]:kb[1]]),
+            todo, state)
+        out[lo:hi] = state[:, 2:] / state[:, 1:2]
+        lse[lo:hi] = state[:, 0] + np.log(state[:, 1])
+    return out, lse
 
 
 def kv_outer(Q, K, V, causal: bool, scale: float, q_cuts=(), k_cuts=()):
