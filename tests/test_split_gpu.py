@@ -217,6 +217,13 @@ def test_split_invalid_arguments_raise():
     with pytest.raises(fa.FAError):
         fa.fa_fwd_split(q, k, v, n_splits=257)
     small = torch.empty(64, dtype=torch.uint8, device=DEV)
-    with pytest.raises(fa.FAError):
+    with pytest.raises(ValueError):   # the binding checks the workspace's size first
         fa.fa_fwd_split(q, k, v, n_splits=4, workspace=small)
+    # and the library refuses it too, when called directly with the true size
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 2, 128), dtype=torch.float32, device=DEV)
+    st = fa.fa_fwd_split_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                             1, 2, 128, 1024, 64, 0, w.scale, fa.FA_DTYPE_BF16, 4,
+                             small.data_ptr(), small.numel(), torch.cuda.current_stream().cuda_stream)
+    assert st == fa.FA_ERR_INVALID_ARG
     torch.cuda.synchronize()
