@@ -14,12 +14,13 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfa.so")
 
 FA_DTYPE_F32, FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1, 2
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH = 0, 1, 2, 3
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH, FA_ERR_SCRATCH = 0, 1, 2, 3, 4
+FA_STATIC_SCRATCH_BYTES = 64 << 20  # include/fa.h
 
 # symbols include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_fwd_split", "fa_fwd_split_workspace", "fa_merge", "fa_split_hint",
-           "fa_bwd", "fa_bwd_workspace", "fa_fwd_dropout", "fa_bwd_dropout", "fa_status_str",
-           "fa_tile_rows")
+EXPORTS = ("fa_fwd", "fa_fwd_split", "fa_fwd_split_workspace", "fa_fwd_split_static", "fa_merge",
+           "fa_split_hint", "fa_bwd", "fa_bwd_workspace", "fa_fwd_dropout", "fa_bwd_dropout",
+           "fa_status_str", "fa_tile_rows")
 
 _lib = None
 
@@ -50,6 +51,8 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_split.argtypes = L.fa_fwd.argtypes[:-1] + [ctypes.c_int, ctypes.c_void_p, i64,
                                                             ctypes.c_void_p]
         L.fa_fwd_split.restype = ctypes.c_int
+        L.fa_fwd_split_static.argtypes = L.fa_fwd.argtypes[:-1] + [ctypes.c_int, ctypes.c_void_p]
+        L.fa_fwd_split_static.restype = ctypes.c_int
         L.fa_fwd_split_workspace.argtypes = [i64, i64, i64, i64, ctypes.c_int]
         L.fa_fwd_split_workspace.restype = i64
         L.fa_merge.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, i64, i64, i64, i64,
@@ -93,6 +96,15 @@ def fa_fwd_split_raw(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N
     """Direct call of fa_fwd_split with integer device pointers; returns the status code."""
     return lib().fa_fwd_split(q, k, v, o, lse, B, H, Nq, Nk, d, int(causal), float(scale),
                               int(dtype), int(n_splits), workspace, int(workspace_bytes), stream)
+
+
+def fa_fwd_split_static_raw(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int,
+                            Nk: int, d: int, causal: int, scale: float, dtype: int, n_splits: int,
+                            stream: int) -> int:
+    """Direct call of fa_fwd_split_static (no workspace, nothing allocated); returns the
+    status code."""
+    return lib().fa_fwd_split_static(q, k, v, o, lse, B, H, Nq, Nk, d, int(causal), float(scale),
+                                     int(dtype), int(n_splits), stream)
 
 
 def fa_merge_raw(o_parts: int, lse_parts: int, n_parts: int, B: int, H: int, Nq: int, d: int,

@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/fa.h"
@@ -314,6 +316,45 @@ extern "C" int64_t fa_fwd_split_workspace(int64_t B, int64_t H, int64_t Nq, int6
     return round_up((int64_t)n_splits * rows * d * 4, kAlign) + (int64_t)n_splits * rows * 4;
 }
 
+namespace {
+
+// The body of fa_fwd_split once the arguments are valid: the unsplit kernel when one
+// key range results, else the split kernels into the partials at `workspace` (which
+// must hold fa_fwd_split_workspace(...) bytes) and the merge.
+fa_status_t split_launch(fa_dtype_t dtype, const Launch& L, const void* q, const void* k,
+                         const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t Nq,
+                         int64_t Nk, int64_t d, int causal, float scale, int n_splits, int s_eff,
+                         int tps, void* workspace, hipStream_t hs)
+{
+    if (s_eff == 1) {  // one range: the unsplit kernel writes o and lse directly
+        Launch L1;
+        pick(dtype, d, causal, false, &L1);
+        const hipError_t err = launch_fwd_any(dtype, L1, q, k, v, o, lse, nullptr, nullptr, B * H,
+                                              Nq, Nk, 1, 0, scale, hs);
+        return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    }
+    const int64_t rows = B * H * Nq;
+    float* o_part = static_cast<float*>(workspace);
+    float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                               round_up((int64_t)n_splits * rows * d * 4, kAlign));
+    hipError_t err = launch_fwd_any(dtype, L, q, k, v, nullptr, nullptr, o_part, lse_part, B * H,
+                                    Nq, Nk, s_eff, tps, scale, hs);
+    if (err != hipSuccess)
+        return FA_ERR_LAUNCH;
+    err = launch_merge(dtype, d, o_part, lse_part, s_eff, rows, o, lse, hs);
+    return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+// Grid limits of the split kernels and the merge for s_eff ranges.
+bool split_fits(const Launch& L, int64_t B, int64_t H, int64_t Nq, int s_eff)
+{
+    const int64_t rows = B * H * Nq;
+    return (int64_t)s_eff * ((Nq + L.rows - 1) / L.rows) * B * H <= INT32_MAX &&
+           (rows + 7) / 8 <= INT32_MAX;
+}
+
+}  // namespace
+
 extern "C" fa_status_t fa_fwd_split(const void* q, const void* k, const void* v, void* o,
                                     float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
                                     int64_t d, int causal, float scale, fa_dtype_t dtype,
@@ -330,30 +371,80 @@ extern "C" fa_status_t fa_fwd_split(const void* q, const void* k, const void* v,
         return st;
     int tps;
     const int s_eff = split_plan(Nk, n_splits, &tps);
-    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    if (s_eff == 1) {  // one range: the unsplit kernel writes o and lse directly
-        Launch L1;
-        pick(dtype, d, causal, false, &L1);
-        const hipError_t err = launch_fwd_any(dtype, L1, q, k, v, o, lse, nullptr, nullptr, B * H,
-                                              Nq, Nk, 1, 0, scale, hs);
-        return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    if (s_eff > 1) {
+        const int64_t need = fa_fwd_split_workspace(B, H, Nq, d, n_splits);
+        if (!workspace || !aligned(workspace, 16) || workspace_bytes < need)
+            return FA_ERR_INVALID_ARG;
+        if (!split_fits(L, B, H, Nq, s_eff))
+            return FA_ERR_INVALID_ARG;
     }
-    const int64_t need = fa_fwd_split_workspace(B, H, Nq, d, n_splits);
-    if (!workspace || !aligned(workspace, 16) || workspace_bytes < need)
-        return FA_ERR_INVALID_ARG;
-    const int64_t rows = B * H * Nq;
-    if ((int64_t)s_eff * ((Nq + L.rows - 1) / L.rows) * B * H > INT32_MAX ||
-        (rows + 7) / 8 > INT32_MAX)
-        return FA_ERR_INVALID_ARG;
-    float* o_part = static_cast<float*>(workspace);
-    float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                               round_up((int64_t)n_splits * rows * d * 4, kAlign));
-    hipError_t err = launch_fwd_any(dtype, L, q, k, v, nullptr, nullptr, o_part, lse_part, B * H,
-                                    Nq, Nk, s_eff, tps, scale, hs);
+    return split_launch(dtype, L, q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, n_splits,
+                        s_eff, tps, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+// ---- fa_fwd_split_static: the partials in a static device array ------------
+
+// The scratch of fa_fwd_split_static.  Each GPU holds its own copy of the array, at an
+// address only the runtime knows: host code never uses this name as an address (it is
+// a host-side stand-in there), only the per-device address looked up below.
+static __device__ __align__(256) char scratch[FA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];  // device address of `scratch`, per device id
+
+// Device address of the current GPU's copy of `scratch`, looked up on the first call
+// with that GPU current and kept for later calls.
+hipError_t scratch_address(void** out)
+{
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess)
-        return FA_ERR_LAUNCH;
-    err = launch_merge(dtype, d, o_part, lse_part, s_eff, rows, o, lse, hs);
-    return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+        return err;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess || !p)
+            return err != hipSuccess ? err : hipErrorInvalidSymbol;
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" fa_status_t fa_fwd_split_static(const void* q, const void* k, const void* v, void* o,
+                                           float* lse, int64_t B, int64_t H, int64_t Nq,
+                                           int64_t Nk, int64_t d, int causal, float scale,
+                                           fa_dtype_t dtype, int n_splits, fa_stream_t stream)
+{
+    if (n_splits < 1 || n_splits > kMaxSplits)
+        return FA_ERR_INVALID_ARG;
+    Launch L;
+    bool empty;
+    const fa_status_t st =
+        check_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, true, &L, &empty);
+    if (st != FA_OK || empty)
+        return st;
+    int tps;
+    const int s_eff = split_plan(Nk, n_splits, &tps);
+    void* ws = nullptr;
+    if (s_eff > 1) {
+        if (fa_fwd_split_workspace(B, H, Nq, d, n_splits) > FA_STATIC_SCRATCH_BYTES)
+            return FA_ERR_SCRATCH;
+        if (!split_fits(L, B, H, Nq, s_eff))
+            return FA_ERR_INVALID_ARG;
+        if (scratch_address(&ws) != hipSuccess)
+            return FA_ERR_LAUNCH;
+    }
+    return split_launch(dtype, L, q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, n_splits,
+                        s_eff, tps, ws, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" fa_status_t fa_merge(const float* o_parts, const float* lse_parts, int n_parts,
@@ -575,6 +666,7 @@ extern "C" const char* fa_status_str(fa_status_t status)
     case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH";
+    case FA_ERR_SCRATCH: return "FA_ERR_SCRATCH";
     }
     return "FA_ERR_UNKNOWN";
 }

@@ -42,7 +42,9 @@ typedef enum {
     FA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative size, Nk = 0 with queries,
                                non-positive or non-finite scale, unknown dtype, size limit */
     FA_ERR_UNSUPPORTED = 2, /* head size d outside {64, 128} */
-    FA_ERR_LAUNCH = 3       /* the HIP runtime rejected the kernel launch */
+    FA_ERR_LAUNCH = 3,      /* the HIP runtime rejected the kernel launch */
+    FA_ERR_SCRATCH = 4      /* fa_fwd_split_static: the problem needs more scratch than
+                               FA_STATIC_SCRATCH_BYTES */
 } fa_status_t;
 
 /* hipStream_t without the HIP headers: pass the stream handle (0 = default stream). */
@@ -128,6 +130,33 @@ fa_status_t fa_fwd_split(const void* q, const void* k, const void* v, void* o, f
 /* Workspace bytes fa_fwd_split needs for (B, H, Nq, d, n_splits); -1 for arguments
  * it would reject (negative sizes, d outside {64, 128}, n_splits outside 1 .. 256). */
 int64_t fa_fwd_split_workspace(int64_t B, int64_t H, int64_t Nq, int64_t d, int n_splits);
+
+/* Size of the library's static scratch buffer (fa_fwd_split_static), per GPU. */
+#define FA_STATIC_SCRATCH_BYTES (64LL << 20)
+
+/*
+ * fa_fwd_split_static — fa_fwd_split without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory: code being captured
+ * into a HIP graph, tight serving loops, harnesses that forbid hipMalloc.  The partial
+ * states live in a static device array of FA_STATIC_SCRATCH_BYTES (64 MiB) that the
+ * library holds on every GPU it runs on until the process ends; its address on a GPU
+ * is looked up once, on the first call with that GPU current.
+ *
+ * Arguments, result and behaviour as fa_fwd_split (same kernels, same bits), with the
+ * workspace replaced by that array.  The problem must fit it:
+ * fa_fwd_split_workspace(B, H, Nq, d, n_splits) <= FA_STATIC_SCRATCH_BYTES when more
+ * than one key range results, else FA_ERR_SCRATCH (before any HIP call).  Every call
+ * on one GPU shares that GPU's array: calls that overlap on one GPU (on concurrent
+ * streams, or before the previous call's kernels have finished on another stream)
+ * race and give wrong results; calls in order on one stream are safe.  The array
+ * keeps the last call's partials; nothing in it needs to start at zero (every partial
+ * the merge reads is written first by the same call).  FA_ERR_LAUNCH if the array's
+ * address cannot be obtained on the current GPU.
+ */
+fa_status_t fa_fwd_split_static(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                int causal, float scale, fa_dtype_t dtype, int n_splits,
+                                fa_stream_t stream);
 
 /*
  * fa_merge — fold partial attention states over disjoint key ranges into the final

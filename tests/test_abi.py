@@ -279,3 +279,32 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         binding.lib()
+
+
+def _split_static(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Nq=64, Nk=640, d=128, causal=0, scale=0.125,
+             dtype=fa.FA_DTYPE_BF16, n_splits=4, stream=0)
+    a.update(kw)
+    return fa.fa_fwd_split_static_raw(**a)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(n_splits=0), fa.FA_ERR_INVALID_ARG),
+    (dict(n_splits=257), fa.FA_ERR_INVALID_ARG),
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(o=P + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=0), fa.FA_OK),
+    # partials of 64 x 16 x 4096 rows x 128 x 4 B x 2 ranges = 1 GiB: beyond the array
+    (dict(B=64, H=16, Nq=4096, Nk=128, n_splits=2), fa.FA_ERR_SCRATCH),
+])
+def test_split_static_validation_before_any_hip_call(kw, want):
+    assert _split_static(**kw) == want
+
+
+def test_split_static_limit_matches_header():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    m = re.search(r"#define FA_STATIC_SCRATCH_BYTES \((\d+)LL << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.FA_STATIC_SCRATCH_BYTES
+    assert fa.fa_status_str(fa.FA_ERR_SCRATCH) == "FA_ERR_SCRATCH"
