@@ -223,3 +223,57 @@ def custom(name: str, B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, caus
            seed: int, sigma_q: float = 1.0, sigma_k: float = 1.0,
            sigma_v: float = 1.0) -> Workload:
     return Workload(name, B, H, Nq, Nk, d, dtype, causal, sigma_q, sigma_k, sigma_v, seed)
+
+
+# ---------------------------------------------------------------------------
+# caller masks: seeded boolean patterns and their bit-packed form
+# ---------------------------------------------------------------------------
+
+MASK_KINDS = ("random", "key_padding", "sliding_window", "block", "empty_rows")
+
+
+def pack_mask(visible: np.ndarray) -> np.ndarray:
+    """Boolean [..., Nq, Nk] (True = key visible) -> uint32 words [..., Nq, ceil(Nk/32)]
+    with key k in bit k % 32 of word k // 32 (bits past Nk are 0)."""
+    vis = np.asarray(visible, dtype=bool)
+    nk = vis.shape[-1]
+    w = -(-nk // 32)
+    pad = np.zeros(vis.shape[:-1] + (w * 32,), dtype=bool)
+    pad[..., :nk] = vis
+    bits = pad.reshape(vis.shape[:-1] + (w, 32)).astype(np.uint64)
+    weights = (np.uint64(1) << np.arange(32, dtype=np.uint64))
+    return (bits * weights).sum(axis=-1).astype(np.uint32)
+
+
+def make_mask(kind: str, mask_b: int, mask_h: int, Nq: int, Nk: int, seed: int,
+              density: float = 0.5, window: int = 100, tile: int = 64) -> np.ndarray:
+    """A seeded boolean mask [mask_b, mask_h, Nq, Nk] (True = visible):
+
+    * random:         each (q, k) visible with probability `density`;
+    * key_padding:    per batch a valid key count drawn in [Nk/4, Nk]; keys past it hidden
+                      (the same for every head and query);
+    * sliding_window: key k visible to query q iff |q - k| <= window;
+    * block:          tile x tile blocks, each wholly visible with probability `density`;
+    * empty_rows:     random, and about one row in eight with no visible key.
+    """
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), 77])))
+    shape = (mask_b, mask_h, Nq, Nk)
+    if kind == "random":
+        return rng.random(shape) < density
+    if kind == "key_padding":
+        valid = rng.integers(max(1, Nk // 4), Nk + 1, size=mask_b)
+        vis = np.arange(Nk)[None, :] < valid[:, None]
+        return np.broadcast_to(vis[:, None, None, :], shape).copy()
+    if kind == "sliding_window":
+        q = np.arange(Nq)[:, None]
+        k = np.arange(Nk)[None, :]
+        return np.broadcast_to(np.abs(q - k) <= window, shape).copy()
+    if kind == "block":
+        tb = rng.random((mask_b, mask_h, -(-Nq // tile), -(-Nk // tile))) < density
+        vis = np.repeat(np.repeat(tb, tile, axis=2), tile, axis=3)
+        return vis[:, :, :Nq, :Nk].copy()
+    if kind == "empty_rows":
+        vis = rng.random(shape) < density
+        vis[rng.random(shape[:3]) < 0.125] = False
+        return vis
+    raise ValueError(kind)

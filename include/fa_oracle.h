@@ -204,6 +204,47 @@ int fa_ref_bwd_head_dropout_f64(const void* q, const void* k, const void* v, con
                                 int causal, float scale, int dtype, int t, uint64_t seed,
                                 int64_t bh, double* dq64, double* dk64, double* dv64);
 
+/*
+ * Part 5: caller masks (blog page "Flash Attention", Algorithm 2: S_masked = mask(S),
+ * P = softmax(S_masked); Algorithm 4 recomputes P from mask(S)).  Reading: mask(S)
+ * sets S[q, k] to -inf where the caller's boolean mask is false (after the causal rule
+ * when causal = 1: both must allow the key).  A query row's mask is bit-packed: key k
+ * in bit k % 32 of 32-bit word k / 32, set = visible; one row holds W = ceil(Nk / 32)
+ * words.  A row with no visible key has no softmax; the reading taken: O = 0 and
+ * L = -inf (the identity of the (+) merge), P = 0 in the gradients.
+ *
+ * mask_rows of the double-array forms: [nq, W] words for the one head.  mask of the
+ * raw-buffer forms: [mask_b, mask_h, Nq, W] words with mask_b in {1, B} and mask_h in
+ * {1, H} (an extent of 1 is shared by every batch / head).
+ */
+int fa_oracle_attention_masked_f64(const double* q, const double* k, const double* v,
+                                   const uint32_t* mask_rows, int64_t nq, int64_t nk, int64_t d,
+                                   int causal, double scale, int64_t n_rows, const int64_t* rows,
+                                   double* o, double* lse);
+int fa_oracle_online_masked_f64(const double* q, const double* k, const double* v,
+                                const uint32_t* mask_rows, int64_t nq, int64_t nk, int64_t d,
+                                int causal, double scale, int64_t key_block, int64_t n_rows,
+                                const int64_t* rows, double* o, double* lse);
+int fa_oracle_attention_bwd_masked_f64(const double* q, const double* k, const double* v,
+                                       const double* dout, const uint32_t* mask_rows, int64_t nq,
+                                       int64_t nk, int64_t d, int causal, double scale,
+                                       double* dq, double* dk, double* dv);
+int fa_ref_rows_masked_f64(const void* q, const void* k, const void* v, const uint32_t* mask,
+                           int64_t mask_b, int64_t mask_h, int64_t B, int64_t H, int64_t Nq,
+                           int64_t Nk, int64_t d, int causal, float scale, int dtype,
+                           int64_t n_sel, const int64_t* sel_bh, const int64_t* sel_row,
+                           double* o64, double* lse64);
+int fa_ref_online_masked_f64(const void* q, const void* k, const void* v, const uint32_t* mask,
+                             int64_t mask_b, int64_t mask_h, int64_t B, int64_t H, int64_t Nq,
+                             int64_t Nk, int64_t d, int causal, float scale, int dtype,
+                             int64_t n_sel, const int64_t* sel_bh, const int64_t* sel_row,
+                             int64_t key_block, double* o64, double* lse64);
+int fa_ref_bwd_head_masked_f64(const void* q, const void* k, const void* v, const void* dout,
+                               const uint32_t* mask, int64_t mask_b, int64_t mask_h, int64_t B,
+                               int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                               float scale, int dtype, int64_t bh, double* dq64, double* dk64,
+                               double* dv64);
+
 /* Whole-tensor host counterpart of the GPU backward: part 3 on every head, the
  * gradients rounded from fp64 to `dtype` (nearest-even) into dq, dk, dv. */
 int fa_bwd_ref(const void* q, const void* k, const void* v, const void* dout, void* dq,

@@ -21,6 +21,9 @@ What is computed, and where it comes from (pages named by title / address):
 * part 4, ``philox4x32_10`` / ``*_dropout_*``: dropout on P (blog page, Algorithms 2
   and 4) with Philox4x32-10 random numbers (Salmon et al., SC'11), the reading taken
   for the generator the pages leave open.
+* part 5, ``*_masked_*``: a caller's boolean mask on the scores (blog page,
+  Algorithm 2, S_masked = mask(S), and Algorithm 4), bit-packed per query row; a
+  row with no visible key gives O = 0 and L = -inf.
 * ``softmax_online``: the one-dimensional online softmax with a per-block trace —
   course file ``online_softmax_stats``; the worked example of
   "手写 Flash Attention" (bjdmk.com.cn) section 2.2 is pinned against it.
@@ -61,6 +64,7 @@ _i64 = ctypes.c_int64
 _dp = ctypes.POINTER(ctypes.c_double)
 _lp = ctypes.POINTER(ctypes.c_int64)
 _vp = ctypes.c_void_p
+_u32p = ctypes.POINTER(ctypes.c_uint32)
 
 
 def load(path: str = _LIB_PATH) -> ctypes.CDLL:
@@ -108,6 +112,26 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
                                             _dp]
     lib.fa_ref_bwd_head_dropout_f64.argtypes = raw4 + [ctypes.c_int, ctypes.c_uint64, _i64, _dp,
                                                        _dp, _dp]
+    lib.fa_oracle_attention_masked_f64.argtypes = [_dp, _dp, _dp, u32p, _i64, _i64, _i64,
+                                                   ctypes.c_int, ctypes.c_double, _i64, _lp, _dp,
+                                                   _dp]
+    lib.fa_oracle_online_masked_f64.argtypes = [_dp, _dp, _dp, u32p, _i64, _i64, _i64,
+                                                ctypes.c_int, ctypes.c_double, _i64, _i64, _lp,
+                                                _dp, _dp]
+    lib.fa_oracle_attention_bwd_masked_f64.argtypes = [_dp, _dp, _dp, _dp, u32p, _i64, _i64,
+                                                       _i64, ctypes.c_int, ctypes.c_double, _dp,
+                                                       _dp, _dp]
+    rawm = [_vp, _vp, _vp, u32p, _i64, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
+            ctypes.c_float, ctypes.c_int]
+    lib.fa_ref_rows_masked_f64.argtypes = rawm + [_i64, _lp, _lp, _dp, _dp]
+    lib.fa_ref_online_masked_f64.argtypes = rawm + [_i64, _lp, _lp, _i64, _dp, _dp]
+    lib.fa_ref_bwd_head_masked_f64.argtypes = [_vp, _vp, _vp, _vp, u32p, _i64, _i64, _i64, _i64,
+                                               _i64, _i64, _i64, ctypes.c_int, ctypes.c_float,
+                                               ctypes.c_int, _i64, _dp, _dp, _dp]
+    for name in ("fa_oracle_attention_masked_f64", "fa_oracle_online_masked_f64",
+                 "fa_oracle_attention_bwd_masked_f64", "fa_ref_rows_masked_f64",
+                 "fa_ref_online_masked_f64", "fa_ref_bwd_head_masked_f64"):
+        getattr(lib, name).restype = ctypes.c_int
     for name in ("fa_oracle_philox4x32_10", "fa_oracle_dropout_keep",
                  "fa_oracle_attention_dropout_f64", "fa_oracle_attention_bwd_dropout_f64",
                  "fa_ref_rows_dropout_f64", "fa_ref_bwd_head_dropout_f64"):
@@ -285,6 +309,127 @@ def ref_rows_f64(q, k, v, causal: bool, scale: float, dtype: str, sel_bh, sel_ro
     if online_key_block is None:
         return o, lse
     return o, lse, raised
+
+
+# ---------------------------------------------------------------------------
+# caller masks (part 5): bit-packed rows, key k in bit k % 32 of word k // 32
+# ---------------------------------------------------------------------------
+
+def _mask_words(mask) -> np.ndarray:
+    m = np.ascontiguousarray(mask)
+    if m.dtype != np.uint32:
+        raise TypeError("mask words must be uint32")
+    return m
+
+
+def attention_masked_f64(q, k, v, mask_rows, causal: bool, scale: float, rows=None, L=None):
+    """Part 1 with a caller mask on one head: mask_rows [nq, ceil(nk/32)] uint32 words.
+    A row with no visible key gives O = 0 and L = -inf."""
+    L = L or lib()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    nq, d = q.shape
+    nk = k.shape[0]
+    m = _mask_words(mask_rows)
+    assert m.shape == (nq, -(-nk // 32))
+    rows = np.arange(nq, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
+    o = np.empty((rows.size, d))
+    lse = np.empty(rows.size)
+    _check(L.fa_oracle_attention_masked_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(m, _u32p), nq, nk,
+                                            d, int(causal), float(scale), rows.size,
+                                            _ptr(rows, _lp), _ptr(o), _ptr(lse)),
+           "fa_oracle_attention_masked_f64")
+    return o, lse
+
+
+def online_masked_f64(q, k, v, mask_rows, causal: bool, scale: float, key_block: int = 0,
+                      rows=None, L=None):
+    """Part 2 with a caller mask on one head; returns (o, lse)."""
+    L = L or lib()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    nq, d = q.shape
+    nk = k.shape[0]
+    m = _mask_words(mask_rows)
+    assert m.shape == (nq, -(-nk // 32))
+    rows = np.arange(nq, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
+    o = np.empty((rows.size, d))
+    lse = np.empty(rows.size)
+    _check(L.fa_oracle_online_masked_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(m, _u32p), nq, nk, d,
+                                         int(causal), float(scale), int(key_block), rows.size,
+                                         _ptr(rows, _lp), _ptr(o), _ptr(lse)),
+           "fa_oracle_online_masked_f64")
+    return o, lse
+
+
+def attention_bwd_masked_f64(q, k, v, dout, mask_rows, causal: bool, scale: float, L=None):
+    """Part 3 with a caller mask on one head; returns (dq, dk, dv)."""
+    L = L or lib()
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    nq, d = q.shape
+    nk = k.shape[0]
+    m = _mask_words(mask_rows)
+    assert m.shape == (nq, -(-nk // 32))
+    dq, dk, dv = np.empty((nq, d)), np.empty((nk, d)), np.empty((nk, d))
+    _check(L.fa_oracle_attention_bwd_masked_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                                _ptr(m, _u32p), nq, nk, d, int(causal),
+                                                float(scale), _ptr(dq), _ptr(dk), _ptr(dv)),
+           "fa_oracle_attention_bwd_masked_f64")
+    return dq, dk, dv
+
+
+def ref_rows_masked_f64(q, k, v, mask, causal: bool, scale: float, dtype: str, sel_bh, sel_row,
+                        threads: int | None = None, online_key_block: int | None = None, L=None):
+    """ref_rows_f64 with a caller mask [mask_b, mask_h, Nq, ceil(Nk/32)] uint32 words
+    (mask_b in {1, B}, mask_h in {1, H}); part 2 when online_key_block is given.
+    Returns (o64 [n_sel, d], lse64 [n_sel])."""
+    L = L or lib()
+    q, k, v = _raw(q, dtype), _raw(k, dtype), _raw(v, dtype)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    m = _mask_words(mask)
+    mb, mh = m.shape[0], m.shape[1]
+    assert m.shape[2:] == (Nq, -(-Nk // 32))
+    sel_bh = np.ascontiguousarray(sel_bh, np.int64)
+    sel_row = np.ascontiguousarray(sel_row, np.int64)
+    n = sel_bh.size
+    o = np.empty((n, d))
+    lse = np.empty(n)
+    code = DTYPE_CODES[dtype]
+
+    def work(span):
+        a, b = span
+        if b <= a:
+            return 0
+        bh, rw = sel_bh[a:b], sel_row[a:b]
+        if online_key_block is None:
+            return L.fa_ref_rows_masked_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                            _ptr(m, _u32p), mb, mh, B, H, Nq, Nk, d, int(causal),
+                                            float(scale), code, b - a, _ptr(bh, _lp),
+                                            _ptr(rw, _lp), _ptr(o[a:b]), _ptr(lse[a:b]))
+        return L.fa_ref_online_masked_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                          _ptr(m, _u32p), mb, mh, B, H, Nq, Nk, d, int(causal),
+                                          float(scale), code, b - a, _ptr(bh, _lp),
+                                          _ptr(rw, _lp), int(online_key_block), _ptr(o[a:b]),
+                                          _ptr(lse[a:b]))
+
+    for rc in _threaded(n, threads, work):
+        _check(rc, "fa_ref_rows_masked_f64")
+    return o, lse
+
+
+def bwd_head_masked_f64(q, k, v, dout, mask, causal: bool, scale: float, dtype: str, bh: int,
+                        L=None):
+    """Part 3 with a caller mask on head bh of raw buffers; returns fp64 (dq, dk, dv)."""
+    L = L or lib()
+    q, k, v, dout, B, H, Nq, Nk, d = _raw4(q, k, v, dout, dtype)
+    m = _mask_words(mask)
+    assert m.shape[2:] == (Nq, -(-Nk // 32))
+    dq, dk, dv = np.empty((Nq, d)), np.empty((Nk, d)), np.empty((Nk, d))
+    _check(L.fa_ref_bwd_head_masked_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                        dout.ctypes.data, _ptr(m, _u32p), m.shape[0], m.shape[1],
+                                        B, H, Nq, Nk, d, int(causal), float(scale),
+                                        DTYPE_CODES[dtype], int(bh), _ptr(dq), _ptr(dk),
+                                        _ptr(dv)), "fa_ref_bwd_head_masked_f64")
+    return dq, dk, dv
 
 
 # ---------------------------------------------------------------------------

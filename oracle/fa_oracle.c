@@ -22,6 +22,8 @@
  *   [D] Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
  *       easy as 1, 2, 3", SC'11): the random numbers of dropout, which [B] leaves
  *       unspecified.
+ * Parts: 1 three-step attention, 2 the online accumulator and (+), 3 gradients,
+ * 4 dropout, 5 caller masks (threaded through parts 1-3 as an optional mask row).
  *
  * Readings where the pages are silent are listed beside the code that takes them.
  */
@@ -254,11 +256,30 @@ int fa_oracle_dropout_keep(uint64_t seed, int t, int64_t bh, int64_t nq, int64_t
 /* Part 1: standard three-step attention, one row  [A] standard_attention     */
 /* ------------------------------------------------------------------------- */
 
-/* score of query row r against key kk: scale * sum_t q[t] k[t], or -inf if masked */
+/* ------------------------------------------------------------------------- */
+/* Caller masks  [B] Algorithm 2 (S_masked = mask(S), P = softmax(S_masked)) and  */
+/*   Algorithm 4 (the backward recomputes P from mask(S)).  Reading: mask(S)   */
+/*   sets S[q, k] to -inf where the caller's boolean mask is false, as the     */
+/*   course page's masked_fill does for its causal mask; the mask of one query */
+/*   row is bit-packed, key k in bit k % 32 of 32-bit word k / 32 (bit set =   */
+/*   visible).  A row with no visible key has no softmax: the reading taken is */
+/*   O = 0 and L = -inf (the identity of the (+) merge), P = 0 in the backward.*/
+/* ------------------------------------------------------------------------- */
+
+/* is key kk visible in the caller's mask row mrow (NULL: no caller mask)? */
+static int mask_visible(const uint32_t* mrow, int64_t kk)
+{
+    return !mrow || ((mrow[kk / 32] >> (kk % 32)) & 1u);
+}
+
+/* score of query row r against key kk: scale * sum_t q[t] k[t], or -inf if masked
+ * (causal rule, then the caller's mask row mrow when given) */
 static double score(const double* q_row, const double* k_row, int64_t d, double scale,
-                    int causal, int64_t r, int64_t kk)
+                    int causal, int64_t r, int64_t kk, const uint32_t* mrow)
 {
     if (causal && kk > r)
+        return -INFINITY;
+    if (!mask_visible(mrow, kk))
         return -INFINITY;
     double dot = 0.0;
     for (int64_t t = 0; t < d; ++t)
@@ -269,17 +290,23 @@ static double score(const double* q_row, const double* k_row, int64_t d, double 
 /* s is caller scratch of nk doubles */
 static void three_step_row(const double* q_row, const double* k, const double* v, int64_t nk,
                            int64_t d, int causal, double scale, int64_t r, double* s,
-                           double* o_row, double* lse, const Drop* dr)
+                           double* o_row, double* lse, const Drop* dr, const uint32_t* mrow)
 {
     /* step 1: materialise the score row S[r, :] */
     for (int64_t kk = 0; kk < nk; ++kk)
-        s[kk] = score(q_row, k + kk * d, d, scale, causal, r, kk);
+        s[kk] = score(q_row, k + kk * d, d, scale, causal, r, kk, mrow);
 
     /* step 2: safe softmax — maximum, shifted exponentials, sum, normalise */
     double m = -INFINITY;
     for (int64_t kk = 0; kk < nk; ++kk)
         if (s[kk] > m)
             m = s[kk];
+    if (m == -INFINITY) { /* no visible key (caller mask): O = 0, L = -inf */
+        for (int64_t t = 0; t < d; ++t)
+            o_row[t] = 0.0;
+        *lse = -INFINITY;
+        return;
+    }
     double l = 0.0;
     for (int64_t kk = 0; kk < nk; ++kk) {
         s[kk] = exp(s[kk] - m); /* masked keys: exp(-inf) = 0 */
@@ -316,7 +343,7 @@ int fa_oracle_attention_f64(const double* q, const double* k, const double* v,
         return FA_ORACLE_ENOMEM;
     for (int64_t i = 0; i < n_rows; ++i)
         three_step_row(q + rows[i] * d, k, v, nk, d, causal, scale, rows[i], s, o + i * d,
-                       lse + i, NULL);
+                       lse + i, NULL, NULL);
     free(s);
     return FA_ORACLE_OK;
 }
@@ -338,7 +365,29 @@ int fa_oracle_attention_dropout_f64(const double* q, const double* k, const doub
         return FA_ORACLE_ENOMEM;
     for (int64_t i = 0; i < n_rows; ++i)
         three_step_row(q + rows[i] * d, k, v, nk, d, causal, scale, rows[i], s, o + i * d,
-                       lse + i, &dr);
+                       lse + i, &dr, NULL);
+    free(s);
+    return FA_ORACLE_OK;
+}
+
+int fa_oracle_attention_masked_f64(const double* q, const double* k, const double* v,
+                                   const uint32_t* mask_rows, int64_t nq, int64_t nk, int64_t d,
+                                   int causal, double scale, int64_t n_rows, const int64_t* rows,
+                                   double* o, double* lse)
+{
+    if (!q || !k || !v || !mask_rows || !o || !lse || nq < 1 || nk < 1 || d < 1 || n_rows < 0 ||
+        (n_rows > 0 && !rows))
+        return FA_ORACLE_EINVAL;
+    for (int64_t i = 0; i < n_rows; ++i)
+        if (rows[i] < 0 || rows[i] >= nq)
+            return FA_ORACLE_EINVAL;
+    double* s = (double*)malloc((size_t)nk * sizeof(double));
+    if (!s)
+        return FA_ORACLE_ENOMEM;
+    const int64_t W = (nk + 31) / 32;
+    for (int64_t i = 0; i < n_rows; ++i)
+        three_step_row(q + rows[i] * d, k, v, nk, d, causal, scale, rows[i], s, o + i * d,
+                       lse + i, NULL, mask_rows + rows[i] * W);
     free(s);
     return FA_ORACLE_OK;
 }
@@ -368,7 +417,8 @@ static void online_step(double* st, int64_t dim, double x, const double* vrow, i
 
 static void online_row(const double* q_row, const double* k, const double* v, int64_t nk,
                        int64_t d, int causal, double scale, int64_t r, int64_t key_block,
-                       double* run, double* blk, double* o_row, double* lse, int64_t* raised)
+                       double* run, double* blk, double* o_row, double* lse, int64_t* raised,
+                       const uint32_t* mrow)
 {
     run[0] = -INFINITY;
     run[1] = 0.0;
@@ -379,7 +429,7 @@ static void online_row(const double* q_row, const double* k, const double* v, in
 
     if (key_block <= 0) {
         for (int64_t kk = 0; kk < nk; ++kk) {
-            double x = score(q_row, k + kk * d, d, scale, causal, r, kk);
+            double x = score(q_row, k + kk * d, d, scale, causal, r, kk, mrow);
             if (x == -INFINITY)
                 continue; /* masked key: skipped */
             online_step(run, d, x, v + kk * d, &nraised, !seen);
@@ -395,7 +445,7 @@ static void online_row(const double* q_row, const double* k, const double* v, in
                 blk[2 + t] = 0.0;
             int blk_seen = 0;
             for (int64_t kk = k0; kk < k1; ++kk) {
-                double x = score(q_row, k + kk * d, d, scale, causal, r, kk);
+                double x = score(q_row, k + kk * d, d, scale, causal, r, kk, mrow);
                 if (x == -INFINITY)
                     continue;
                 online_step(blk, d, x, v + kk * d, NULL, !blk_seen);
@@ -409,10 +459,11 @@ static void online_row(const double* q_row, const double* k, const double* v, in
             seen = 1;
         }
     }
-    /* final normalisation and logsumexp */
+    /* final normalisation and logsumexp; a row that absorbed no key keeps the empty
+     * state, read as O = 0 and L = -inf */
     for (int64_t t = 0; t < d; ++t)
-        o_row[t] = run[2 + t] / run[1];
-    *lse = run[0] + log(run[1]);
+        o_row[t] = seen ? run[2 + t] / run[1] : 0.0;
+    *lse = seen ? run[0] + log(run[1]) : -INFINITY;
     if (raised)
         *raised = nraised;
 }
@@ -434,7 +485,29 @@ int fa_oracle_online_f64(const double* q, const double* k, const double* v,
     double* blk = run + (d + 2);
     for (int64_t i = 0; i < n_rows; ++i)
         online_row(q + rows[i] * d, k, v, nk, d, causal, scale, rows[i], key_block, run, blk,
-                   o + i * d, lse + i, max_raised ? max_raised + i : NULL);
+                   o + i * d, lse + i, max_raised ? max_raised + i : NULL, NULL);
+    free(run);
+    return FA_ORACLE_OK;
+}
+
+int fa_oracle_online_masked_f64(const double* q, const double* k, const double* v,
+                                const uint32_t* mask_rows, int64_t nq, int64_t nk, int64_t d,
+                                int causal, double scale, int64_t key_block, int64_t n_rows,
+                                const int64_t* rows, double* o, double* lse)
+{
+    if (!q || !k || !v || !mask_rows || !o || !lse || nq < 1 || nk < 1 || d < 1 || n_rows < 0 ||
+        (n_rows > 0 && !rows))
+        return FA_ORACLE_EINVAL;
+    for (int64_t i = 0; i < n_rows; ++i)
+        if (rows[i] < 0 || rows[i] >= nq)
+            return FA_ORACLE_EINVAL;
+    double* run = (double*)malloc((size_t)(2 * (d + 2)) * sizeof(double));
+    if (!run)
+        return FA_ORACLE_ENOMEM;
+    const int64_t W = (nk + 31) / 32;
+    for (int64_t i = 0; i < n_rows; ++i)
+        online_row(q + rows[i] * d, k, v, nk, d, causal, scale, rows[i], key_block, run,
+                   run + (d + 2), o + i * d, lse + i, NULL, mask_rows + rows[i] * W);
     free(run);
     return FA_ORACLE_OK;
 }
@@ -457,15 +530,39 @@ static int check_raw(const void* q, const void* k, const void* v, int64_t B, int
 
 /* shared driver of fa_ref_rows_f64 / fa_ref_online_f64: widens K and V once per run
  * of equal sel_bh, widens each selected query row, then runs part 1 or part 2 on it */
+/* the caller-mask row of query r of head bh in a [mask_b, mask_h, Nq, W] array, W =
+ * ceil(Nk / 32) words, whose leading extents are 1 (shared) or B and H */
+static const uint32_t* mask_row(const uint32_t* mask, int64_t mask_b, int64_t mask_h, int64_t H,
+                                int64_t Nq, int64_t Nk, int64_t bh, int64_t r)
+{
+    if (!mask)
+        return NULL;
+    const int64_t W = (Nk + 31) / 32;
+    const int64_t b = mask_b == 1 ? 0 : bh / H, h = mask_h == 1 ? 0 : bh % H;
+    return mask + ((b * mask_h + h) * Nq + r) * W;
+}
+
+static int check_mask(const uint32_t* mask, int64_t mask_b, int64_t mask_h, int64_t B, int64_t H)
+{
+    if (!mask)
+        return FA_ORACLE_OK;
+    if ((mask_b != 1 && mask_b != B) || (mask_h != 1 && mask_h != H))
+        return FA_ORACLE_EINVAL;
+    return FA_ORACLE_OK;
+}
+
 static int ref_rows(const void* q, const void* k, const void* v, int64_t B, int64_t H,
                     int64_t Nq, int64_t Nk, int64_t d, int causal, float scale, int dtype,
                     int64_t n_sel, const int64_t* sel_bh, const int64_t* sel_row,
                     int use_online, int64_t key_block, double* o64, double* lse64,
-                    int64_t* max_raised, int drop_t, uint64_t seed)
+                    int64_t* max_raised, int drop_t, uint64_t seed, const uint32_t* mask,
+                    int64_t mask_b, int64_t mask_h)
 {
     int rc = check_raw(q, k, v, B, H, Nq, Nk, d, dtype);
     if (rc)
         return rc;
+    if (check_mask(mask, mask_b, mask_h, B, H))
+        return FA_ORACLE_EINVAL;
     Drop dr;
     if (drop_t >= 0 && make_drop(&dr, drop_t, seed, 0))
         return FA_ORACLE_EINVAL;
@@ -499,12 +596,13 @@ static int ref_rows(const void* q, const void* k, const void* v, int64_t B, int6
         }
         widen_span(q, (bh * Nq + r) * d, d, dtype, qr);
         dr.bh = bh;
+        const uint32_t* mrow = mask_row(mask, mask_b, mask_h, H, Nq, Nk, bh, r);
         if (use_online)
             online_row(qr, kh, vh, Nk, d, causal, sc, r, key_block, st, st + (d + 2),
-                       o64 + i * d, lse64 + i, max_raised ? max_raised + i : NULL);
+                       o64 + i * d, lse64 + i, max_raised ? max_raised + i : NULL, mrow);
         else
             three_step_row(qr, kh, vh, Nk, d, causal, sc, r, s, o64 + i * d, lse64 + i,
-                           drop_t >= 0 ? &dr : NULL);
+                           drop_t >= 0 ? &dr : NULL, mrow);
     }
     free(kh);
     free(vh);
@@ -520,7 +618,7 @@ int fa_ref_rows_f64(const void* q, const void* k, const void* v, int64_t B, int6
                     double* lse64)
 {
     return ref_rows(q, k, v, B, H, Nq, Nk, d, causal, scale, dtype, n_sel, sel_bh, sel_row, 0, 0,
-                    o64, lse64, NULL, -1, 0);
+                    o64, lse64, NULL, -1, 0, NULL, 1, 1);
 }
 
 int fa_ref_rows_dropout_f64(const void* q, const void* k, const void* v, int64_t B, int64_t H,
@@ -531,7 +629,7 @@ int fa_ref_rows_dropout_f64(const void* q, const void* k, const void* v, int64_t
     if (t < 0 || t > 255)
         return FA_ORACLE_EINVAL;
     return ref_rows(q, k, v, B, H, Nq, Nk, d, causal, scale, dtype, n_sel, sel_bh, sel_row, 0, 0,
-                    o64, lse64, NULL, t, seed);
+                    o64, lse64, NULL, t, seed, NULL, 1, 1);
 }
 
 int fa_ref_online_f64(const void* q, const void* k, const void* v, int64_t B, int64_t H,
@@ -540,7 +638,33 @@ int fa_ref_online_f64(const void* q, const void* k, const void* v, int64_t B, in
                       int64_t key_block, double* o64, double* lse64, int64_t* max_raised)
 {
     return ref_rows(q, k, v, B, H, Nq, Nk, d, causal, scale, dtype, n_sel, sel_bh, sel_row, 1,
-                    key_block, o64, lse64, max_raised, -1, 0);
+                    key_block, o64, lse64, max_raised, -1, 0, NULL, 1, 1);
+}
+
+/* The same two parts with a caller mask: mask [mask_b, mask_h, Nq, ceil(Nk / 32)] uint32
+ * words, mask_b in {1, B} and mask_h in {1, H} (1 = shared by every batch / head). */
+int fa_ref_rows_masked_f64(const void* q, const void* k, const void* v, const uint32_t* mask,
+                           int64_t mask_b, int64_t mask_h, int64_t B, int64_t H, int64_t Nq,
+                           int64_t Nk, int64_t d, int causal, float scale, int dtype,
+                           int64_t n_sel, const int64_t* sel_bh, const int64_t* sel_row,
+                           double* o64, double* lse64)
+{
+    if (!mask)
+        return FA_ORACLE_EINVAL;
+    return ref_rows(q, k, v, B, H, Nq, Nk, d, causal, scale, dtype, n_sel, sel_bh, sel_row, 0, 0,
+                    o64, lse64, NULL, -1, 0, mask, mask_b, mask_h);
+}
+
+int fa_ref_online_masked_f64(const void* q, const void* k, const void* v, const uint32_t* mask,
+                             int64_t mask_b, int64_t mask_h, int64_t B, int64_t H, int64_t Nq,
+                             int64_t Nk, int64_t d, int causal, float scale, int dtype,
+                             int64_t n_sel, const int64_t* sel_bh, const int64_t* sel_row,
+                             int64_t key_block, double* o64, double* lse64)
+{
+    if (!mask)
+        return FA_ORACLE_EINVAL;
+    return ref_rows(q, k, v, B, H, Nq, Nk, d, causal, scale, dtype, n_sel, sel_bh, sel_row, 1,
+                    key_block, o64, lse64, NULL, -1, 0, mask, mask_b, mask_h);
 }
 
 /* ------------------------------------------------------------------------- */
@@ -674,13 +798,18 @@ int fa_fwd_ref(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /* P[r, :] of one query row (the softmax of the scaled, masked scores) */
 static void prob_row(const double* q_row, const double* k, int64_t nk, int64_t d, int causal,
-                     double scale, int64_t r, double* p)
+                     double scale, int64_t r, double* p, const uint32_t* mrow)
 {
     double m = -INFINITY;
     for (int64_t kk = 0; kk < nk; ++kk) {
-        p[kk] = score(q_row, k + kk * d, d, scale, causal, r, kk);
+        p[kk] = score(q_row, k + kk * d, d, scale, causal, r, kk, mrow);
         if (p[kk] > m)
             m = p[kk];
+    }
+    if (m == -INFINITY) { /* no visible key (caller mask): P = 0 */
+        for (int64_t kk = 0; kk < nk; ++kk)
+            p[kk] = 0.0;
+        return;
     }
     double l = 0.0;
     for (int64_t kk = 0; kk < nk; ++kk) {
@@ -708,8 +837,10 @@ static double dprob_row(const double* do_row, const double* v, const double* p, 
 
 static int attention_bwd(const double* q, const double* k, const double* v, const double* dout,
                          int64_t nq, int64_t nk, int64_t d, int causal, double scale,
-                         double* dq, double* dk, double* dv, const Drop* dr)
+                         double* dq, double* dk, double* dv, const Drop* dr,
+                         const uint32_t* mask_rows)
 {
+    const int64_t W = (nk + 31) / 32;
     if (!q || !k || !v || !dout || !dq || !dk || !dv || nq < 1 || nk < 1 || d < 1)
         return FA_ORACLE_EINVAL;
     double* p = (double*)malloc((size_t)nk * sizeof(double));
@@ -726,7 +857,8 @@ static int attention_bwd(const double* q, const double* k, const double* v, cons
     for (int64_t r = 0; r < nq; ++r) {
         const double* q_row = q + r * d;
         const double* do_row = dout + r * d;
-        prob_row(q_row, k, nk, d, causal, scale, r, p);            /* P[r, :] */
+        prob_row(q_row, k, nk, d, causal, scale, r, p,
+                 mask_rows ? mask_rows + r * W : NULL);               /* P[r, :] */
         const double D = dprob_row(do_row, v, p, nk, d, dp, dr, r); /* dP[r, :], D_r */
         for (int64_t t = 0; t < d; ++t)
             dq[r * d + t] = 0.0;
@@ -749,7 +881,17 @@ int fa_oracle_attention_bwd_f64(const double* q, const double* k, const double* 
                                 const double* dout, int64_t nq, int64_t nk, int64_t d,
                                 int causal, double scale, double* dq, double* dk, double* dv)
 {
-    return attention_bwd(q, k, v, dout, nq, nk, d, causal, scale, dq, dk, dv, NULL);
+    return attention_bwd(q, k, v, dout, nq, nk, d, causal, scale, dq, dk, dv, NULL, NULL);
+}
+
+int fa_oracle_attention_bwd_masked_f64(const double* q, const double* k, const double* v,
+                                       const double* dout, const uint32_t* mask_rows, int64_t nq,
+                                       int64_t nk, int64_t d, int causal, double scale,
+                                       double* dq, double* dk, double* dv)
+{
+    if (!mask_rows)
+        return FA_ORACLE_EINVAL;
+    return attention_bwd(q, k, v, dout, nq, nk, d, causal, scale, dq, dk, dv, NULL, mask_rows);
 }
 
 int fa_oracle_attention_bwd_dropout_f64(const double* q, const double* k, const double* v,
@@ -760,7 +902,7 @@ int fa_oracle_attention_bwd_dropout_f64(const double* q, const double* k, const 
     Drop dr;
     if (bh < 0 || make_drop(&dr, t, seed, bh))
         return FA_ORACLE_EINVAL;
-    return attention_bwd(q, k, v, dout, nq, nk, d, causal, scale, dq, dk, dv, &dr);
+    return attention_bwd(q, k, v, dout, nq, nk, d, causal, scale, dq, dk, dv, &dr, NULL);
 }
 
 /* raw-buffer gradients ---------------------------------------------------- */
@@ -776,11 +918,13 @@ static int check_bwd_raw(const void* q, const void* k, const void* v, const void
 static int bwd_head(const void* q, const void* k, const void* v, const void* dout, int64_t B,
                     int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal, float scale,
                     int dtype, int64_t bh, double* dq64, double* dk64, double* dv64,
-                    const Drop* dr)
+                    const Drop* dr, const uint32_t* mask, int64_t mask_b, int64_t mask_h)
 {
     int rc = check_bwd_raw(q, k, v, dout, B, H, Nq, Nk, d, dtype);
     if (rc)
         return rc;
+    if (check_mask(mask, mask_b, mask_h, B, H))
+        return FA_ORACLE_EINVAL;
     if (bh < 0 || bh >= B * H || !dq64 || !dk64 || !dv64)
         return FA_ORACLE_EINVAL;
     double* buf = (double*)malloc((size_t)(2 * Nq * d + 2 * Nk * d) * sizeof(double));
@@ -791,7 +935,8 @@ static int bwd_head(const void* q, const void* k, const void* v, const void* dou
     widen_span(dout, bh * Nq * d, Nq * d, dtype, doh);
     widen_span(k, bh * Nk * d, Nk * d, dtype, kh);
     widen_span(v, bh * Nk * d, Nk * d, dtype, vh);
-    rc = attention_bwd(qh, kh, vh, doh, Nq, Nk, d, causal, (double)scale, dq64, dk64, dv64, dr);
+    rc = attention_bwd(qh, kh, vh, doh, Nq, Nk, d, causal, (double)scale, dq64, dk64, dv64, dr,
+                       mask_row(mask, mask_b, mask_h, H, Nq, Nk, bh, 0));
     free(buf);
     return rc;
 }
@@ -803,7 +948,21 @@ int fa_ref_bwd_head_f64(const void* q, const void* k, const void* v, const void*
                         double* dv64)
 {
     return bwd_head(q, k, v, dout, B, H, Nq, Nk, d, causal, scale, dtype, bh, dq64, dk64, dv64,
-                    NULL);
+                    NULL, NULL, 1, 1);
+}
+
+/* The same with a caller mask ([mask_b, mask_h, Nq, ceil(Nk / 32)] words, as
+ * fa_ref_rows_masked_f64). */
+int fa_ref_bwd_head_masked_f64(const void* q, const void* k, const void* v, const void* dout,
+                               const uint32_t* mask, int64_t mask_b, int64_t mask_h, int64_t B,
+                               int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                               float scale, int dtype, int64_t bh, double* dq64, double* dk64,
+                               double* dv64)
+{
+    if (!mask)
+        return FA_ORACLE_EINVAL;
+    return bwd_head(q, k, v, dout, B, H, Nq, Nk, d, causal, scale, dtype, bh, dq64, dk64, dv64,
+                    NULL, mask, mask_b, mask_h);
 }
 
 /* The same with dropout (threshold t, seed) on P. */
@@ -816,7 +975,7 @@ int fa_ref_bwd_head_dropout_f64(const void* q, const void* k, const void* v, con
     if (make_drop(&dr, t, seed, bh))
         return FA_ORACLE_EINVAL;
     return bwd_head(q, k, v, dout, B, H, Nq, Nk, d, causal, scale, dtype, bh, dq64, dk64, dv64,
-                    &dr);
+                    &dr, NULL, 1, 1);
 }
 
 /* dQ of selected query rows (sel_bh[i], sel_row[i]) -> dq64[i * d .. +d] */
@@ -849,7 +1008,7 @@ int fa_ref_bwd_dq_rows_f64(const void* q, const void* k, const void* v, const vo
         }
         widen_span(q, (bh * Nq + r) * d, d, dtype, qr);
         widen_span(dout, (bh * Nq + r) * d, d, dtype, dor);
-        prob_row(qr, kh, Nk, d, causal, sc, r, p);
+        prob_row(qr, kh, Nk, d, causal, sc, r, p, NULL);
         const double D = dprob_row(dor, vh, p, Nk, d, dp, NULL, r);
         double* out = dq64 + i * d;
         for (int64_t t = 0; t < d; ++t)
@@ -895,8 +1054,8 @@ int fa_ref_bwd_rowstats_f64(const void* q, const void* k, const void* v, const v
         }
         widen_span(q, (bh * Nq + r) * d, d, dtype, qr);
         widen_span(dout, (bh * Nq + r) * d, d, dtype, dor);
-        three_step_row(qr, kh, vh, Nk, d, causal, sc, r, p, o_row, lse64 + i, NULL);
-        prob_row(qr, kh, Nk, d, causal, sc, r, p);
+        three_step_row(qr, kh, vh, Nk, d, causal, sc, r, p, o_row, lse64 + i, NULL, NULL);
+        prob_row(qr, kh, Nk, d, causal, sc, r, p, NULL);
         D64[i] = dprob_row(dor, vh, p, Nk, d, dp, NULL, r);
     }
     free(buf);
@@ -944,7 +1103,7 @@ int fa_ref_bwd_dkv_keys_f64(const void* q, const void* k, const void* v, const v
             dvj[t] = 0.0;
         }
         for (int64_t r = 0; r < Nq; ++r) {
-            const double s = score(qh + r * d, kr, d, sc, causal, r, j);
+            const double s = score(qh + r * d, kr, d, sc, causal, r, j, NULL);
             if (s == -INFINITY)
                 continue; /* masked: P[r, j] = 0 */
             const double p = exp(s - lse64_all[bh * Nq + r]);

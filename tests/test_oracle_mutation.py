@@ -8,7 +8,9 @@ the running sum — "手写"/CUTLASS article section 3.3 and its section 6.3 tab
 the rest are a dropped scale, an inverted mask, a wrong index, a wrong sign, and in
 the gradients a dropped softmax-Jacobian term, a flipped sign, an unweighted D, a
 dropped scale and wrong operands, and in dropout a broken generator round, an
-inverted keep test, a dropped keep scale and the mask left out of dV or dP.
+inverted keep test, a dropped keep scale and the mask left out of dV or dP, and in
+the caller masks a reversed bit order, an ignored mask, a wrong empty-row L and the
+mask left out of the gradients.
 """
 import json
 import math
@@ -39,7 +41,7 @@ MUTANTS = {
     "value_index_transposed": ("o_row[t] += pk * v[kk * d + t];",
                                "o_row[t] += pk * v[kk * d + (d - 1 - t)];"),
     "lse_wrong_sign": ("*lse = m + log(l);", "*lse = m - log(l);"),
-    "online_lse_wrong_sign": ("*lse = run[0] + log(run[1]);", "*lse = run[0] - log(run[1]);"),
+    "online_lse_wrong_sign": ("*lse = seen ? run[0] + log(run[1])", "*lse = seen ? run[0] - log(run[1])"),
     # gradients (part 3): the softmax-Jacobian term, signs, scales and operands
     "bwd_D_dropped": ("const double ds = p[kk] * (dp[kk] - D);",
                       "const double ds = p[kk] * dp[kk];"),
@@ -61,6 +63,14 @@ MUTANTS = {
     "dropout_dv_unmasked": ("const double pz = p[kk] * drop_factor(dr, r, kk);",
                             "const double pz = p[kk];"),
     "dropout_dp_unmasked": ("dp[kk] = acc * drop_factor(dr, r, kk);", "dp[kk] = acc;"),
+    # caller masks (part 5): the bit order, the mask left out, the empty-row reading,
+    # the mask left out of the backward
+    "mask_bit_order_reversed": ("((mrow[kk / 32] >> (kk % 32)) & 1u)",
+                                "((mrow[kk / 32] >> (31 - kk % 32)) & 1u)"),
+    "mask_ignored": ("return !mrow || ((mrow[kk / 32] >> (kk % 32)) & 1u);", "return 1;"),
+    "empty_row_lse_zero": ("        *lse = -INFINITY;\n        return;",
+                           "        *lse = 0.0;\n        return;"),
+    "bwd_mask_dropped": ("mask_rows ? mask_rows + r * W : NULL", "NULL"),
 }
 
 
@@ -175,7 +185,42 @@ def _pins(L):
                 dn = np.sum(dout * oracle.attention_dropout_f64(*args, False, 0.6, 90, 3, L=L)[0])
                 assert abs((up - dn) / (2 * h) - got[which][idx]) < 1e-7
 
+    def masked_torch_sdpa():
+        import torch
+        from flashattention_tiling_online_amd import inputs
+        rng = np.random.default_rng(11)
+        q, k, v = (rng.standard_normal((20, 8)) for _ in range(3))
+        k, v = rng.standard_normal((45, 8)), rng.standard_normal((45, 8))
+        vis = rng.random((20, 45)) < 0.5
+        vis[4] = False
+        live = vis.any(axis=1)
+        o, lse = oracle.attention_masked_f64(q, k, v, inputs.pack_mask(vis), False, 0.4, L=L)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            *(torch.from_numpy(a)[None] for a in (q, k, v)),
+            attn_mask=torch.from_numpy(vis)[None], scale=0.4)[0].numpy()
+        np.testing.assert_allclose(o[live], ref[live], rtol=1e-12, atol=1e-13)
+        assert (o[~live] == 0).all() and np.isneginf(lse[~live]).all()
+
+    def masked_bwd_torch():
+        import torch
+        from flashattention_tiling_online_amd import inputs
+        rng = np.random.default_rng(12)
+        q, dout = rng.standard_normal((10, 4)), rng.standard_normal((10, 4))
+        k, v = rng.standard_normal((37, 4)), rng.standard_normal((37, 4))
+        vis = rng.random((10, 37)) < 0.5
+        vis[:, 0] = True
+        got = oracle.attention_bwd_masked_f64(q, k, v, dout, inputs.pack_mask(vis), False, 0.5,
+                                              L=L)
+        t = [torch.from_numpy(a).clone().requires_grad_(True) for a in (q, k, v)]
+        torch.nn.functional.scaled_dot_product_attention(
+            *(x[None] for x in t), attn_mask=torch.from_numpy(vis)[None],
+            scale=0.5)[0].backward(torch.from_numpy(dout))
+        for g, x in zip(got, t):
+            np.testing.assert_allclose(g, x.grad.numpy(), rtol=1e-10, atol=1e-12)
+
     for name, fn in [("worked_example", worked_example), ("torch_sdpa", torch_sdpa),
+                     ("masked_torch_sdpa", masked_torch_sdpa),
+                     ("masked_bwd_torch", masked_bwd_torch),
                      ("lse_scipy", lse_scipy), ("part2_vs_part1", part2_vs_part1),
                      ("merge_closed_form", merge_closed_form),
                      ("bwd_finite_differences", bwd_finite_differences),
