@@ -18,9 +18,9 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH, FA_ERR_SCRATCH = 0
 FA_STATIC_SCRATCH_BYTES = 64 << 20  # include/fa.h
 
 # symbols include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_fwd_split", "fa_fwd_split_workspace", "fa_fwd_split_static", "fa_merge",
-           "fa_split_hint", "fa_bwd", "fa_bwd_workspace", "fa_fwd_dropout", "fa_bwd_dropout",
-           "fa_status_str", "fa_tile_rows")
+EXPORTS = ("fa_fwd", "fa_fwd_masked", "fa_fwd_split", "fa_fwd_split_workspace",
+           "fa_fwd_split_static", "fa_merge", "fa_split_hint", "fa_bwd", "fa_bwd_workspace",
+           "fa_fwd_dropout", "fa_bwd_dropout", "fa_status_str", "fa_tile_rows")
 
 _lib = None
 
@@ -51,6 +51,9 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_split.argtypes = L.fa_fwd.argtypes[:-1] + [ctypes.c_int, ctypes.c_void_p, i64,
                                                             ctypes.c_void_p]
         L.fa_fwd_split.restype = ctypes.c_int
+        L.fa_fwd_masked.argtypes = [ctypes.c_void_p] * 4 + [i64, i64] + [ctypes.c_void_p] * 2 + [
+            i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+        L.fa_fwd_masked.restype = ctypes.c_int
         L.fa_fwd_split_static.argtypes = L.fa_fwd.argtypes[:-1] + [ctypes.c_int, ctypes.c_void_p]
         L.fa_fwd_split_static.restype = ctypes.c_int
         L.fa_fwd_split_workspace.argtypes = [i64, i64, i64, i64, ctypes.c_int]
@@ -88,6 +91,14 @@ def fa_fwd_raw(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int
     """Direct call with integer device pointers; returns the fa_status_t code."""
     return lib().fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, int(causal), float(scale),
                         int(dtype), stream)
+
+
+def fa_fwd_masked_raw(q: int, k: int, v: int, mask: int, mask_b: int, mask_h: int, o: int,
+                      lse: int, B: int, H: int, Nq: int, Nk: int, d: int, causal: int,
+                      scale: float, dtype: int, stream: int) -> int:
+    """Direct call of fa_fwd_masked with integer device pointers; returns the status code."""
+    return lib().fa_fwd_masked(q, k, v, mask, int(mask_b), int(mask_h), o, lse, B, H, Nq, Nk, d,
+                               int(causal), float(scale), int(dtype), stream)
 
 
 def fa_fwd_split_raw(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int, Nk: int,
@@ -347,6 +358,45 @@ def fa_fwd(q, k, v, causal: bool = False, scale: float | None = None, o=None, ls
         o, lse = _outputs_fwd(q, B, H, Nq, o, lse)
     st = fa_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H,
                     Nq, Nk, d, int(bool(causal)), scale, code, stream.cuda_stream)
+    if st != FA_OK:
+        raise FAError(st)
+    return o, lse
+
+
+def _check_mask(mask, B, H, Nq, Nk, device):
+    """A caller mask: a contiguous int32 or uint32 GPU tensor [mask_b, mask_h, Nq,
+    ceil(Nk/32)] with mask_b in {1, B} and mask_h in {1, H}."""
+    import torch
+    if not hasattr(mask, "is_cuda") or not mask.is_cuda or mask.device != device:
+        raise ValueError(f"mask must be a GPU tensor on {device}")
+    if mask.dtype not in (torch.int32, getattr(torch, "uint32", torch.int32)):
+        raise TypeError("mask must hold 32-bit words (int32 or uint32)")
+    if not mask.is_contiguous() or mask.dim() != 4:
+        raise ValueError("mask must be a contiguous 4-D tensor [mask_b, mask_h, Nq, W]")
+    mb, mh, nq, w = mask.shape
+    if mb not in (1, B) or mh not in (1, H) or nq != Nq or w != -(-Nk // 32):
+        raise ValueError(f"mask must be [1 or {B}, 1 or {H}, {Nq}, {-(-Nk // 32)}], got "
+                         f"{tuple(mask.shape)}")
+    return mb, mh
+
+
+def fa_fwd_masked(q, k, v, mask, causal: bool = False, scale: float | None = None, o=None,
+                  lse=None, stream=None):
+    """fa_fwd with a caller mask (fa_fwd_masked): ``mask`` holds the bit-packed rows
+    [mask_b, mask_h, Nq, ceil(Nk/32)] (key k in bit k % 32 of word k // 32, set =
+    visible).  A row with no visible key gets O = 0 and L = -inf."""
+    import torch
+    B, H, Nq, Nk, d = _check_qkv(q, k, v)
+    mb, mh = _check_mask(mask, B, H, Nq, Nk, q.device)
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    stream = _launch_stream(stream, q.device)
+    with torch.cuda.stream(stream):
+        o, lse = _outputs_fwd(q, B, H, Nq, o, lse)
+    st = fa_fwd_masked_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), mask.data_ptr(), mb, mh,
+                           o.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d, int(bool(causal)),
+                           scale, code, stream.cuda_stream)
     if st != FA_OK:
         raise FAError(st)
     return o, lse

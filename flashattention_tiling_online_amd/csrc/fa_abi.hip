@@ -103,6 +103,40 @@ Launch fwd16_drop(int64_t d, bool c)
                    fa::Tile16<64>::BR, fa::Tile16<64>::NT);
 }
 
+// the forward kernel with a caller mask (unsplit): d = 128 on the phase-alternating
+// kernel, d = 64 on fa_fwd_mfma16, fp32 on fa_fwd_f32
+template <typename T>
+Launch fwd16_mask(int64_t d, bool c)
+{
+    if (d == 128)
+        return c ? Launch{reinterpret_cast<const void*>(&fa::fa_fwd_pp_kernel<T, true, false, false, true>),
+                          fa::TilePP::BR, fa::TilePP::NT}
+                 : Launch{reinterpret_cast<const void*>(&fa::fa_fwd_pp_kernel<T, false, false, false, true>),
+                          fa::TilePP::BR, fa::TilePP::NT};
+    return c ? Launch{reinterpret_cast<const void*>(&fa::fa_fwd_mfma16_kernel<T, 64, true, false, false, true>),
+                      fa::Tile16<64>::BR, fa::Tile16<64>::NT}
+             : Launch{reinterpret_cast<const void*>(&fa::fa_fwd_mfma16_kernel<T, 64, false, false, false, true>),
+                      fa::Tile16<64>::BR, fa::Tile16<64>::NT};
+}
+
+template <int D>
+Launch f32_mask(bool c)
+{
+    return c ? Launch{reinterpret_cast<const void*>(&fa::fa_fwd_f32_kernel<D, true, false, true>),
+                      fa::TileF32<D>::BR, fa::TileF32<D>::NT}
+             : Launch{reinterpret_cast<const void*>(&fa::fa_fwd_f32_kernel<D, false, false, true>),
+                      fa::TileF32<D>::BR, fa::TileF32<D>::NT};
+}
+
+Launch fwd_mask_of(fa_dtype_t dtype, int64_t d, bool c)
+{
+    switch (dtype) {
+    case FA_DTYPE_BF16: return fwd16_mask<__bf16>(d, c);
+    case FA_DTYPE_F16: return fwd16_mask<_Float16>(d, c);
+    default: return d == 128 ? f32_mask<128>(c) : f32_mask<64>(c);
+    }
+}
+
 // the byte threshold of a drop probability: t = round(256 p); -1 outside [0, 1) or
 // beyond 255
 int drop_threshold(float p)
@@ -188,13 +222,26 @@ struct Dropout {
     uint64_t seed;
 };
 
+// a caller mask: the words, their strides per batch and head (0 = shared), the words
+// per row and the head count that splits b * H + h
+struct MaskArg {
+    const uint32_t* words;
+    int64_t sb, sh;
+    int w, H;
+};
+
 template <typename T>
 hipError_t launch_fwd(const Launch& L, const void* q, const void* k, const void* v, void* o,
                       float* lse, float* o_part, float* lse_part, int64_t BH, int64_t Nq,
                       int64_t Nk, int n_splits, int split_tiles, float scale, hipStream_t stream,
-                      const Dropout* drop = nullptr)
+                      const Dropout* drop = nullptr, const MaskArg* mask = nullptr)
 {
     fa::FwdParams<T> prm;
+    prm.mask = mask ? mask->words : nullptr;
+    prm.mask_sb = mask ? mask->sb : 0;
+    prm.mask_sh = mask ? mask->sh : 0;
+    prm.mask_w = mask ? mask->w : 0;
+    prm.H = mask ? mask->H : 1;
     prm.drop_key0 = drop ? (uint32_t)drop->seed : 0u;
     prm.drop_key1 = drop ? (uint32_t)(drop->seed >> 32) : 0u;
     prm.drop_t = drop ? drop->t : 0u;
@@ -221,18 +268,19 @@ hipError_t launch_fwd(const Launch& L, const void* q, const void* k, const void*
 hipError_t launch_fwd_any(fa_dtype_t dtype, const Launch& L, const void* q, const void* k,
                           const void* v, void* o, float* lse, float* o_part, float* lse_part,
                           int64_t BH, int64_t Nq, int64_t Nk, int n_splits, int split_tiles,
-                          float scale, hipStream_t stream, const Dropout* drop = nullptr)
+                          float scale, hipStream_t stream, const Dropout* drop = nullptr,
+                          const MaskArg* mask = nullptr)
 {
     switch (dtype) {
     case FA_DTYPE_BF16:
         return launch_fwd<__bf16>(L, q, k, v, o, lse, o_part, lse_part, BH, Nq, Nk, n_splits,
-                                  split_tiles, scale, stream, drop);
+                                  split_tiles, scale, stream, drop, mask);
     case FA_DTYPE_F16:
         return launch_fwd<_Float16>(L, q, k, v, o, lse, o_part, lse_part, BH, Nq, Nk, n_splits,
-                                    split_tiles, scale, stream, drop);
+                                    split_tiles, scale, stream, drop, mask);
     default:
         return launch_fwd<float>(L, q, k, v, o, lse, o_part, lse_part, BH, Nq, Nk, n_splits,
-                                 split_tiles, scale, stream);
+                                 split_tiles, scale, stream, nullptr, mask);
     }
 }
 
@@ -303,6 +351,52 @@ extern "C" fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* 
     const Dropout drop{(uint32_t)t, seed};
     const hipError_t err = launch_fwd_any(dtype, L, q, k, v, o, lse, nullptr, nullptr, B * H, Nq,
                                           Nk, 1, 0, scale, hs, t > 0 ? &drop : nullptr);
+    return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+namespace {
+
+// Checks of a caller mask [mask_b, mask_h, Nq, ceil(Nk / 32)] words against (B, H, Nq,
+// Nk): extents 1 or B / H and a 4-byte aligned pointer (a workgroup's rows of it stay
+// below 2^30 bytes: Nk < 2^25 by the forward's limits).  Fills the kernel's view of it.
+fa_status_t check_mask(const uint32_t* mask, int64_t mask_b, int64_t mask_h, int64_t B,
+                       int64_t H, int64_t Nq, int64_t Nk, MaskArg* out)
+{
+    if (!mask || !aligned(mask, 4))
+        return FA_ERR_INVALID_ARG;
+    if ((mask_b != 1 && mask_b != B) || (mask_h != 1 && mask_h != H))
+        return FA_ERR_INVALID_ARG;
+    const int64_t w = (Nk + 31) / 32;
+    out->words = mask;
+    out->w = (int)w;
+    out->sh = mask_h == 1 ? 0 : Nq * w;
+    out->sb = mask_b == 1 ? 0 : mask_h * Nq * w;
+    out->H = (int)H;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" fa_status_t fa_fwd_masked(const void* q, const void* k, const void* v,
+                                     const uint32_t* mask, int64_t mask_b, int64_t mask_h,
+                                     void* o, float* lse, int64_t B, int64_t H, int64_t Nq,
+                                     int64_t Nk, int64_t d, int causal, float scale,
+                                     fa_dtype_t dtype, fa_stream_t stream)
+{
+    Launch L;
+    bool empty;
+    fa_status_t st =
+        check_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, false, &L, &empty);
+    if (st != FA_OK || empty)
+        return st;
+    MaskArg mk;
+    st = check_mask(mask, mask_b, mask_h, B, H, Nq, Nk, &mk);
+    if (st != FA_OK)
+        return st;
+    L = fwd_mask_of(dtype, d, causal != 0);
+    const hipError_t err = launch_fwd_any(dtype, L, q, k, v, o, lse, nullptr, nullptr, B * H, Nq,
+                                          Nk, 1, 0, scale, reinterpret_cast<hipStream_t>(stream),
+                                          nullptr, &mk);
     return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -96,7 +96,60 @@ struct FwdParams {
     // threshold and keep scale, as in fa_philox.hpp
     uint32_t drop_key0, drop_key1, drop_t;
     float drop_keep_scale;
+    // caller mask (used by the masked instantiations only): bit-packed rows of
+    // mask_w = ceil(Nk / 32) words, key k in bit k % 32 of word k / 32 (set = visible);
+    // head bh = b * H + h reads the [Nq, mask_w] slice at mask + b * mask_sb + h * mask_sh
+    // (strides in words, 0 where the mask is shared)
+    const uint32_t* mask;
+    int64_t mask_sb, mask_sh;
+    int mask_w, H;
 };
+
+// The caller-mask slice of head bh (see FwdParams::mask).
+template <typename Prm>
+__device__ __forceinline__ const uint32_t* mask_slice(const Prm& prm, int bh)
+{
+    return prm.mask + (bh / prm.H) * prm.mask_sb + (bh % prm.H) * prm.mask_sh;
+}
+
+// Buffer resource over rows [row0, min(row0 + rows, Nq)) of a head's mask slice:
+// words past the end read as zero (key k hidden).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mask_rsrc(const uint32_t* slice, int row0,
+                                                           int rows, int Nq, int w)
+{
+    const int64_t n = min(row0 + rows, Nq) - row0;
+    const int64_t bytes = (n > 0 ? n : 0) * (int64_t)w * 4;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(slice) + (size_t)row0 * w, 0,
+                                             bytes < (1 << 30) ? (int)bytes : (1 << 30),
+                                             0x00020000);
+}
+
+// Scores s[kb][r] of a 64-key tile whose keys, for lane half hh, sit at offsets
+// 32 kb + 8 (r / 4) + 4 hh + r % 4 become -inf where the mask words w0 (keys 0-31 of
+// the tile) and w1 (keys 32-63) have the key's bit clear.  Returns true when every
+// key of every lane of the wave is visible (and nothing was changed).
+__device__ __forceinline__ bool apply_mask_words(f32x16* s, uint32_t w0, uint32_t w1, int hh)
+{
+    const uint32_t a = w0 >> (4 * hh), b = w1 >> (4 * hh);
+    const uint32_t lane_bits = 0x0F0F0F0Fu;  // this half's 16 keys of each word
+    const bool all_mine = ((a & b & lane_bits) == lane_bits);
+    if (__builtin_amdgcn_ballot_w64(!all_mine) == 0)
+        return true;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t w = kb ? b : a;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            // all ones where the key is visible, zero where hidden (the score is copied
+            // out of the vector before its bits are taken)
+            const uint32_t keep = (uint32_t)(-(int32_t)((w >> (8 * (r >> 2) + (r & 3))) & 1u));
+            const float x = s[kb][r];
+            const uint32_t bits = __builtin_bit_cast(uint32_t, x);
+            s[kb][r] = __builtin_bit_cast(float, (bits & keep) | (0xFF800000u & ~keep));
+        }
+    }
+    return false;
+}
 
 // -inf as a float constant usable in device code
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }

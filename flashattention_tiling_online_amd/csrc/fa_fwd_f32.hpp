@@ -8,6 +8,10 @@
 // single-precision accuracy; it is simple rather than fast (single-buffered
 // LDS, two barriers per tile).
 //
+// With a caller mask (blog page "Flash Attention", Algorithm 2: S_masked = mask(S)) the
+// hidden scores become -inf from the mask words of the tile; a row that sees no key ends
+// with O = 0 and L = -inf.
+//
 // Register layouts mirror the bf16 kernel: S^T = K Q^T and O^T = V^T P^T, so each
 // lane owns one query.  With k = 2 per MFMA, lane half hh supplies one k index:
 //   S:  A = K[key = 32kb + lane%32][d = 2c + hh],   B = Q[my_q][2c + hh]
@@ -32,7 +36,7 @@ struct TileF32 {
     static constexpr int DB = D / 32;
 };
 
-template <int D, bool CAUSAL, bool SPLIT>
+template <int D, bool CAUSAL, bool SPLIT, bool MASK = false>
 __global__ __launch_bounds__(256)
 void fa_fwd_f32_kernel(const FwdParams<float> prm)
 {
@@ -67,6 +71,14 @@ void fa_fwd_f32_kernel(const FwdParams<float> prm)
     const float* Qh = prm.q + (size_t)bh * Nq * D;
     const float* Kh = prm.k + ((size_t)bh * Nk + kbeg) * D;
     const float* Vh = prm.v + ((size_t)bh * Nk + kbeg) * D;
+
+    // caller mask: this lane's row of the head's mask slice
+    static_assert(!(MASK && SPLIT), "the masked forward is not split");
+    const __amdgpu_buffer_rsrc_t mrs = mask_rsrc(MASK ? mask_slice(prm, bh) : nullptr, q0, P::BR, Nq,
+                                                 MASK ? prm.mask_w : 0);
+    int mrow_off = 0;
+    if (MASK)
+        mrow_off = (my_q - q0) * prm.mask_w * 4;
 
     float qf[D / 2];
 #pragma unroll
@@ -123,6 +135,10 @@ void fa_fwd_f32_kernel(const FwdParams<float> prm)
                                                              qf[c], s[kb], 0, 0, 0);
         }
 
+        if (MASK)
+            apply_mask_words(s, __builtin_amdgcn_raw_buffer_load_b32(mrs, mrow_off + 8 * j, 0, 0),
+                             __builtin_amdgcn_raw_buffer_load_b32(mrs, mrow_off + 8 * j + 4, 0, 0),
+                             hh);
         const bool need_mask = (key0 + P::BC > Nks) || (CAUSAL && key0 + P::BC - 1 > qkw0);
         if (need_mask) {
 #pragma unroll

@@ -45,6 +45,8 @@
 //     rounded P it was built from (see update_max).
 #pragma once
 
+#include <type_traits>
+
 #include "fa_philox.hpp"
 #include "fa_tiles.hpp"
 
@@ -79,7 +81,7 @@ struct Tile16 {
     static_assert(KT % 1024 == 0, "K tiles must be whole DMA blocks");
 };
 
-template <typename T, int D, bool CAUSAL, bool SPLIT, bool DROP = false>
+template <typename T, int D, bool CAUSAL, bool SPLIT, bool DROP = false, bool MASK = false>
 __global__ __launch_bounds__(Tile16<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
 {
@@ -158,7 +160,25 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
     // vbase + 32db*VTSTR + 32cc.
     const int vbase = ql * P::VTSTR + hh * 16;
 
+    // ---- caller mask: this lane's row of the head's mask slice; the words of tile t
+    // sit in slot t % 2, loaded two tiles ahead of the S MFMAs that need them
+    static_assert(!(MASK && SPLIT), "the masked forward is not split");
+    const __amdgpu_buffer_rsrc_t mrs = mask_rsrc(MASK ? mask_slice(prm, bh) : nullptr, q0, P::BR, Nq,
+                                                 MASK ? prm.mask_w : 0);
+    int mrow_off = 0;
+    uint32_t mwd[2][2] = {{0u, 0u}, {0u, 0u}};
+    if (MASK)
+        mrow_off = (my_q - q0) * prm.mask_w * 4;
+    auto load_mask = [&](int t, int slot) {
+        mwd[slot][0] = __builtin_amdgcn_raw_buffer_load_b32(mrs, mrow_off + 8 * t, 0, 0);
+        mwd[slot][1] = __builtin_amdgcn_raw_buffer_load_b32(mrs, mrow_off + 8 * t + 4, 0, 0);
+    };
+
     // ---- prologue: tiles 0 and 1 in flight, Q fragment into registers
+    if (MASK && 0 < n_w)
+        load_mask(0, 0);
+    if (MASK && 1 < n_w)
+        load_mask(1, 1);
     if (0 < nkt) {
         stage_k(0, P::K0);
         load_v_block<D>(Vh, 0, Nks, v_kg, v_dq, vreg);
@@ -266,7 +286,9 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
         const float mh = mx * c2;  // c2 > 0: max commutes with the scale
         if (__builtin_amdgcn_ballot_w64(mh > thr2) != 0) {
             const float m_new = fmaxf(m2, fmaxf(mh, swap_halves(mh)));
-            const float alpha = exp2_fast(m2 - m_new);  // 0 on the first tile (m2 = -inf)
+            // 0 on a row's first visible tile (m2 = -inf); 1 for a row that has seen no
+            // visible key yet (a caller mask can hide all of them)
+            const float alpha = m_new == neg_inf() ? 1.f : exp2_fast(m2 - m_new);
 #pragma unroll
             for (int db = 0; db < P::DB; ++db)
                 o[db] *= alpha;
@@ -346,6 +368,8 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
     float ma = 0.f, mb = 0.f;  // half-row maxima of the scores in sa / sb
     if (0 < n_w) {
         scores(P::K0, sa);
+        if (MASK)
+            apply_mask_words(sa, mwd[0][0], mwd[0][1], hh);
         ma = half_max(sa);
     }
     __syncthreads();  // every wave has read K_0
@@ -361,13 +385,16 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
     // K_{j+2} (DMA issued one step ago), and the next loads go out: V_{j+2} into
     // registers, K_{j+3} into kn.
     auto step = [&](int j, f32x16* s_cur, f32x16* s_nxt, float& m_cur, float& m_nxt, int kn,
-                    int vc, int vn) {
+                    int vc, int vn, auto SL) {
+        constexpr int sl = decltype(SL)::value;  // mask-word slot of tile j + 1
         if (j + 1 < n_w) {
             update_max(m_cur);
             scores(kn, s_nxt);
             vec pb[4];
             exp_sum_pack(j, s_cur, pb);
             pv(pb, vc);
+            if (MASK)
+                apply_mask_words(s_nxt, mwd[sl][0], mwd[sl][1], hh);
             m_nxt = half_max(s_nxt);
         } else if (j < n_w) {
             if (needs_mask(j)) {
@@ -382,15 +409,17 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
         if (j + 1 < nkt)
             store_vt_block<P::VTSTR>(smem + vn, v_kg, v_dq, vreg);
         __syncthreads();
+        if (MASK && j + 2 < n_w)
+            load_mask(j + 2, sl ^ 1);  // tile j + 2 has the parity of tile j
         if (j + 2 < nkt)
             load_v_block<D>(Vh, j + 2, Nks, v_kg, v_dq, vreg);
         if (j + 3 < nkt)
             stage_k(j + 3, kn);
     };
     for (int j = 0; j < nkt; j += 2) {
-        step(j, sa, sb, ma, mb, P::K1, P::V0, P::V1);
+        step(j, sa, sb, ma, mb, P::K1, P::V0, P::V1, std::integral_constant<int, 1>{});
         if (j + 1 < nkt)
-            step(j + 1, sb, sa, mb, ma, P::K0, P::V1, P::V0);
+            step(j + 1, sb, sa, mb, ma, P::K0, P::V1, P::V0, std::integral_constant<int, 0>{});
     }
 
     if (!wave_active)
@@ -434,7 +463,8 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
             prm.lse_part[((size_t)split * prm.bh_count + bh) * Nq + my_q] =
                 lt > 0.f ? (m2 + log2_fast(lt)) * kLn2 : neg_inf();
     } else {
-        const float inv = (DROP ? prm.drop_keep_scale : 1.0f) / lrt;
+        // a row that saw no visible key (only with a caller mask): O = 0, L = -inf
+        const float inv = (MASK && !(lrt > 0.f)) ? 0.f : (DROP ? prm.drop_keep_scale : 1.0f) / lrt;
 #pragma unroll
         for (int db = 0; db < P::DB; ++db)
 #pragma unroll
@@ -457,7 +487,8 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
                 *reinterpret_cast<u32x4*>(ohead + (size_t)(qw0 + r) * D + 8 * ch) = piece;
         }
         if (hh == 0 && my_q < Nq)
-            prm.lse[(size_t)bh * Nq + my_q] = (m2 + log2_fast(lt)) * kLn2;
+            prm.lse[(size_t)bh * Nq + my_q] =
+                (MASK && !(lt > 0.f)) ? neg_inf() : (m2 + log2_fast(lt)) * kLn2;
     }
 }
 

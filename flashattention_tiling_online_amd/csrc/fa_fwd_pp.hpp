@@ -44,7 +44,10 @@
 //
 // With key splits a workgroup stages one range of whole key tiles and writes fp32
 // partial states, as fa_fwd_mfma16.hpp does; with dropout the softmax phase zeroes
-// the dropped entries of the rounded P (the Philox words of fa_philox.hpp).
+// the dropped entries of the rounded P (the Philox words of fa_philox.hpp); with a
+// caller mask (the blog page "Flash Attention", Algorithm 2: S_masked = mask(S)) the
+// softmax phase sets the hidden scores to -inf from the mask words, loaded one tile
+// ahead, and a row that sees no key ends with O = 0 and L = -inf.
 #pragma once
 
 #include <type_traits>
@@ -82,7 +85,7 @@ struct TilePP {
 constexpr int kWaitLds = 0xC07F;  // lgkmcnt(0)
 constexpr int kWaitAll = 0x0070;  // vmcnt(0) lgkmcnt(0)
 
-template <typename T, bool CAUSAL, bool SPLIT, bool DROP = false>
+template <typename T, bool CAUSAL, bool SPLIT, bool DROP = false, bool MASK = false>
 __global__ __launch_bounds__(TilePP::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_fwd_pp_kernel(const FwdParams<T> prm)
 {
@@ -152,6 +155,20 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     auto load_v = [&](int t, int slot) { load_v_block<D>(Vh, t, Nks, v_kg, v_dq, vreg[slot]); };
     auto write_vt = [&](int lds_off, int slot) {
         store_vt_block<P::VTSTR>(smem + lds_off, v_kg, v_dq, vreg[slot]);
+    };
+
+    // ---- caller mask: this lane's row of the head's mask slice, the words of one tile
+    // loaded a tile ahead (slot = tile % 2); the workgroup's rows bound the resource
+    static_assert(!(MASK && SPLIT), "the masked forward is not split");
+    const __amdgpu_buffer_rsrc_t mrs = mask_rsrc(MASK ? mask_slice(prm, bh) : nullptr, q0, P::BR, Nq,
+                                                 MASK ? prm.mask_w : 0);
+    int mrow_off = 0;
+    uint32_t mwd[2][2] = {{0u, 0u}, {0u, 0u}};
+    if (MASK)
+        mrow_off = (my_q - q0) * prm.mask_w * 4;
+    auto load_mask = [&](int t, int slot) {
+        mwd[slot][0] = __builtin_amdgcn_raw_buffer_load_b32(mrs, mrow_off + 8 * t, 0, 0);
+        mwd[slot][1] = __builtin_amdgcn_raw_buffer_load_b32(mrs, mrow_off + 8 * t + 4, 0, 0);
     };
 
     const int kbase = ql * P::KSTR + hh * 16;
@@ -269,7 +286,9 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
         if (__builtin_amdgcn_ballot_w64(mx > thr) != 0) {
             const float mh = mx * c2;  // c2 > 0: max commutes with the scale
             const float m_new = fmaxf(m2, fmaxf(mh, swap_halves(mh)));
-            alpha = exp2_fast(m2 - m_new);  // 0 on a wave's first tile (m2 = -inf)
+            // 0 on a row's first visible tile (m2 = -inf); 1 for a row that has seen no
+            // visible key yet (a caller mask can hide all of them)
+            alpha = m_new == neg_inf() ? 1.f : exp2_fast(m2 - m_new);
             rescale = true;
             ls0 *= alpha;
             ls1 *= alpha;
@@ -315,10 +334,13 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     };
     // softmax phase of tile u; forced inline, since with dropout the compiler would
     // otherwise emit it as a function and keep the captured state in scratch memory
-    auto softmax = [&](int u, auto UPD) __attribute__((always_inline)) {
+    auto softmax = [&](int u, auto UPD, auto R) __attribute__((always_inline)) {
+        constexpr int r = decltype(R)::value;
         if (u < n_w) {
             if (needs_mask(u))
                 mask_tile(u);
+            if (MASK)
+                apply_mask_words(s, mwd[r & 1][0], mwd[r & 1][1], hh);
             update_max();
             exp_sum_pack();
             if (decltype(UPD)::value)
@@ -375,6 +397,8 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     auto stage = [&](int u, auto R) {
         constexpr int r = decltype(R)::value;
         __builtin_amdgcn_s_setprio(0);
+        if (MASK && u + 1 < n_w)
+            load_mask(u + 1, (r + 1) & 1);
         if (u + 2 < nkt) {
             load_v(u + 2, r & 1);
             stage_k(u + 2, ((r + 2) % P::NKB) * P::KT);
@@ -405,6 +429,8 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
         load_v(0, 0);
     if (1 < nkt)
         load_v(1, 1);
+    if (MASK && 0 < n_w)
+        load_mask(0, 0);
     barrier(true);
     {
         const char* const qrow = sm + P::KT + (qw0 - q0 + ql) * P::KSTR + hh * 16;
@@ -432,7 +458,7 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
         scores_only(0);
     barrier(true);
     stage(0, std::integral_constant<int, 0>{});
-    softmax(0, std::false_type{});
+    softmax(0, std::false_type{}, std::integral_constant<int, 0>{});
     barrier(false);
     // unrolled by 6 = lcm(3 K buffers, 2 V^T buffers), so that every buffer offset
     // and register slot is a constant of the code
@@ -441,7 +467,8 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
         mfma(j, R);
         barrier(true);
         stage(j + 1, std::integral_constant<int, (r + 1) % 6>{});
-        softmax(j + 1, std::integral_constant<bool, (r & 1) == 0>{});  // odd tiles
+        softmax(j + 1, std::integral_constant<bool, (r & 1) == 0>{},  // odd tiles
+                std::integral_constant<int, (r + 1) % 6>{});
         barrier(false);
     };
     for (int j = 0; j < nkt; j += 6) {
@@ -505,7 +532,8 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     // O rounded to T goes through this wave's own LDS rows (the K and V^T buffers are
     // free after the last barrier), so that each store writes four whole rows of O
     // rather than 16-byte pieces of 32 rows
-    const float inv = (DROP ? prm.drop_keep_scale : 1.0f) / lrt;
+    // a row that saw no visible key (only with a caller mask): O = 0, L = -inf
+    const float inv = (MASK && !(lrt > 0.f)) ? 0.f : (DROP ? prm.drop_keep_scale : 1.0f) / lrt;
     char* const ost = smem + wave * 32 * P::OSTR;
 #pragma unroll
     for (int db = 0; db < P::DB; ++db)
@@ -527,7 +555,8 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
             *reinterpret_cast<u32x4*>(ohead + (size_t)(qw0 + r) * D + 8 * ch) = piece;
     }
     if (hh == 0 && my_q < Nq)
-        prm.lse[(size_t)bh * Nq + my_q] = (m2 + log2_fast(lt)) * kLn2;
+        prm.lse[(size_t)bh * Nq + my_q] =
+            (MASK && !(lt > 0.f)) ? neg_inf() : (m2 + log2_fast(lt)) * kLn2;
 }
 
 }  // namespace fa

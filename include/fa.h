@@ -90,6 +90,30 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    float scale, fa_dtype_t dtype, fa_stream_t stream);
 
 /*
+ * fa_fwd_masked — fa_fwd with a caller's boolean mask on the scores: the "Flash
+ * Attention" blog page (blog.cyberangel.work), Algorithm 2, S_masked = mask(S) before
+ * the softmax.  A hidden (q, k) gets S[q, k] = -inf, on top of the causal rule when
+ * causal = 1 (a key must be allowed by both).
+ *
+ *   mask        DEVICE buffer of uint32 words [mask_b, mask_h, Nq, W], W = ceil(Nk / 32),
+ *               4-byte aligned, owned by the caller: row (b, h, q) holds key k in bit
+ *               k % 32 of word k / 32, set = visible (bits for keys >= Nk are ignored)
+ *   mask_b      1 (one mask for every batch) or B
+ *   mask_h      1 (one mask for every head) or H
+ *   other arguments as fa_fwd.
+ *
+ * A query row with no visible key has no softmax; it gets O = 0 and L = -inf (the
+ * identity of the (+) merge of partial states, as fa_fwd_split's empty ranges).
+ * Behaviour, limits and errors as fa_fwd (FA_ERR_INVALID_ARG also for a null or
+ * misaligned mask or mask_b / mask_h outside {1, B} / {1, H}); every dtype and d of
+ * fa_fwd.  Deterministic.
+ */
+fa_status_t fa_fwd_masked(const void* q, const void* k, const void* v, const uint32_t* mask,
+                          int64_t mask_b, int64_t mask_h, void* o, float* lse, int64_t B,
+                          int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal, float scale,
+                          fa_dtype_t dtype, fa_stream_t stream);
+
+/*
  * fa_fwd_split — the same result as fa_fwd, computed over key ranges in parallel and
  * merged; for grids that fa_fwd leaves under-filled (few heads, short query
  * sequences, long key sequences).

@@ -308,3 +308,28 @@ def test_split_static_limit_matches_header():
     m = re.search(r"#define FA_STATIC_SCRATCH_BYTES \((\d+)LL << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == fa.FA_STATIC_SCRATCH_BYTES
     assert fa.fa_status_str(fa.FA_ERR_SCRATCH) == "FA_ERR_SCRATCH"
+
+
+def _masked(**kw):
+    a = dict(q=P, k=P, v=P, mask=P, mask_b=1, mask_h=1, o=P, lse=P, B=2, H=3, Nq=64, Nk=100,
+             d=128, causal=0, scale=0.125, dtype=fa.FA_DTYPE_BF16, stream=0)
+    a.update(kw)
+    return fa.fa_fwd_masked_raw(**a)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(mask=0), fa.FA_ERR_INVALID_ARG),
+    (dict(mask=P + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(mask_b=0), fa.FA_ERR_INVALID_ARG),
+    (dict(mask_b=3), fa.FA_ERR_INVALID_ARG),
+    (dict(mask_h=2), fa.FA_ERR_INVALID_ARG),
+    (dict(mask_h=4), fa.FA_ERR_INVALID_ARG),
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=0), fa.FA_OK),
+    (dict(B=0, q=0, k=0, v=0, o=0, lse=0, mask=0), fa.FA_OK),
+])
+def test_masked_validation_before_any_hip_call(kw, want):
+    assert _masked(**kw) == want
