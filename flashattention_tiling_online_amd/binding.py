@@ -19,8 +19,9 @@ FA_STATIC_SCRATCH_BYTES = 64 << 20  # include/fa.h
 
 # symbols include/fa.h declares
 EXPORTS = ("fa_fwd", "fa_fwd_masked", "fa_fwd_split", "fa_fwd_split_workspace",
-           "fa_fwd_split_static", "fa_merge", "fa_split_hint", "fa_bwd", "fa_bwd_workspace",
-           "fa_fwd_dropout", "fa_bwd_dropout", "fa_status_str", "fa_tile_rows")
+           "fa_fwd_split_static", "fa_merge", "fa_split_hint", "fa_bwd", "fa_bwd_masked",
+           "fa_bwd_workspace", "fa_fwd_dropout", "fa_bwd_dropout", "fa_status_str",
+           "fa_tile_rows")
 
 _lib = None
 
@@ -67,6 +68,10 @@ def lib() -> ctypes.CDLL:
                                                       ctypes.c_float, ctypes.c_int,
                                                       ctypes.c_void_p, i64, ctypes.c_void_p]
         L.fa_bwd.restype = ctypes.c_int
+        L.fa_bwd_masked.argtypes = [ctypes.c_void_p] * 4 + [i64, i64] + [ctypes.c_void_p] * 6 + [
+            i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p,
+            i64, ctypes.c_void_p]
+        L.fa_bwd_masked.restype = ctypes.c_int
         L.fa_bwd_workspace.argtypes = [i64, i64, i64, i64]
         L.fa_bwd_workspace.restype = i64
         drop = [ctypes.c_float, ctypes.c_uint64]
@@ -131,6 +136,16 @@ def fa_bwd_raw(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk:
     """Direct call of fa_bwd with integer device pointers; returns the status code."""
     return lib().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, int(causal),
                         float(scale), int(dtype), workspace, int(workspace_bytes), stream)
+
+
+def fa_bwd_masked_raw(q: int, k: int, v: int, mask: int, mask_b: int, mask_h: int, o: int,
+                      lse: int, dout: int, dq: int, dk: int, dv: int, B: int, H: int, Nq: int,
+                      Nk: int, d: int, causal: int, scale: float, dtype: int, workspace: int,
+                      workspace_bytes: int, stream: int) -> int:
+    """Direct call of fa_bwd_masked with integer device pointers; returns the status code."""
+    return lib().fa_bwd_masked(q, k, v, mask, int(mask_b), int(mask_h), o, lse, dout, dq, dk, dv,
+                               B, H, Nq, Nk, d, int(causal), float(scale), int(dtype), workspace,
+                               int(workspace_bytes), stream)
 
 
 def fa_fwd_dropout_raw(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int,
@@ -335,6 +350,25 @@ def fa_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = No
                     dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Nq, Nk, d,
                     int(bool(causal)), scale, code, workspace.data_ptr(),
                     workspace.numel() * workspace.element_size(), stream.cuda_stream)
+    if st != FA_OK:
+        raise FAError(st)
+    return dq, dk, dv
+
+
+def fa_bwd_masked(q, k, v, mask, o, lse, dout, causal: bool = False, scale: float | None = None,
+                  dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """dQ, dK, dV of fa_fwd_masked's forward (fa_bwd_masked), with the same mask."""
+    (B, H, Nq, Nk, d), dq, dk, dv, workspace, stream = _bwd_buffers(
+        q, k, v, o, lse, dout, dq, dk, dv, workspace, stream)
+    mb, mh = _check_mask(mask, B, H, Nq, Nk, q.device)
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = fa_bwd_masked_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), mask.data_ptr(), mb, mh,
+                           o.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                           dk.data_ptr(), dv.data_ptr(), B, H, Nq, Nk, d, int(bool(causal)),
+                           scale, code, workspace.data_ptr(),
+                           workspace.numel() * workspace.element_size(), stream.cuda_stream)
     if st != FA_OK:
         raise FAError(st)
     return dq, dk, dv

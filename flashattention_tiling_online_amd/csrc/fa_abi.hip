@@ -594,13 +594,18 @@ extern "C" int fa_split_hint(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
 
 namespace {
 
-template <typename T, int D, bool C, bool DR>
+template <typename T, int D, bool C, bool DR, bool MK>
 hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* o,
                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
                         int64_t BH, int64_t Nq, int64_t Nk, float scale, float* delta,
-                        hipStream_t stream, const Dropout& drop)
+                        hipStream_t stream, const Dropout& drop, const MaskArg* mask)
 {
     fa::BwdParams<T> prm;
+    prm.mask = mask ? mask->words : nullptr;
+    prm.mask_sb = mask ? mask->sb : 0;
+    prm.mask_sh = mask ? mask->sh : 0;
+    prm.mask_w = mask ? mask->w : 0;
+    prm.H = mask ? mask->H : 1;
     prm.q = static_cast<const T*>(q);
     prm.k = static_cast<const T*>(k);
     prm.v = static_cast<const T*>(v);
@@ -635,39 +640,43 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
     void* args[] = {(void*)&prm};
     using PK = fa::DkvTile<D>;
     prm.n_tiles = (int)((Nk + PK::KEYS - 1) / PK::KEYS);  // dK, dV (zeros when Nq == 0)
-    err = hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dkv_kernel<T, D, C, DR>),
+    err = hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dkv_kernel<T, D, C, DR, MK>),
                           dim3((unsigned)(prm.n_tiles * BH)), dim3(PK::NT), args, 0, stream);
     if (err != hipSuccess || rows == 0)
         return err;
     using PQ = fa::DqTile<D>;
     prm.n_tiles = (int)((Nq + PQ::ROWS - 1) / PQ::ROWS);  // dQ
-    return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dq_kernel<T, D, C, DR>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dq_kernel<T, D, C, DR, MK>),
                            dim3((unsigned)(prm.n_tiles * BH)), dim3(PQ::NT), args, 0, stream);
 }
 
-template <typename T, bool DR>
+template <typename T, bool DR, bool MK>
 hipError_t launch_bwd_dr(int64_t d, int causal, const void* q, const void* k, const void* v,
                          const void* o, const float* lse, const void* dout, void* dq, void* dk,
                          void* dv, int64_t BH, int64_t Nq, int64_t Nk, float scale, float* delta,
-                         hipStream_t s, const Dropout& dr)
+                         hipStream_t s, const Dropout& dr, const MaskArg* mk)
 {
     if (d == 128)
-        return causal ? launch_bwd_t<T, 128, true, DR>(q, k, v, o, lse, dout, dq, dk, dv, BH, Nq, Nk, scale, delta, s, dr)
-                      : launch_bwd_t<T, 128, false, DR>(q, k, v, o, lse, dout, dq, dk, dv, BH, Nq, Nk, scale, delta, s, dr);
-    return causal ? launch_bwd_t<T, 64, true, DR>(q, k, v, o, lse, dout, dq, dk, dv, BH, Nq, Nk, scale, delta, s, dr)
-                  : launch_bwd_t<T, 64, false, DR>(q, k, v, o, lse, dout, dq, dk, dv, BH, Nq, Nk, scale, delta, s, dr);
+        return causal ? launch_bwd_t<T, 128, true, DR, MK>(q, k, v, o, lse, dout, dq, dk, dv, BH, Nq, Nk, scale, delta, s, dr, mk)
+                      : launch_bwd_t<T, 128, false, DR, MK>(q, k, v, o, lse, dout, dq, dk, dv, BH, Nq, Nk, scale, delta, s, dr, mk);
+    return causal ? launch_bwd_t<T, 64, true, DR, MK>(q, k, v, o, lse, dout, dq, dk, dv, BH, Nq, Nk, scale, delta, s, dr, mk)
+                  : launch_bwd_t<T, 64, false, DR, MK>(q, k, v, o, lse, dout, dq, dk, dv, BH, Nq, Nk, scale, delta, s, dr, mk);
 }
 
+// dropout and a caller mask are not combined (fa_bwd_dropout has no mask argument)
 template <typename T>
 hipError_t launch_bwd_d(int64_t d, int causal, const void* q, const void* k, const void* v,
                         const void* o, const float* lse, const void* dout, void* dq, void* dk,
                         void* dv, int64_t BH, int64_t Nq, int64_t Nk, float scale, float* delta,
-                        hipStream_t s, const Dropout& dr)
+                        hipStream_t s, const Dropout& dr, const MaskArg* mk)
 {
-    return dr.t > 0 ? launch_bwd_dr<T, true>(d, causal, q, k, v, o, lse, dout, dq, dk, dv, BH, Nq,
-                                             Nk, scale, delta, s, dr)
-                    : launch_bwd_dr<T, false>(d, causal, q, k, v, o, lse, dout, dq, dk, dv, BH,
-                                              Nq, Nk, scale, delta, s, dr);
+    if (mk)
+        return launch_bwd_dr<T, false, true>(d, causal, q, k, v, o, lse, dout, dq, dk, dv, BH, Nq,
+                                             Nk, scale, delta, s, dr, mk);
+    return dr.t > 0 ? launch_bwd_dr<T, true, false>(d, causal, q, k, v, o, lse, dout, dq, dk, dv,
+                                                    BH, Nq, Nk, scale, delta, s, dr, nullptr)
+                    : launch_bwd_dr<T, false, false>(d, causal, q, k, v, o, lse, dout, dq, dk, dv,
+                                                     BH, Nq, Nk, scale, delta, s, dr, nullptr);
 }
 
 }  // namespace
@@ -685,7 +694,8 @@ fa_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
                      const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H,
                      int64_t Nq, int64_t Nk, int64_t d, int causal, float scale,
                      fa_dtype_t dtype, void* workspace, int64_t workspace_bytes,
-                     fa_stream_t stream, const Dropout& drop)
+                     fa_stream_t stream, const Dropout& drop, const uint32_t* mask = nullptr,
+                     int64_t mask_b = 0, int64_t mask_h = 0, bool masked = false)
 {
     if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
         return FA_ERR_INVALID_ARG;
@@ -716,14 +726,21 @@ fa_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
     if (Nq * d > lim || Nk * d > lim || B * H > lim || B * H * ((Nq + 127) / 128) > lim ||
         B * H * ((Nk + 127) / 128) > lim || B * H * Nq / 8 > lim)
         return FA_ERR_INVALID_ARG;
+    MaskArg mk;
+    if (masked && Nq > 0) {
+        const fa_status_t st = check_mask(mask, mask_b, mask_h, B, H, Nq, Nk, &mk);
+        if (st != FA_OK)
+            return st;
+    }
+    const MaskArg* mkp = (masked && Nq > 0) ? &mk : nullptr;
     const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     float* delta = static_cast<float*>(workspace);
     const hipError_t err =
         dtype == FA_DTYPE_BF16
             ? launch_bwd_d<__bf16>(d, causal, q, k, v, o, lse, dout, dq, dk, dv, B * H, Nq, Nk,
-                                   scale, delta, hs, drop)
+                                   scale, delta, hs, drop, mkp)
             : launch_bwd_d<_Float16>(d, causal, q, k, v, o, lse, dout, dq, dk, dv, B * H, Nq, Nk,
-                                     scale, delta, hs, drop);
+                                     scale, delta, hs, drop, mkp);
     return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -737,6 +754,19 @@ extern "C" fa_status_t fa_bwd(const void* q, const void* k, const void* v, const
 {
     return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, causal, scale, dtype,
                     workspace, workspace_bytes, stream, Dropout{0u, 0u});
+}
+
+extern "C" fa_status_t fa_bwd_masked(const void* q, const void* k, const void* v,
+                                     const uint32_t* mask, int64_t mask_b, int64_t mask_h,
+                                     const void* o, const float* lse, const void* dout, void* dq,
+                                     void* dk, void* dv, int64_t B, int64_t H, int64_t Nq,
+                                     int64_t Nk, int64_t d, int causal, float scale,
+                                     fa_dtype_t dtype, void* workspace, int64_t workspace_bytes,
+                                     fa_stream_t stream)
+{
+    return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, causal, scale, dtype,
+                    workspace, workspace_bytes, stream, Dropout{0u, 0u}, mask, mask_b, mask_h,
+                    true);
 }
 
 extern "C" fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,

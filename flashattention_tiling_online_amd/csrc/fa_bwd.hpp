@@ -21,7 +21,9 @@
 // Both main kernels stage row tiles and transposed tiles through LDS in the layouts
 // of fa_tiles.hpp, each thread loading one 4x4 block per tensor one tile ahead and
 // writing it in both layouts; exp is exp2 with scale * log2(e) folded into one FMA
-// and L taken in base 2.
+// and L taken in base 2.  With a caller mask (the blog page's Algorithm 4 recomputes P
+// from mask(S)) a hidden (query, key) gets P = 0, which also covers the rows with no
+// visible key (L = -inf, no gradient).
 #pragma once
 
 #include "fa_philox.hpp"
@@ -46,6 +48,11 @@ struct BwdParams {
     float c2;         // scale * log2(e)
     float scale;
     DropParams drop;  // dropout on P (dropout instantiations only)
+    // caller mask (masked instantiations only), as in FwdParams: rows of mask_w words,
+    // head bh = b * H + h at mask + b * mask_sb + h * mask_sh
+    const uint32_t* mask;
+    int64_t mask_sb, mask_sh;
+    int mask_w, H;
 };
 
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -102,7 +109,8 @@ struct DkvTile {
     static constexpr int DOT = QT + D * TSTR;
     static constexpr int LS = DOT + D * TSTR;
     static constexpr int DS = LS + TILE * 4;
-    static constexpr int LDS = DS + TILE * 4;
+    static constexpr int MS = DS + TILE * 4;     // caller-mask words: [4 key words][64 queries]
+    static constexpr int LDS = MS + 4 * TILE * 4;
     // thread blocks of 4 rows x 4 columns per staged [64, D] tile: 16 x D/4
     static constexpr int BLOCKS = 16 * (D / 4);
     // partial accumulators of the second query half, exchanged at the end
@@ -129,7 +137,7 @@ __device__ __forceinline__ void store_row_block(char* dst, int kg, int dq, const
         *reinterpret_cast<u32x2*>(dst + (4 * kg + m) * RSTR + 8 * dq) = r[m];
 }
 
-template <typename T, int D, bool CAUSAL, bool DROP = false>
+template <typename T, int D, bool CAUSAL, bool DROP = false, bool MASK = false>
 __global__ __launch_bounds__(DkvTile<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_bwd_dkv_kernel(const BwdParams<T> prm)
 {
@@ -160,6 +168,7 @@ void fa_bwd_dkv_kernel(const BwdParams<T> prm)
     const T* dOh = prm.dout + (size_t)bh * Nq * D;
     const float* Lh = prm.lse + (size_t)bh * Nq;
     const float* Dh = prm.delta + (size_t)bh * Nq;
+    const uint32_t* mslice = MASK ? mask_slice(prm, bh) : nullptr;
 
     // K and V rows of the workgroup's keys, resident for the whole loop (rows past Nk
     // read as zero; their gradients are not stored)
@@ -221,6 +230,14 @@ void fa_bwd_dkv_kernel(const BwdParams<T> prm)
             reinterpret_cast<float*>(smem + P::LS)[tid] = q < Nq ? Lh[q] * kLog2e : __builtin_inff();
             reinterpret_cast<float*>(smem + P::DS)[tid] = q < Nq ? Dh[q] : 0.f;
         }
+        if (MASK && tid < 4 * P::TILE) {
+            // word kw of query row q: the bits of keys k0 + 32 kw .. +31 (rows past Nq and
+            // words past the row read as 0)
+            const int q = i * P::TILE + (tid >> 2), kw = tid & 3;
+            const int word = k0 / 32 + kw;
+            reinterpret_cast<uint32_t*>(smem + P::MS)[kw * P::TILE + (tid >> 2)] =
+                (q < Nq && word < prm.mask_w) ? mslice[(size_t)q * prm.mask_w + word] : 0u;
+        }
     };
 
     const int rbase = kl * P::RSTR + hh * 16;   // row-tile operand: row kl, chunk 8hh
@@ -263,6 +280,9 @@ void fa_bwd_dkv_kernel(const BwdParams<T> prm)
             const int qo = 32 * qh + 8 * g + 4 * hh;
             const f32x4 l2 = *reinterpret_cast<const f32x4*>(sm + P::LS + qo * 4);
             const f32x4 dd = *reinterpret_cast<const f32x4*>(sm + P::DS + qo * 4);
+            u32x4 mw = {0u, 0u, 0u, 0u};
+            if (MASK)
+                mw = *reinterpret_cast<const u32x4*>(sm + P::MS + (kblk * P::TILE + qo) * 4);
             uint32_t bytes = 0;
             if (DROP)
                 bytes = dw[g];
@@ -272,6 +292,8 @@ void fa_bwd_dkv_kernel(const BwdParams<T> prm)
                 float p = exp2_fast(fmaf(s[r], prm.c2, -l2[e]));
                 if (diag && my_k > i * P::TILE + qo + e)
                     p = 0.f;  // key after the query
+                if (MASK && !((mw[e] >> kl) & 1u))
+                    p = 0.f;  // key hidden by the caller's mask (also for a row with L = -inf)
                 if (DROP) {
                     const float z = drop_keep(bytes, e, prm.drop.t) ? prm.drop.keep_scale : 0.f;
                     pp[r >> 3][r & 7] = (T)(p * z);
@@ -387,7 +409,7 @@ struct DqTile {
     static_assert(NT == 4 * D, "one 4x4 block of K per thread");
 };
 
-template <typename T, int D, bool CAUSAL, bool DROP = false>
+template <typename T, int D, bool CAUSAL, bool DROP = false, bool MASK = false>
 __global__ __launch_bounds__(DqTile<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_bwd_dq_kernel(const BwdParams<T> prm)
 {
@@ -455,6 +477,19 @@ void fa_bwd_dq_kernel(const BwdParams<T> prm)
     const float l2 = my_q < Nq ? prm.lse[(size_t)bh * Nq + my_q] * kLog2e : 0.f;
     const float dd = my_q < Nq ? prm.delta[(size_t)bh * Nq + my_q] : 0.f;
 
+    // caller mask: this lane's row, the two words of a key tile loaded a tile ahead
+    // (words past the row and rows past Nq read as 0 through the resource's bound)
+    const __amdgpu_buffer_rsrc_t mrs = mask_rsrc(MASK ? mask_slice(prm, bh) : nullptr, q0, P::ROWS,
+                                                 Nq, MASK ? prm.mask_w : 0);
+    const int mrow_off = MASK ? (my_q - q0) * prm.mask_w * 4 : 0;
+    uint32_t mw[2] = {0u, 0u};
+    auto load_mask = [&](int t) {
+        mw[0] = __builtin_amdgcn_raw_buffer_load_b32(mrs, mrow_off + 8 * t, 0, 0);
+        mw[1] = __builtin_amdgcn_raw_buffer_load_b32(mrs, mrow_off + 8 * t + 4, 0, 0);
+    };
+    if (MASK && 0 < n_w)
+        load_mask(0);
+
     f32x16 dqt[P::DB];
 #pragma unroll
     for (int db = 0; db < P::DB; ++db)
@@ -495,6 +530,15 @@ void fa_bwd_dq_kernel(const BwdParams<T> prm)
         const int key0 = j * P::TILE;
         const bool mask = (key0 + P::TILE > Nk) || (CAUSAL && key0 + P::TILE - 1 > qw0);
         const int last = CAUSAL ? min(Nk - 1, my_q) : Nk - 1;
+        // this lane's caller-mask bits of the tile, shifted so that register r of block kb
+        // finds its key at bit 8 (r / 4) + r % 4 of cm[kb]; then the next tile's words
+        uint32_t cm[2] = {~0u, ~0u};
+        if (MASK) {
+            cm[0] = mw[0] >> (4 * hh);
+            cm[1] = mw[1] >> (4 * hh);
+            if (j + 1 < n_w)
+                load_mask(j + 1);
+        }
         vec ps[4];
         uint32_t dw[8];  // group 2cc + g: keys key0 + 16cc + 8g + 4hh + 0..3
         if (DROP)
@@ -513,6 +557,8 @@ void fa_bwd_dq_kernel(const BwdParams<T> prm)
                 float p = exp2_fast(fmaf(st[kb][r], prm.c2, -l2));
                 if (mask && key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3) > last)
                     p = 0.f;
+                if (MASK && !((cm[kb] >> (8 * (r >> 2) + (r & 3))) & 1u))
+                    p = 0.f;  // key hidden by the caller's mask (also for a row with L = -inf)
                 float dpz = dpt[kb][r];
                 if (DROP)
                     dpz *= drop_keep(bytes[e >> 2], e & 3, prm.drop.t) ? prm.drop.keep_scale : 0.f;

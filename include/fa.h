@@ -249,6 +249,21 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
 int64_t fa_bwd_workspace(int64_t B, int64_t H, int64_t Nq, int64_t d);
 
 /*
+ * fa_bwd_masked — fa_bwd for the forward of fa_fwd_masked: the "Flash Attention" blog
+ * page's Algorithm 4 recomputes P from mask(S), so a hidden (q, k) has P = 0 and adds
+ * nothing to dQ, dK or dV; a query row with no visible key (L = -inf) has no gradient
+ * (dQ row 0).  mask, mask_b, mask_h: as fa_fwd_masked (the same array the forward
+ * used; with Nq == 0 it is not read and may be NULL).  Other arguments, behaviour and
+ * errors as fa_bwd; dtype BF16 or F16.
+ */
+fa_status_t fa_bwd_masked(const void* q, const void* k, const void* v, const uint32_t* mask,
+                          int64_t mask_b, int64_t mask_h, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                          int64_t Nq, int64_t Nk, int64_t d, int causal, float scale,
+                          fa_dtype_t dtype, void* workspace, int64_t workspace_bytes,
+                          fa_stream_t stream);
+
+/*
  * fa_fwd_dropout / fa_bwd_dropout — the forward and backward above with dropout on P.
  * The "Flash Attention" blog page (Algorithm 2) drops entries of P after the softmax
  * and multiplies the kept ones by 1/(1 - p): O = (P o Z) V with L unchanged (the

@@ -33,9 +33,9 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import flashattention_tiling_online_amd as fa  # noqa: E402
+import bwd_bounds  # noqa: E402
 from parity_util import DEV, say, to_dev, to_host  # noqa: E402
 
-BWD_BOUND = {"bf16": (2e-2, 5e-2), "f16": (3e-3, 1e-2)}
 
 
 def threshold(p):
@@ -167,14 +167,17 @@ def test_dropout_invalid_arguments_raise():
 # backward
 # ---------------------------------------------------------------------------
 
-def check_grad(name, got64, ref64, dtype):
-    cf, cm = BWD_BOUND[dtype]
-    err = got64 - ref64
-    rel_f = np.linalg.norm(err) / max(np.linalg.norm(ref64), 1e-300)
-    rel_m = np.abs(err).max() / max(np.abs(ref64).max(), 1e-300)
-    say(f"    {name}: |d|_F/|ref|_F={rel_f:.2e}  max|d|/max|ref|={rel_m:.2e}")
-    assert np.isfinite(got64).all()
-    assert rel_f <= cf and rel_m <= cm
+def drop_factors(w, p, seed, bh):
+    """Z of head bh: keep_scale where the oracle's generator keeps (q, k), else 0."""
+    keep = oracle.dropout_keep(seed, threshold(p), bh, w.Nq, w.Nk)
+    return keep.astype(np.float64) * keep_scale(p)
+
+
+def check_grads(w, p, seed, q, k, v, dout, bh, got, ref):
+    """Element-wise bounds of tests/bwd_bounds.py with the dropout factors Z."""
+    a = bwd_bounds.scales(w, q, k, v, dout, bh, z=drop_factors(w, p, seed, bh))
+    for nm, g, r, s in zip(("dq", "dk", "dv"), got, ref, a):
+        bwd_bounds.check(f"{nm} head {bh}", g, r, s, w.dtype, say)
 
 
 BWD_SHAPES = [
@@ -203,8 +206,7 @@ def test_dropout_bwd_all_rows(spec, p):
     for bh in range(B * H):
         ref = oracle.bwd_head_dropout_f64(q, k, v, dout, causal, w.scale, dt, threshold(p),
                                           rng_seed, bh)
-        for nm, a, b in zip(("dq", "dk", "dv"), g, ref):
-            check_grad(f"{nm} head {bh}", a[bh], b, dt)
+        check_grads(w, p, rng_seed, q, k, v, dout, bh, [x[bh] for x in g], ref)
 
 
 def test_dropout_bwd_zero_probability_is_fa_bwd():

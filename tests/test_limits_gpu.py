@@ -152,7 +152,7 @@ def test_backward_largest_offsets(causal):
     dV and the placed dQ rows equal the fp64 oracle's gradients of the small problem
     made of the placed rows (all 64 keys visible to each), within the backward's
     bounds, and the other dQ rows are exactly zero."""
-    from test_bwd_gpu import check_close  # noqa: E402
+    import bwd_bounds  # noqa: E402
     small = inputs.custom("limits_bwd", 1, H, N_PLACED, NK, D, "bf16", False, seed=63)
     say(f"[limits bwd] B=1 H={H} Nq={NQ} Nk={NK} d={D} bf16 causal={causal}; rows from {small.describe()}")
     q_s, k, v = inputs.make_qkv(small)
@@ -176,9 +176,10 @@ def test_backward_largest_offsets(causal):
         got_dk = oracle.widen(to_host(dk[0, h], "bf16"), "bf16")
         got_dv = oracle.widen(to_host(dv[0, h], "bf16"), "bf16")
         say(f"  head {h}")
-        check_close("dq (placed rows)", got_dq, ref_dq, "bf16")
-        check_close("dk", got_dk, ref_dk, "bf16")
-        check_close("dv", got_dv, ref_dv, "bf16")
+        a_q, a_k, a_v = bwd_bounds.scales(small, q_s, k, v, do_s, h)
+        bwd_bounds.check("dq (placed rows)", got_dq, ref_dq, a_q, "bf16", say)
+        bwd_bounds.check("dk", got_dk, ref_dk, a_k, "bf16", say)
+        bwd_bounds.check("dv", got_dv, ref_dv, a_v, "bf16", say)
         assert bool((dq[0, h].index_select(0, zero_rows) == 0).all())
     del tq, tdo, o, lse, dq
     torch.cuda.empty_cache()

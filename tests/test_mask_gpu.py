@@ -129,3 +129,61 @@ def test_masked_c4a_sample():
     words = inputs.pack_mask(vis)
     sel_bh, sel_row = inputs.sample_rows(w, 4, 256)
     assert check_masked(w, q, k, v, words, vis, sel_bh, sel_row) == 0
+
+
+# ---------------------------------------------------------------------------
+# backward with the same mask (fa_bwd_masked)
+# ---------------------------------------------------------------------------
+
+BWD_CASES = [
+    # (B, H, Nq, Nk, d, dtype, causal, kind, mask_b, mask_h, density)
+    (1, 2, 200, 333, 128, "bf16", False, "random", 1, 2, 0.5),
+    (2, 2, 257, 190, 64, "bf16", True, "empty_rows", 2, 1, 0.5),
+    (1, 3, 300, 260, 128, "f16", True, "sliding_window", 1, 1, 0.5),
+    (1, 2, 129, 400, 64, "f16", False, "key_padding", 1, 1, 0.5),
+    (1, 2, 384, 384, 128, "bf16", False, "block", 1, 2, 0.5),
+    (2, 2, 300, 300, 128, "bf16", True, "empty_rows", 2, 2, 0.2),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[f"{c[7]}_{c[5]}_d{c[4]}_{'c' if c[6] else 'n'}_{i}"
+                                                 for i, c in enumerate(BWD_CASES)])
+def test_masked_backward_all_rows(case):
+    import bwd_bounds
+    B, H, Nq, Nk, d, dt, causal, kind, mb, mh, dens = case
+    w = inputs.custom(f"mask_bwd_{kind}", B, H, Nq, Nk, d, dt, causal, seed=700 + Nq + Nk)
+    say(f"[mask bwd] {w.describe()} kind={kind} mask=[{mb},{mh}] density={dens}")
+    q, k, v = inputs.make_qkv(w)
+    dout = inputs.make_do(w)
+    vis = inputs.make_mask(kind, mb, mh, Nq, Nk, seed=Nq * 3 + Nk, density=dens, window=50,
+                           tile=32)
+    words = inputs.pack_mask(vis)
+    tq, tk, tv, tdo = (to_dev(a, dt) for a in (q, k, v, dout))
+    tm = mask_dev(words)
+    o, lse = fa.fa_fwd_masked(tq, tk, tv, tm, causal=causal, scale=w.scale)
+    dq, dk, dv = fa.fa_bwd_masked(tq, tk, tv, tm, o, lse, tdo, causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    g = [oracle.widen(to_host(t, dt), dt).reshape(B * H, -1, d) for t in (dq, dk, dv)]
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        hv = vis[b if mb > 1 else 0, h if mh > 1 else 0]
+        ref = oracle.bwd_head_masked_f64(q, k, v, dout, words, causal, w.scale, dt, bh)
+        a = bwd_bounds.scales(w, q, k, v, dout, bh, vis=hv)
+        say(f"  head {bh}")
+        for nm, got, r, s in zip(("dq", "dk", "dv"), g, ref, a):
+            bwd_bounds.check(nm, got[bh], r, s, dt, say)
+        live = (hv & (np.tril(np.ones((Nq, Nk), bool)) if causal else hv)).any(axis=1)
+        assert (g[0][bh][~live] == 0).all(), "a row with no visible key has no gradient"
+
+
+def test_masked_backward_all_visible_gives_fa_bwd_bits():
+    w = inputs.custom("mask_bwd_all", 1, 2, 300, 270, 128, "bf16", True, seed=71)
+    q, k, v = (to_dev(a, "bf16") for a in inputs.make_qkv(w))
+    dout = to_dev(inputs.make_do(w), "bf16")
+    tm = mask_dev(inputs.pack_mask(np.ones((1, 1, 300, 270), bool)))
+    o, lse = fa.fa_fwd(q, k, v, causal=True, scale=w.scale)
+    a = fa.fa_bwd(q, k, v, o, lse, dout, causal=True, scale=w.scale)
+    b = fa.fa_bwd_masked(q, k, v, tm, o, lse, dout, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))

@@ -25,7 +25,7 @@ import flashattention_tiling_online_amd as fa  # noqa: E402
 from parity_util import compare, say, to_dev, to_host  # noqa: E402
 from sweep_specs import BWD, DROP_BWD, DROP_FWD, FWD, SPLIT, workload  # noqa: E402
 from test_bwd_gpu import check_all_rows as bwd_check_all_rows  # noqa: E402
-from test_dropout_gpu import check_grad, compare_fwd, run_fwd, threshold  # noqa: E402
+from test_dropout_gpu import check_grads, compare_fwd, run_fwd, threshold  # noqa: E402
 
 
 P_DROP = (0.1, 0.3, 0.5, 0.9)
@@ -99,5 +99,4 @@ def test_sweep_dropout_bwd(spec):
     for bh in range(w.B * w.H):
         ref = oracle.bwd_head_dropout_f64(q, k, v, dout, w.causal, w.scale, w.dtype,
                                           threshold(p), rng_seed, bh)
-        for nm, a, b in zip(("dq", "dk", "dv"), g, ref):
-            check_grad(f"{nm} head {bh}", a[bh], b, w.dtype)
+        check_grads(w, p, rng_seed, q, k, v, dout, bh, [x[bh] for x in g], ref)
