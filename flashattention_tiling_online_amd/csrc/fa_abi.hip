@@ -169,6 +169,14 @@ const void* merge_fn(fa_dtype_t dtype, int64_t d)
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// a * b for non-negative a and b, INT64_MAX when the product does not fit: size checks
+// compare it with their limits, so an argument whose product would wrap is refused
+int64_t mul_sat(int64_t a, int64_t b)
+{
+    int64_t r;
+    return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
+}
+
 bool valid_dtype(fa_dtype_t dtype)
 {
     return dtype == FA_DTYPE_F32 || dtype == FA_DTYPE_F16 || dtype == FA_DTYPE_BF16;
@@ -205,7 +213,7 @@ fa_status_t check_fwd(const void* q, const void* k, const void* v, void* o, floa
 
     // size limits: in-head offsets are 32-bit, the grid is 1-D
     const int64_t lim = INT32_MAX;
-    if (Nq * d > lim || Nk * d > lim || B > lim || H > lim || B * H > lim)
+    if (mul_sat(Nq, d) > lim || mul_sat(Nk, d) > lim || mul_sat(B, H) > lim)
         return FA_ERR_INVALID_ARG;
     const int64_t n_qtiles = (Nq + L->rows - 1) / L->rows;
     if (n_qtiles * B * H > lim)
@@ -406,8 +414,11 @@ extern "C" int64_t fa_fwd_split_workspace(int64_t B, int64_t H, int64_t Nq, int6
     if (B < 0 || H < 0 || Nq < 0 || (d != 64 && d != 128) || n_splits < 1 ||
         n_splits > kMaxSplits)
         return -1;
-    const int64_t rows = B * H * Nq;
-    return round_up((int64_t)n_splits * rows * d * 4, kAlign) + (int64_t)n_splits * rows * 4;
+    const int64_t parts = mul_sat(mul_sat(mul_sat(B, H), Nq), n_splits);
+    const int64_t o_bytes = mul_sat(parts, d * 4);
+    if (o_bytes > INT64_MAX / 2)
+        return -1;  // no buffer of that size exists
+    return round_up(o_bytes, kAlign) + parts * 4;
 }
 
 namespace {
@@ -467,7 +478,7 @@ extern "C" fa_status_t fa_fwd_split(const void* q, const void* k, const void* v,
     const int s_eff = split_plan(Nk, n_splits, &tps);
     if (s_eff > 1) {
         const int64_t need = fa_fwd_split_workspace(B, H, Nq, d, n_splits);
-        if (!workspace || !aligned(workspace, 16) || workspace_bytes < need)
+        if (need < 0 || !workspace || !aligned(workspace, 16) || workspace_bytes < need)
             return FA_ERR_INVALID_ARG;
         if (!split_fits(L, B, H, Nq, s_eff))
             return FA_ERR_INVALID_ARG;
@@ -530,7 +541,8 @@ extern "C" fa_status_t fa_fwd_split_static(const void* q, const void* k, const v
     const int s_eff = split_plan(Nk, n_splits, &tps);
     void* ws = nullptr;
     if (s_eff > 1) {
-        if (fa_fwd_split_workspace(B, H, Nq, d, n_splits) > FA_STATIC_SCRATCH_BYTES)
+        const int64_t need = fa_fwd_split_workspace(B, H, Nq, d, n_splits);
+        if (need < 0 || need > FA_STATIC_SCRATCH_BYTES)
             return FA_ERR_SCRATCH;
         if (!split_fits(L, B, H, Nq, s_eff))
             return FA_ERR_INVALID_ARG;
@@ -551,14 +563,15 @@ extern "C" fa_status_t fa_merge(const float* o_parts, const float* lse_parts, in
         return FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128)
         return FA_ERR_UNSUPPORTED;
-    const int64_t rows = B * H * Nq;
+    const int64_t rows = mul_sat(mul_sat(B, H), Nq);
     if (rows == 0)
         return FA_OK;
     if (!o_parts || !lse_parts || !o || !lse)
         return FA_ERR_INVALID_ARG;
     if (!aligned(o_parts, 16) || !aligned(lse_parts, 4) || !aligned(o, 16) || !aligned(lse, 4))
         return FA_ERR_INVALID_ARG;
-    if ((rows + 7) / 8 > INT32_MAX)
+    // the grid is 1-D, 8 rows a workgroup; the parts' element offsets are 64-bit
+    if (rows > 8 * (int64_t)INT32_MAX || mul_sat(mul_sat(rows, n_parts), d) == INT64_MAX)
         return FA_ERR_INVALID_ARG;
     const hipError_t err = launch_merge(dtype, d, o_parts, lse_parts, n_parts, rows, o, lse,
                                         reinterpret_cast<hipStream_t>(stream));
@@ -574,12 +587,12 @@ extern "C" int fa_split_hint(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
         return 0;
     const int64_t cus = 256;
     const int64_t slots = cus * wgs_per_cu(dtype, d);
-    const int64_t wgs = B * H * ((Nq + L.rows - 1) / L.rows);
+    const int64_t wgs = mul_sat(mul_sat(B, H), Nq / L.rows + (Nq % L.rows != 0));
     if (wgs >= slots)
         return 1;
     // each range must keep enough key tiles to amortise its partial-state write and
     // the merge launch: 8 for the 16-bit kernels, 2 for the slower fp32 one
-    const int64_t nkt = (Nk + kKeyTile - 1) / kKeyTile;
+    const int64_t nkt = Nk / kKeyTile + (Nk % kKeyTile != 0);
     const int64_t min_tiles = dtype == FA_DTYPE_F32 ? 2 : 8;
     int64_t s = (slots + wgs - 1) / wgs;
     const int64_t most = nkt / min_tiles > 1 ? nkt / min_tiles : 1;
@@ -685,7 +698,8 @@ extern "C" int64_t fa_bwd_workspace(int64_t B, int64_t H, int64_t Nq, int64_t d)
 {
     if (B < 0 || H < 0 || Nq < 0 || (d != 64 && d != 128))
         return -1;
-    return round_up(B * H * Nq * 4, kAlign);
+    const int64_t bytes = mul_sat(mul_sat(mul_sat(B, H), Nq), 4);
+    return bytes > INT64_MAX / 2 ? -1 : round_up(bytes, kAlign);
 }
 
 namespace {
@@ -711,6 +725,14 @@ fa_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
         return FA_OK;  // nothing to compute
     if (Nk == 0)
         return FA_ERR_INVALID_ARG;  // queries without keys: the forward is undefined
+    // size limits: in-head offsets are 32-bit, the grids are 1-D (128-row tiles; the
+    // delta pass takes 8 rows a workgroup)
+    const int64_t lim = INT32_MAX;
+    if (mul_sat(Nq, d) > lim || mul_sat(Nk, d) > lim || mul_sat(B, H) > lim)
+        return FA_ERR_INVALID_ARG;
+    if (B * H * ((Nq + 127) / 128) > lim || B * H * ((Nk + 127) / 128) > lim ||
+        B * H * Nq / 8 > lim)
+        return FA_ERR_INVALID_ARG;
     if (!k || !v || !dk || !dv || !aligned(k, 16) || !aligned(v, 16) || !aligned(dk, 16) ||
         !aligned(dv, 16))
         return FA_ERR_INVALID_ARG;
@@ -722,10 +744,6 @@ fa_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
             workspace_bytes < fa_bwd_workspace(B, H, Nq, d))
             return FA_ERR_INVALID_ARG;
     }
-    const int64_t lim = INT32_MAX;
-    if (Nq * d > lim || Nk * d > lim || B * H > lim || B * H * ((Nq + 127) / 128) > lim ||
-        B * H * ((Nk + 127) / 128) > lim || B * H * Nq / 8 > lim)
-        return FA_ERR_INVALID_ARG;
     MaskArg mk;
     if (masked && Nq > 0) {
         const fa_status_t st = check_mask(mask, mask_b, mask_h, B, H, Nq, Nk, &mk);

@@ -30,14 +30,23 @@
 extern "C" {
 #endif
 
+/* Under C++ the two enums below have int as their fixed underlying type, so any int a
+ * C caller passes is a value of the type there too; the entry points refuse the ones
+ * they do not know (FA_ERR_INVALID_ARG). */
+#ifdef __cplusplus
+#define FA_ENUM_INT : int
+#else
+#define FA_ENUM_INT
+#endif
+
 /* Element type of q, k, v and o.  lse is always fp32. */
-typedef enum {
+typedef enum FA_ENUM_INT {
     FA_DTYPE_F32 = 0,  /* IEEE binary32 */
     FA_DTYPE_F16 = 1,  /* IEEE binary16 */
     FA_DTYPE_BF16 = 2  /* bfloat16 (upper half of binary32) */
 } fa_dtype_t;
 
-typedef enum {
+typedef enum FA_ENUM_INT {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative size, Nk = 0 with queries,
                                non-positive or non-finite scale, unknown dtype, size limit */
@@ -152,7 +161,8 @@ fa_status_t fa_fwd_split(const void* q, const void* k, const void* v, void* o, f
                          int64_t workspace_bytes, fa_stream_t stream);
 
 /* Workspace bytes fa_fwd_split needs for (B, H, Nq, d, n_splits); -1 for arguments
- * it would reject (negative sizes, d outside {64, 128}, n_splits outside 1 .. 256). */
+ * it would reject (negative sizes, d outside {64, 128}, n_splits outside 1 .. 256) and
+ * for sizes whose byte count does not fit in int64. */
 int64_t fa_fwd_split_workspace(int64_t B, int64_t H, int64_t Nq, int64_t d, int n_splits);
 
 /* Size of the library's static scratch buffer (fa_fwd_split_static), per GPU. */
@@ -244,8 +254,8 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
                    int64_t Nq, int64_t Nk, int64_t d, int causal, float scale, fa_dtype_t dtype,
                    void* workspace, int64_t workspace_bytes, fa_stream_t stream);
 
-/* Workspace bytes fa_bwd needs (D as fp32, rounded up to 256); -1 for negative sizes or
- * d outside {64, 128}. */
+/* Workspace bytes fa_bwd needs (D as fp32, rounded up to 256); -1 for negative sizes,
+ * d outside {64, 128}, or sizes whose byte count does not fit in int64. */
 int64_t fa_bwd_workspace(int64_t B, int64_t H, int64_t Nq, int64_t d);
 
 /*
