@@ -158,6 +158,29 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
 // Exchange with the lane 32 positions away (the other half of a wave64).
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+// x of lanes 0-31 (lo) and of lanes 32-63 (hi) of the same lane pair (l, l ^ 32), both in
+// every lane, from one v_permlane32_swap(x, x): its two results hold the low half of x
+// in both halves and the high half in both halves.  A VALU exchange: unlike a shuffle
+// (ds_bpermute) it does not queue behind other waves' LDS operand reads.  Combining lo
+// and hi with a commutative operation gives every lane of the pair the same bits.
+struct Halves {
+    float lo, hi;
+};
+__device__ __forceinline__ Halves halves(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float half_max(float x)
+{
+    const Halves h = halves(x);
+    return fmaxf(h.lo, h.hi);
+}
+__device__ __forceinline__ float half_sum(float x)
+{
+    const Halves h = halves(x);
+    return h.lo + h.hi;
+}
 
 }  // namespace fa

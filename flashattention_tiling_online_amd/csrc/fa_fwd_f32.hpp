@@ -157,7 +157,7 @@ void fa_fwd_f32_kernel(const FwdParams<float> prm)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 mx = fmaxf(mx, s[kb][r]);
-        mx = fmaxf(mx, swap_halves(mx));
+        mx = half_max(mx);
         const float m_new = fmaxf(m2, mx * c2);
         const bool none = (m_new == neg_inf());
         const float alpha = none ? 1.f : exp2_fast(m2 - m_new);
@@ -199,7 +199,7 @@ void fa_fwd_f32_kernel(const FwdParams<float> prm)
     // split: a row that saw no key of its range leaves the merge identity
     // (L = -inf, O = 0)
     const float lsum = l_done + l;
-    const float lt = lsum + swap_halves(lsum);
+    const float lt = half_sum(lsum);
     if (my_q < Nq) {
         const size_t row = SPLIT ? ((size_t)split * prm.bh_count + bh) * Nq + my_q
                                  : (size_t)bh * Nq + my_q;

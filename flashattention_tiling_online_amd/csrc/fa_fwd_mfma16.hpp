@@ -273,7 +273,7 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
     constexpr float kSlack = 8.0f;
     constexpr int kShift = 3;
     float thr2 = neg_inf();
-    auto half_max = [&](const f32x16* s) {
+    auto tile_max = [&](const f32x16* s) {
         float mx = s[0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -285,7 +285,7 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
     auto update_max = [&](float mx) {
         const float mh = mx * c2;  // c2 > 0: max commutes with the scale
         if (__builtin_amdgcn_ballot_w64(mh > thr2) != 0) {
-            const float m_new = fmaxf(m2, fmaxf(mh, swap_halves(mh)));
+            const float m_new = fmaxf(m2, fa::half_max(mh));
             // 0 on a row's first visible tile (m2 = -inf); 1 for a row that has seen no
             // visible key yet (a caller mask can hide all of them)
             const float alpha = m_new == neg_inf() ? 1.f : exp2_fast(m2 - m_new);
@@ -370,7 +370,7 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
         scores(P::K0, sa);
         if (MASK)
             apply_mask_words(sa, mwd[0][0], mwd[0][1], hh);
-        ma = half_max(sa);
+        ma = tile_max(sa);
     }
     __syncthreads();  // every wave has read K_0
     if (2 < nkt)
@@ -395,11 +395,11 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
             pv(pb, vc);
             if (MASK)
                 apply_mask_words(s_nxt, mwd[sl][0], mwd[sl][1], hh);
-            m_nxt = half_max(s_nxt);
+            m_nxt = tile_max(s_nxt);
         } else if (j < n_w) {
             if (needs_mask(j)) {
                 mask_tile(j, s_cur);
-                m_cur = half_max(s_cur);
+                m_cur = tile_max(s_cur);
             }
             update_max(m_cur);
             vec pb[4];
@@ -429,8 +429,8 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
     // split: O~ / l and L in fp32 into the partial buffers, and for a row that saw
     // no key of its range the identity of the merge, L = -inf with O = 0
     const float lsum = done[0] + l, lrsum = done[1] + lr;
-    const float lt = lsum + swap_halves(lsum);
-    const float lrt = lrsum + swap_halves(lrsum);
+    const float lt = half_sum(lsum);
+    const float lrt = half_sum(lrsum);
     // O goes through this wave's own LDS rows (the tile buffers are free after the
     // last barrier; the row sums lie past them), so that each store writes whole
     // rows rather than 8 or 16 bytes of 32 rows; fp32 partials 64 columns at a time

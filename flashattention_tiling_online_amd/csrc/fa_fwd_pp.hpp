@@ -285,7 +285,7 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
                 mx = fmaxf(mx, s[kb][r]);
         if (__builtin_amdgcn_ballot_w64(mx > thr) != 0) {
             const float mh = mx * c2;  // c2 > 0: max commutes with the scale
-            const float m_new = fmaxf(m2, fmaxf(mh, swap_halves(mh)));
+            const float m_new = fmaxf(m2, half_max(mh));
             // 0 on a row's first visible tile (m2 = -inf); 1 for a row that has seen no
             // visible key yet (a caller mask can hide all of them)
             alpha = m_new == neg_inf() ? 1.f : exp2_fast(m2 - m_new);
@@ -495,8 +495,8 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     // range the identity of the merge, L = -inf with O = 0
     const float lsum = l_done + (ls0 + ls1);
     const float lrsum = lr_done + (lrs0 + lrs1);
-    const float lt = lsum + swap_halves(lsum);
-    const float lrt = lrsum + swap_halves(lrsum);
+    const float lt = half_sum(lsum);
+    const float lrt = half_sum(lrsum);
     if (SPLIT) {
         // fp32 partial O through this wave's LDS rows as below, in two halves of 64
         // columns (256 bytes a row, like a row of T)
