@@ -22,6 +22,10 @@ namespace {
 constexpr int kKeyTile = 64;     // keys per tile in every kernel (the split granularity)
 constexpr int kMaxSplits = 256;  // most key ranges fa_fwd_split accepts
 constexpr int64_t kAlign = 256;  // alignment of the partial-L block in the workspace
+// d = 64 forward: key groups per workgroup when the grid of 128-row workgroups would
+// leave CUs without one (kSmallGridWgs or fewer workgroups)
+constexpr int kKeyGroups = 4;
+constexpr int64_t kSmallGridWgs = 256;
 
 struct Launch {
     const void* fn;  // device function address
@@ -34,6 +38,15 @@ Launch mfma16()
 {
     return Launch{reinterpret_cast<const void*>(&fa::fa_fwd_mfma16_kernel<T, D, C, S>),
                   fa::Tile16<D>::BR, fa::Tile16<D>::NT};
+}
+
+// d = 64 with KG key groups per workgroup (for grids too small to fill the chip)
+template <typename T, bool C>
+Launch mfma16_kg()
+{
+    return Launch{reinterpret_cast<const void*>(
+                      &fa::fa_fwd_mfma16_kernel<T, 64, C, false, false, false, kKeyGroups>),
+                  fa::Tile16<64, kKeyGroups>::BR, fa::Tile16<64, kKeyGroups>::NT};
 }
 
 template <int D, bool C, bool S>
@@ -329,6 +342,9 @@ extern "C" fa_status_t fa_fwd(const void* q, const void* k, const void* v, void*
         check_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, false, &L, &empty);
     if (st != FA_OK || empty)
         return st;
+    if (d == 64 && dtype != FA_DTYPE_F32 && B * H * ((Nq + L.rows - 1) / L.rows) <= kSmallGridWgs)
+        L = dtype == FA_DTYPE_BF16 ? (causal ? mfma16_kg<__bf16, true>() : mfma16_kg<__bf16, false>())
+                                   : (causal ? mfma16_kg<_Float16, true>() : mfma16_kg<_Float16, false>());
     const hipError_t err = launch_fwd_any(dtype, L, q, k, v, o, lse, nullptr, nullptr, B * H, Nq,
                                           Nk, 1, 0, scale, reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;

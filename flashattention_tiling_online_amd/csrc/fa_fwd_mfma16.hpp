@@ -16,6 +16,13 @@
 //     workgroup is 8 waves (256 rows) and fills a CU alone, for d = 64 it is 4 waves
 //     (128 rows) and two share a CU: either way each SIMD interleaves two waves, and
 //     each staged K/V tile serves as many query rows as fit;
+//   * key groups (d = 64, grids of at most 256 of those 128-row workgroups, which
+//     would leave CUs idle and run one wave per SIMD through all the key tiles): a
+//     workgroup is 2 query waves (64 rows) times 4 key groups, group g takes key
+//     tiles g, g + 4, ... with K/V buffers of its own, so each SIMD interleaves two
+//     waves and each wave's chain of tiles is a quarter as long; at the end the
+//     groups' (m, l, O~) states are folded with the blog page's (+) operator through
+//     LDS, and group 0 writes the result;
 //   * both contractions on v_mfma_f32_32x32x16_{bf16,f16}; S is computed
 //     transposed, S^T = K Q^T, so each lane owns ONE query (lane % 32) and 16 of
 //     the 32 keys of a 32-key block: the row max needs one exchange between the
@@ -52,40 +59,56 @@
 
 namespace fa {
 
-template <int D>
+template <int D, int KG = 1>
 struct Tile16 {
     // d = 128: 8 waves (256 query rows) share each staged K/V tile, one workgroup
     // per CU (2 waves per SIMD); d = 64: 4 waves (128 rows), two workgroups per CU,
-    // so that the small-d grids still cover the chip.
-    static constexpr int NW = D == 128 ? 8 : 4;  // waves per workgroup
-    static constexpr int BR = 32 * NW;           // query rows per workgroup
+    // so that the small-d grids still cover the chip.  KG > 1 (d = 64, for grids too
+    // small to give every CU a workgroup): 2 query waves (64 rows) times KG key groups;
+    // group g takes key tiles g, g + KG, g + 2 KG, ... with K/V buffers of its own,
+    // and the groups' states are merged by the (+) operator at the end.
+    static constexpr int NQW = D == 128 ? 8 : (KG == 1 ? 4 : 2);  // query waves
+    static constexpr int NW = NQW * KG;          // waves per workgroup
+    static constexpr int BR = 32 * NQW;          // query rows per workgroup
     static constexpr int BC = 64;                // keys per K/V tile
     static constexpr int NT = 64 * NW;           // threads per workgroup
+    static constexpr int GT = 64 * NQW;          // threads of one key group
     static constexpr int ROWB = D * 2;           // bytes per K/V row in memory
     static constexpr int KSTR = ROWB + 16;       // K row stride in LDS
     static constexpr int VTSTR = 2 * BC + 16;    // V^T row stride in LDS (one row per dim)
     static constexpr int KT = BC * KSTR;         // bytes of one K tile in LDS
     static constexpr int VT = D * VTSTR;         // bytes of one V^T tile in LDS
     static constexpr int KNB = KT / 1024;        // 1-KB DMA blocks per K tile
-    static constexpr int KPW = (KNB + NW - 1) / NW;  // K blocks per wave (at most)
-    static_assert(NT == 4 * D, "V staging: one 4-key x 4-dim block per thread");
+    static constexpr int KPW = (KNB + NQW - 1) / NQW;  // K blocks per wave (at most)
+    static constexpr int VPT = 4 * D / GT;       // 4-key x 4-dim V blocks per thread and tile
+    static_assert(VPT >= 1 && VPT * GT == 4 * D, "V staging: whole 4 x 4 blocks per thread");
     static constexpr int DC = D / 16;            // 16-wide d chunks of the S contraction
     static constexpr int DB = D / 32;            // 32-wide d blocks of O
-    static constexpr int SUMS = 2 * KT + 2 * VT;  // per thread: completed row-sum blocks
-    static constexpr int LDS = SUMS + 8 * NT;      // K[2], V^T[2], sums
-    static constexpr int K0 = 0, K1 = KT, V0 = 2 * KT, V1 = 2 * KT + VT;
+    static constexpr int GR = 2 * KT + 2 * VT;   // one key group's K[2], V^T[2]
+    static constexpr int SUMS = KG * GR;         // per thread: completed row-sum blocks
+    static constexpr int LDS = SUMS + 8 * NT;    // the groups' buffers, sums
+    static constexpr int K0 = 0, K1 = KT, V0 = 2 * KT, V1 = 2 * KT + VT;  // in a group's
     // epilogue: a wave's 32 rows of O (2D bytes each) or of 64 fp32 partial columns
     // (256 bytes), staged in LDS with 16 bytes of padding
     static constexpr int OSTR = (2 * D > 256 ? 2 * D : 256) + 16;
-    static_assert(NW * 32 * OSTR <= SUMS, "the epilogue's rows must fit the tile buffers");
+    static_assert(NQW * 32 * OSTR <= SUMS, "the epilogue's rows must fit the tile buffers");
     static_assert(KT % 1024 == 0, "K tiles must be whole DMA blocks");
+    // KG > 1: the state one wave of group g > 0 hands to group 0 (per lane: O^T
+    // registers, this half's two row sums, the reference), past the epilogue's rows
+    static constexpr int XSTR = 4 * (16 * DB + 4);   // bytes per lane
+    static constexpr int XOFF = (NQW * 32 * OSTR + 1023) / 1024 * 1024;
+    static_assert(KG == 1 || XOFF + (KG - 1) * NQW * 64 * XSTR <= SUMS,
+                  "the merge's states must fit the tile buffers");
 };
 
-template <typename T, int D, bool CAUSAL, bool SPLIT, bool DROP = false, bool MASK = false>
-__global__ __launch_bounds__(Tile16<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
+template <typename T, int D, bool CAUSAL, bool SPLIT, bool DROP = false, bool MASK = false,
+          int KG = 1>
+__global__ __launch_bounds__((Tile16<D, KG>::NT)) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
 {
-    using P = Tile16<D>;
+    static_assert(KG == 1 || (D == 64 && !SPLIT && !DROP && !MASK),
+                  "key groups serve the plain d = 64 forward");
+    using P = Tile16<D, KG>;
     using M = Mfma16<T>;
     using vec = typename M::vec;
     typedef T T4 __attribute__((ext_vector_type(4)));
@@ -105,10 +128,14 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
 
     const int tid = (int)threadIdx.x;
     const int wave = tid >> 6;
+    const int qw = KG == 1 ? wave : wave % P::NQW;  // query wave: rows 32 qw .. of the tile
+    const int grp = KG == 1 ? 0 : wave / P::NQW;    // key group: tiles grp, grp + KG, ...
+    const int gbase = grp * P::GR;  // the group's K / V^T buffers
+    const int gtid = tid - grp * P::GT;  // thread index within the group
     const int lane = tid & 63;
     const int ql = lane & 31;  // query column of this lane in the accumulators
     const int hh = lane >> 5;  // wave half
-    const int qw0 = q0 + wave * 32;
+    const int qw0 = q0 + qw * 32;
     const int my_q = qw0 + ql;
 
     // ---- key range: keys [kbeg, kbeg + Nks) of the head (all of them unless split);
@@ -136,21 +163,40 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
         const int last = min(qw0 + 31, Nq - 1) - kbeg;
         n_w = last < 0 ? 0 : min(nkt, last / P::BC + 1);
     }
+    // the key group's share: local tile i is tile grp + KG i; ni_g of the workgroup's
+    // tiles are staged by the group, this wave computes the first ni_w of them, and
+    // every wave runs ni steps (the most any group has), so all pass the same barriers
+    auto share = [&](int n) { return n > grp ? (n - grp + KG - 1) / KG : 0; };
+    const int ni = (nkt + KG - 1) / KG;
+    const int ni_g = share(nkt);
+    const int ni_w = share(n_w);
+    auto tile_of = [&](int i) { return grp + KG * i; };
 
     // ---- K staging by DMA: per-lane source offsets of this wave's blocks (fixed)
     int ksrc[P::KPW];
 #pragma unroll
     for (int i = 0; i < P::KPW; ++i)
-        ksrc[i] = dma_src<D>(wave + P::NW * i, lane, P::KSTR);
+        ksrc[i] = dma_src<D>(qw + P::NQW * i, lane, P::KSTR);
     auto stage_k = [&](int tile, int lds_off) {
-        stage_tile<D, P::KNB, P::KPW, P::NW>(Kh, tile, Nks, smem + lds_off, wave, ksrc);
+        stage_tile<D, P::KNB, P::KPW, P::NQW>(Kh, tile, Nks, smem + gbase + lds_off, qw, ksrc);
     };
-    // ---- V staging through registers: this thread's 4-key x 4-dim block.  Within a
-    // 32-lane half-wave the blocks cover 4 consecutive dim-quads x 8 key groups, which
-    // makes the transposed ds_write_b64 conflict-free.
-    const int v_dq = (tid & 3) + 4 * (tid >> 6);
-    const int v_kg = ((tid >> 2) & 3) + 4 * (((tid >> 4) & 1) + 2 * ((tid >> 5) & 1));
-    u32x2 vreg[4];
+    // ---- V staging through registers: this thread's 4-key x 4-dim blocks (VPT of
+    // them; block b covers dims 4 (v_dq + 4 NQW b) ..).  Within a 32-lane half-wave the
+    // blocks cover 4 consecutive dim-quads x 8 key groups, which makes the transposed
+    // ds_write_b64 conflict-free.
+    const int v_dq = (gtid & 3) + 4 * (gtid >> 6);
+    const int v_kg = ((gtid >> 2) & 3) + 4 * (((gtid >> 4) & 1) + 2 * ((gtid >> 5) & 1));
+    u32x2 vreg[P::VPT][4];
+    auto load_v = [&](int tile) {
+#pragma unroll
+        for (int b = 0; b < P::VPT; ++b)
+            load_v_block<D>(Vh, tile, Nks, v_kg, v_dq + 4 * P::NQW * b, vreg[b]);
+    };
+    auto store_vt = [&](int lds_off) {
+#pragma unroll
+        for (int b = 0; b < P::VPT; ++b)
+            store_vt_block<P::VTSTR>(smem + gbase + lds_off, v_kg, v_dq + 4 * P::NQW * b, vreg[b]);
+    };
 
     // ---- operand addresses inside a K / V^T tile: one base each, the rest immediates
     // K (A operand of S^T): lane reads K[32kb + ql][16c + 8hh .. +8] at
@@ -174,21 +220,21 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
         mwd[slot][1] = __builtin_amdgcn_raw_buffer_load_b32(mrs, mrow_off + 8 * t + 4, 0, 0);
     };
 
-    // ---- prologue: tiles 0 and 1 in flight, Q fragment into registers
-    if (MASK && 0 < n_w)
-        load_mask(0, 0);
-    if (MASK && 1 < n_w)
-        load_mask(1, 1);
-    if (0 < nkt) {
-        stage_k(0, P::K0);
-        load_v_block<D>(Vh, 0, Nks, v_kg, v_dq, vreg);
+    // ---- prologue: the group's tiles 0 and 1 in flight, Q fragment into registers
+    if (MASK && 0 < ni_w)
+        load_mask(tile_of(0), 0);
+    if (MASK && 1 < ni_w)
+        load_mask(tile_of(1), 1);
+    if (0 < ni_g) {
+        stage_k(tile_of(0), P::K0);
+        load_v(tile_of(0));
     }
-    if (1 < nkt)
-        stage_k(1, P::K1);
-    if (0 < nkt)
-        store_vt_block<P::VTSTR>(smem + P::V0, v_kg, v_dq, vreg);
-    if (1 < nkt)
-        load_v_block<D>(Vh, 1, Nks, v_kg, v_dq, vreg);  // written to LDS during step 0
+    if (1 < ni_g)
+        stage_k(tile_of(1), P::K1);
+    if (0 < ni_g)
+        store_vt(P::V0);
+    if (1 < ni_g)
+        load_v(tile_of(1));  // written to LDS during step 0
     // Q (B operand of S^T = K Q^T): lane supplies Q[my_q][16c + 8hh .. +8]
     vec qf[P::DC];
 #pragma unroll
@@ -340,7 +386,7 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
             // 16cc + 4hh + 0..3 (e < 4) and 16cc + 8 + 4hh + 0..3 (e >= 4) of the tile
             const DropParams dp{prm.drop_key0, prm.drop_key1, prm.drop_t, prm.drop_keep_scale};
             uint32_t words[8];  // group 2cc + g: keys kbase + 16cc + 8g + 0..3
-            drop_words_q8(dp, bh, my_q, kbeg + j * P::BC + 4 * hh, words);
+            drop_words_q8(dp, bh, my_q, kbeg + tile_of(j) * P::BC + 4 * hh, words);
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
@@ -366,60 +412,119 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
     __syncthreads();  // waits for this wave's DMA (vmcnt), publishes K_0, K_1 and V_0
     f32x16 sa[2], sb[2];
     float ma = 0.f, mb = 0.f;  // half-row maxima of the scores in sa / sb
-    if (0 < n_w) {
-        scores(P::K0, sa);
+    if (0 < ni_w) {
+        scores(gbase + P::K0, sa);
         if (MASK)
             apply_mask_words(sa, mwd[0][0], mwd[0][1], hh);
         ma = tile_max(sa);
     }
     __syncthreads();  // every wave has read K_0
-    if (2 < nkt)
-        stage_k(2, P::K0);
+    if (2 < ni_g)
+        stage_k(tile_of(2), P::K0);
 
-    // One pipelined step: the reference check for tile j (scores in s_cur, their
-    // half-row max in m_cur), then, as one branch-free block, the S MFMAs of tile j+1
-    // (K buffer kn, into s_nxt) and their max, together with the softmax and P.V
-    // MFMAs of tile j (V^T buffer vc); a wave's last tile is masked if it needs it
-    // and has no next tile.  Then V_{j+1} (in registers since the last step) is
-    // written to the other V^T buffer vn, the barrier publishes it together with
-    // K_{j+2} (DMA issued one step ago), and the next loads go out: V_{j+2} into
-    // registers, K_{j+3} into kn.
+    // One pipelined step of the group's local tile j (tile t = tile_of(j)): the
+    // reference check for tile t (scores in s_cur, their half-row max in m_cur), then,
+    // as one branch-free block, the S MFMAs of the group's next tile (K buffer kn, into
+    // s_nxt) and their max, together with the softmax and P.V MFMAs of tile t (V^T
+    // buffer vc); a wave's last tile is masked if it needs it and has no next tile.
+    // Then the next tile's V (in registers since the last step) is written to the
+    // other V^T buffer vn, the barrier publishes it together with the K of local tile
+    // j + 2 (DMA issued one step ago), and the next loads go out: V of local tile
+    // j + 2 into registers, K of local tile j + 3 into kn.
     auto step = [&](int j, f32x16* s_cur, f32x16* s_nxt, float& m_cur, float& m_nxt, int kn,
                     int vc, int vn, auto SL) {
-        constexpr int sl = decltype(SL)::value;  // mask-word slot of tile j + 1
-        if (j + 1 < n_w) {
+        constexpr int sl = decltype(SL)::value;  // mask-word slot of local tile j + 1
+        if (j + 1 < ni_w) {
             update_max(m_cur);
-            scores(kn, s_nxt);
+            scores(gbase + kn, s_nxt);
             vec pb[4];
             exp_sum_pack(j, s_cur, pb);
-            pv(pb, vc);
+            pv(pb, gbase + vc);
             if (MASK)
                 apply_mask_words(s_nxt, mwd[sl][0], mwd[sl][1], hh);
             m_nxt = tile_max(s_nxt);
-        } else if (j < n_w) {
-            if (needs_mask(j)) {
-                mask_tile(j, s_cur);
+        } else if (j < ni_w) {
+            if (needs_mask(tile_of(j))) {
+                mask_tile(tile_of(j), s_cur);
                 m_cur = tile_max(s_cur);
             }
             update_max(m_cur);
             vec pb[4];
             exp_sum_pack(j, s_cur, pb);
-            pv(pb, vc);
+            pv(pb, gbase + vc);
         }
-        if (j + 1 < nkt)
-            store_vt_block<P::VTSTR>(smem + vn, v_kg, v_dq, vreg);
+        if (j + 1 < ni_g)
+            store_vt(vn);
         __syncthreads();
-        if (MASK && j + 2 < n_w)
-            load_mask(j + 2, sl ^ 1);  // tile j + 2 has the parity of tile j
-        if (j + 2 < nkt)
-            load_v_block<D>(Vh, j + 2, Nks, v_kg, v_dq, vreg);
-        if (j + 3 < nkt)
-            stage_k(j + 3, kn);
+        if (MASK && j + 2 < ni_w)
+            load_mask(tile_of(j + 2), sl ^ 1);  // local tile j + 2 has the parity of j
+        if (j + 2 < ni_g)
+            load_v(tile_of(j + 2));
+        if (j + 3 < ni_g)
+            stage_k(tile_of(j + 3), kn);
     };
-    for (int j = 0; j < nkt; j += 2) {
+    for (int j = 0; j < ni; j += 2) {
         step(j, sa, sb, ma, mb, P::K1, P::V0, P::V1, std::integral_constant<int, 1>{});
-        if (j + 1 < nkt)
+        if (j + 1 < ni)
             step(j + 1, sb, sa, mb, ma, P::K0, P::V1, P::V0, std::integral_constant<int, 0>{});
+    }
+
+    // ---- key groups: the waves of groups 1 .. KG-1 hand their state to the group-0
+    // wave of the same rows, which folds them in with the (+) operator of the
+    // "Flash Attention" blog page on (m, d, o~): with M the largest reference,
+    // o~ = sum_g 2^(m_g - M) o~_g and the same factors on both row sums (a group that
+    // saw no key of the row has m_g = -inf and contributes nothing)
+    float lsum = done[0] + l, lrsum = done[1] + lr;
+    if (KG > 1) {
+        constexpr int XW = 64 * (16 * P::DB + 4);  // floats per wave
+        if (grp > 0) {
+            float* const x = reinterpret_cast<float*>(smem + P::XOFF) +
+                             ((grp - 1) * P::NQW + qw) * XW + lane * (16 * P::DB + 4);
+#pragma unroll
+            for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+                    *reinterpret_cast<f32x4*>(x + 16 * db + 4 * a) =
+                        f32x4{o[db][4 * a], o[db][4 * a + 1], o[db][4 * a + 2], o[db][4 * a + 3]};
+            *reinterpret_cast<f32x4*>(x + 16 * P::DB) = f32x4{lsum, lrsum, m2, 0.f};
+        }
+        __syncthreads();
+        if (grp > 0)
+            return;  // no barrier follows
+        const float* xg[KG - 1 > 0 ? KG - 1 : 1];
+        float mg[KG - 1 > 0 ? KG - 1 : 1];
+        float mx = m2;
+#pragma unroll
+        for (int g = 0; g < KG - 1; ++g) {
+            xg[g] = reinterpret_cast<const float*>(smem + P::XOFF) + (g * P::NQW + qw) * XW +
+                    lane * (16 * P::DB + 4);
+            mg[g] = xg[g][16 * P::DB + 2];
+            mx = fmaxf(mx, mg[g]);
+        }
+        // every row sees key 0 (tile 0 is group 0's), so m2 and mx are finite
+        const float f0 = exp2_fast(m2 - mx);
+#pragma unroll
+        for (int db = 0; db < P::DB; ++db)
+            o[db] *= f0;
+        lsum *= f0;
+        lrsum *= f0;
+#pragma unroll
+        for (int g = 0; g < KG - 1; ++g) {
+            const float f = mg[g] == neg_inf() ? 0.f : exp2_fast(mg[g] - mx);
+#pragma unroll
+            for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const f32x4 w = *reinterpret_cast<const f32x4*>(xg[g] + 16 * db + 4 * a);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        o[db][4 * a + e] = fmaf(f, w[e], o[db][4 * a + e]);
+                }
+            const f32x4 sums = *reinterpret_cast<const f32x4*>(xg[g] + 16 * P::DB);
+            lsum = fmaf(f, sums[0], lsum);
+            lrsum = fmaf(f, sums[1], lrsum);
+        }
+        m2 = mx;
     }
 
     if (!wave_active)
@@ -428,13 +533,12 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
     // ---- epilogue: O = O~ / l (rounded to T, nearest-even), L = ln2 * (m2 + log2 l);
     // split: O~ / l and L in fp32 into the partial buffers, and for a row that saw
     // no key of its range the identity of the merge, L = -inf with O = 0
-    const float lsum = done[0] + l, lrsum = done[1] + lr;
     const float lt = half_sum(lsum);
     const float lrt = half_sum(lrsum);
     // O goes through this wave's own LDS rows (the tile buffers are free after the
     // last barrier; the row sums lie past them), so that each store writes whole
     // rows rather than 8 or 16 bytes of 32 rows; fp32 partials 64 columns at a time
-    char* const ost = smem + wave * 32 * P::OSTR;
+    char* const ost = smem + qw * 32 * P::OSTR;
     if (SPLIT) {
         const float inv = lrt > 0.f ? 1.0f / lrt : 0.f;
         float* const phead = prm.o_part + ((size_t)split * prm.bh_count + bh) * Nq * D;

@@ -118,6 +118,16 @@ EXTRA = [
     (3, 8, 520, 520, 128, "f16", True, 1.0),
     (1, 12, 600, 600, 128, "bf16", True, 1.0),
     (2, 8, 700, 700, 64, "bf16", True, 1.0),
+    # d = 64 grids of at most 256 workgroups of 128 rows run with key groups (64-row
+    # workgroups, 4 groups of key tiles merged at the end): groups without a tile, a
+    # ragged last tile in a later group, causal Nq < Nk; larger grids take the 128-row
+    # kernel without groups
+    (1, 2, 70, 1, 64, "bf16", False, 1.0),
+    (1, 2, 200, 129, 64, "bf16", False, 1.0),
+    (1, 3, 64, 1000, 64, "f16", True, 1.0),
+    (2, 2, 130, 450, 64, "bf16", True, 3.0),
+    (4, 16, 600, 600, 64, "bf16", True, 1.0),
+    (4, 16, 520, 333, 64, "f16", False, 1.0),
 ]
 
 
