@@ -12,6 +12,7 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfa.so")
+DEBUG_LIB_PATH = os.path.join(PKG, "libfa_debug.so")  # the full-barrier check build
 
 FA_DTYPE_F32, FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH, FA_ERR_SCRATCH = 0, 1, 2, 3, 4
@@ -35,52 +36,58 @@ class FAError(RuntimeError):
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(
-                f"{LIB_PATH} is missing: build the HIP library first "
-                "(python -m flashattention_tiling_online_amd.build)")
-        L = ctypes.CDLL(LIB_PATH)
-        i64 = ctypes.c_int64
-        L.fa_fwd.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_void_p, i64, i64, i64, i64, i64,
-                                                      ctypes.c_int, ctypes.c_float, ctypes.c_int,
-                                                      ctypes.c_void_p]
-        L.fa_fwd.restype = ctypes.c_int
-        L.fa_status_str.argtypes = [ctypes.c_int]
-        L.fa_status_str.restype = ctypes.c_char_p
-        L.fa_tile_rows.argtypes = [ctypes.c_int, i64, ctypes.c_int]
-        L.fa_tile_rows.restype = ctypes.c_int
-        L.fa_fwd_split.argtypes = L.fa_fwd.argtypes[:-1] + [ctypes.c_int, ctypes.c_void_p, i64,
-                                                            ctypes.c_void_p]
-        L.fa_fwd_split.restype = ctypes.c_int
-        L.fa_fwd_masked.argtypes = [ctypes.c_void_p] * 4 + [i64, i64] + [ctypes.c_void_p] * 2 + [
-            i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
-        L.fa_fwd_masked.restype = ctypes.c_int
-        L.fa_fwd_split_static.argtypes = L.fa_fwd.argtypes[:-1] + [ctypes.c_int, ctypes.c_void_p]
-        L.fa_fwd_split_static.restype = ctypes.c_int
-        L.fa_fwd_split_workspace.argtypes = [i64, i64, i64, i64, ctypes.c_int]
-        L.fa_fwd_split_workspace.restype = i64
-        L.fa_merge.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, i64, i64, i64, i64,
-                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
-        L.fa_merge.restype = ctypes.c_int
-        L.fa_split_hint.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
-        L.fa_split_hint.restype = ctypes.c_int
-        L.fa_bwd.argtypes = [ctypes.c_void_p] * 9 + [i64, i64, i64, i64, i64, ctypes.c_int,
-                                                      ctypes.c_float, ctypes.c_int,
-                                                      ctypes.c_void_p, i64, ctypes.c_void_p]
-        L.fa_bwd.restype = ctypes.c_int
-        L.fa_bwd_masked.argtypes = [ctypes.c_void_p] * 4 + [i64, i64] + [ctypes.c_void_p] * 6 + [
-            i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p,
-            i64, ctypes.c_void_p]
-        L.fa_bwd_masked.restype = ctypes.c_int
-        L.fa_bwd_workspace.argtypes = [i64, i64, i64, i64]
-        L.fa_bwd_workspace.restype = i64
-        drop = [ctypes.c_float, ctypes.c_uint64]
-        L.fa_fwd_dropout.argtypes = L.fa_fwd.argtypes[:12] + drop + L.fa_fwd.argtypes[12:]
-        L.fa_fwd_dropout.restype = ctypes.c_int
-        L.fa_bwd_dropout.argtypes = L.fa_bwd.argtypes[:16] + drop + L.fa_bwd.argtypes[16:]
-        L.fa_bwd_dropout.restype = ctypes.c_int
-        _lib = L
+        _lib = load_library(LIB_PATH)
     return _lib
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Load a build of the library (libfa.so, or the check build libfa_debug.so) and
+    declare the argument and result types of every entry point."""
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build the HIP library first "
+            "(python -m flashattention_tiling_online_amd.build --all)")
+    L = ctypes.CDLL(path)
+    i64 = ctypes.c_int64
+    L.fa_fwd.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_void_p, i64, i64, i64, i64, i64,
+                                                  ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                                  ctypes.c_void_p]
+    L.fa_fwd.restype = ctypes.c_int
+    L.fa_status_str.argtypes = [ctypes.c_int]
+    L.fa_status_str.restype = ctypes.c_char_p
+    L.fa_tile_rows.argtypes = [ctypes.c_int, i64, ctypes.c_int]
+    L.fa_tile_rows.restype = ctypes.c_int
+    L.fa_fwd_split.argtypes = L.fa_fwd.argtypes[:-1] + [ctypes.c_int, ctypes.c_void_p, i64,
+                                                        ctypes.c_void_p]
+    L.fa_fwd_split.restype = ctypes.c_int
+    L.fa_fwd_masked.argtypes = [ctypes.c_void_p] * 4 + [i64, i64] + [ctypes.c_void_p] * 2 + [
+        i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    L.fa_fwd_masked.restype = ctypes.c_int
+    L.fa_fwd_split_static.argtypes = L.fa_fwd.argtypes[:-1] + [ctypes.c_int, ctypes.c_void_p]
+    L.fa_fwd_split_static.restype = ctypes.c_int
+    L.fa_fwd_split_workspace.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    L.fa_fwd_split_workspace.restype = i64
+    L.fa_merge.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, i64, i64, i64, i64,
+                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.fa_merge.restype = ctypes.c_int
+    L.fa_split_hint.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    L.fa_split_hint.restype = ctypes.c_int
+    L.fa_bwd.argtypes = [ctypes.c_void_p] * 9 + [i64, i64, i64, i64, i64, ctypes.c_int,
+                                                  ctypes.c_float, ctypes.c_int,
+                                                  ctypes.c_void_p, i64, ctypes.c_void_p]
+    L.fa_bwd.restype = ctypes.c_int
+    L.fa_bwd_masked.argtypes = [ctypes.c_void_p] * 4 + [i64, i64] + [ctypes.c_void_p] * 6 + [
+        i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p,
+        i64, ctypes.c_void_p]
+    L.fa_bwd_masked.restype = ctypes.c_int
+    L.fa_bwd_workspace.argtypes = [i64, i64, i64, i64]
+    L.fa_bwd_workspace.restype = i64
+    drop = [ctypes.c_float, ctypes.c_uint64]
+    L.fa_fwd_dropout.argtypes = L.fa_fwd.argtypes[:12] + drop + L.fa_fwd.argtypes[12:]
+    L.fa_fwd_dropout.restype = ctypes.c_int
+    L.fa_bwd_dropout.argtypes = L.fa_bwd.argtypes[:16] + drop + L.fa_bwd.argtypes[16:]
+    L.fa_bwd_dropout.restype = ctypes.c_int
+    return L
 
 
 def fa_status_str(status: int) -> str:

@@ -9,6 +9,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "fa_abi.hip")
 OUT = os.path.join(PKG, "libfa.so")
+# the check build: every workgroup barrier waits for all outstanding memory operations
+# first; tests compare its outputs with libfa.so's bit for bit
+DEBUG_OUT = os.path.join(PKG, "libfa_debug.so")
+DEBUG_FLAGS = ("-DFA_DEBUG_FULL_BARRIER",)
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -31,5 +35,16 @@ def build(out: str = OUT, extra=()) -> str:
     return out
 
 
+def build_all() -> None:
+    """Both libraries, compiled in parallel."""
+    import concurrent.futures as cf
+    with cf.ThreadPoolExecutor(2) as ex:
+        for f in [ex.submit(build), ex.submit(build, DEBUG_OUT, DEBUG_FLAGS)]:
+            f.result()
+
+
 if __name__ == "__main__":
-    print(build(*(sys.argv[1:2] or [])))
+    if sys.argv[1:2] == ["--all"]:
+        build_all()
+    else:
+        print(build(*(sys.argv[1:2] or [])))

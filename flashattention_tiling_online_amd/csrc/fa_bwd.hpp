@@ -248,9 +248,9 @@ void fa_bwd_dkv_kernel(const BwdParams<T> prm)
     if (i0 < nqt)
         load_tile(i0);
     for (int i = i0; i < nqt; ++i) {
-        __syncthreads();  // the previous tile is consumed (and K, V are staged)
+        wg_barrier();  // the previous tile is consumed (and K, V are staged)
         store_tile(i);
-        __syncthreads();
+        wg_barrier();
         if (i + 1 < nqt)
             load_tile(i + 1);  // in flight while this tile is computed
         const int qw = i * P::TILE + 32 * qh;  // first query of this wave's half
@@ -319,7 +319,7 @@ void fa_bwd_dkv_kernel(const BwdParams<T> prm)
     }
 
     // the second query half hands its partial sums to the first through LDS
-    __syncthreads();
+    wg_barrier();
     float* xch = reinterpret_cast<float*>(smem);
     if (qh == 1) {
 #pragma unroll
@@ -330,7 +330,7 @@ void fa_bwd_dkv_kernel(const BwdParams<T> prm)
                 xch[(((kblk * 2 + 1) * P::DB + db) * 16 + r) * 64 + lane] = dvt[db][r];
             }
     }
-    __syncthreads();
+    wg_barrier();
     if (qh == 0) {
 #pragma unroll
         for (int db = 0; db < P::DB; ++db)
@@ -340,7 +340,7 @@ void fa_bwd_dkv_kernel(const BwdParams<T> prm)
                 dvt[db][r] += xch[(((kblk * 2 + 1) * P::DB + db) * 16 + r) * 64 + lane];
             }
     }
-    __syncthreads();  // the exchange is read: its space takes the rows of dK and dV
+    wg_barrier();  // the exchange is read: its space takes the rows of dK and dV
     if (qh == 1)
         return;
     // epilogue: accumulator register r of block db holds d = 32db + 8(r/4) + 4hh + r%4.
@@ -499,11 +499,11 @@ void fa_bwd_dq_kernel(const BwdParams<T> prm)
     const int tbase = ql * P::TSTR + hh * 16;
 
     for (int j = 0; j < nkt; ++j) {
-        __syncthreads();  // the previous tile is consumed
+        wg_barrier();  // the previous tile is consumed
         store_row_block<P::RSTR>(smem + P::KR, s_kg, s_dq, kreg);
         store_vt_block<P::TSTR>(smem + P::KT, s_kg, s_dq, kreg);
         __builtin_amdgcn_s_waitcnt(0x0070);  // this wave's DMA blocks of V_j have landed
-        __syncthreads();
+        wg_barrier();
         const int vr = (j & 1) ? P::VR1 : P::VR;
         if (j + 1 < nkt) {  // in flight while this tile is computed
             load_v_block<D>(Kh, j + 1, Nk, s_kg, s_dq, kreg);
@@ -577,7 +577,7 @@ void fa_bwd_dq_kernel(const BwdParams<T> prm)
 
     // dQ rows through this wave's LDS rows, 64 columns at a time (the K and V tiles
     // are consumed after the barrier), so that each store writes 128 bytes of 8 rows
-    __syncthreads();
+    wg_barrier();
     char* const ost = smem + wave * 32 * P::OSTR;
     T* const dqh = prm.dq + (size_t)bh * Nq * D;
 #pragma unroll

@@ -24,6 +24,25 @@ constexpr float kLn2 = 0.693147180559945309417f;
 // key tiles per block of the forward kernels' row sums (a power of two)
 constexpr int kSumBlock = 64;
 
+// Check build (FA_DEBUG_FULL_BARRIER defined): every workgroup barrier of the kernels
+// first waits for all of the wave's outstanding memory operations (global loads, DMA
+// into LDS, LDS reads and writes).  Its outputs must equal the optimised build's bit
+// for bit, which holds only if no kernel reads a buffer before the operation that
+// fills it has completed, whatever the latencies.
+#ifdef FA_DEBUG_FULL_BARRIER
+constexpr bool kFullBarrier = true;
+#else
+constexpr bool kFullBarrier = false;
+#endif
+
+// The kernels' workgroup barrier (a full wait first in the check build).
+__device__ __forceinline__ void wg_barrier()
+{
+    if (kFullBarrier)
+        __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt and lgkmcnt all zero
+    __syncthreads();
+}
+
 // Number of XCDs (accelerator complex dies) on gfx950.  Consecutive workgroup ids
 // are dispatched round-robin over them, and each has its own L2.
 constexpr int kXcds = 8;

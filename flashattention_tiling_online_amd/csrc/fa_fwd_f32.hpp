@@ -103,7 +103,7 @@ void fa_fwd_f32_kernel(const FwdParams<float> prm)
 
     for (int j = 0; j < nkt; ++j) {
         const int key0 = j * P::BC;
-        __syncthreads();  // previous tile fully consumed
+        wg_barrier();  // previous tile fully consumed
 #pragma unroll
         for (int i = 0; i < P::CH; ++i) {
             const int f = i * P::NT + tid;
@@ -120,7 +120,7 @@ void fa_fwd_f32_kernel(const FwdParams<float> prm)
                 Ks[key * P::KS + 4 * d4 + e] = kv[e];
             *reinterpret_cast<f32x4*>(Vs + key * P::VS + 4 * d4) = vv;
         }
-        __syncthreads();
+        wg_barrier();
 
         if (!wave_active || (CAUSAL && key0 > qw_last))
             continue;

@@ -409,7 +409,7 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
             }
     };
 
-    __syncthreads();  // waits for this wave's DMA (vmcnt), publishes K_0, K_1 and V_0
+    wg_barrier();  // waits for this wave's DMA (vmcnt), publishes K_0, K_1 and V_0
     f32x16 sa[2], sb[2];
     float ma = 0.f, mb = 0.f;  // half-row maxima of the scores in sa / sb
     if (0 < ni_w) {
@@ -418,7 +418,7 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
             apply_mask_words(sa, mwd[0][0], mwd[0][1], hh);
         ma = tile_max(sa);
     }
-    __syncthreads();  // every wave has read K_0
+    wg_barrier();  // every wave has read K_0
     if (2 < ni_g)
         stage_k(tile_of(2), P::K0);
 
@@ -455,7 +455,7 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
         }
         if (j + 1 < ni_g)
             store_vt(vn);
-        __syncthreads();
+        wg_barrier();
         if (MASK && j + 2 < ni_w)
             load_mask(tile_of(j + 2), sl ^ 1);  // local tile j + 2 has the parity of j
         if (j + 2 < ni_g)
@@ -488,7 +488,7 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
                         f32x4{o[db][4 * a], o[db][4 * a + 1], o[db][4 * a + 2], o[db][4 * a + 3]};
             *reinterpret_cast<f32x4*>(x + 16 * P::DB) = f32x4{lsum, lrsum, m2, 0.f};
         }
-        __syncthreads();
+        wg_barrier();
         if (grp > 0)
             return;  // no barrier follows
         const float* xg[KG - 1 > 0 ? KG - 1 : 1];

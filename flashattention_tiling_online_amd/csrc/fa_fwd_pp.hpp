@@ -407,7 +407,7 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     // complete, then the workgroup barrier
     auto barrier = [&](bool loads) {
         __asm__ volatile("" ::: "memory");
-        if (loads)
+        if (loads || kFullBarrier)
             __builtin_amdgcn_s_waitcnt(kWaitAll);
         else
             __builtin_amdgcn_s_waitcnt(kWaitLds);
