@@ -12,11 +12,10 @@
 // SIMD.  Waves 0-3 form group 0, waves 4-7 group 1, and the two groups run in
 // opposite phases separated by workgroup barriers:
 //   * an MFMA phase of tile j, at raised wave priority: S_{j+1} = K_{j+1} Q^T (16
-//     MFMAs) and O~ += V_j^T P_j^T (16 MFMAs), operands read from LDS, then this
-//     group's half of V^T_{j+1} written to LDS from registers;
+//     MFMAs) and O~ += V_j^T P_j^T (16 MFMAs), operands read from LDS;
 //   * a softmax phase of tile u: mask, running max, P_u = 2^(S_u c - m) rounded to
-//     T, the two row sums, plus this group's share of the staging: V_{u+2} into
-//     registers (its half of the dims) and its DMA blocks of K_{u+2}.
+//     T, the two row sums, plus the wave's share of the staging: its DMA blocks of
+//     K_{u+2} and of V_{u+1}.
 // While one wave of a SIMD issues its 32 MFMAs back to back, the other wave's
 // softmax instructions take the issue slots the matrix core leaves free, instead of
 // both waves contending for the same slots in the same phase:
@@ -26,16 +25,22 @@
 // blocks (wave w: rows 32 (2 (w % 4) + w / 4) of the tile), which keeps their
 // causal tile counts within one of each other.
 //
-// Staging (K by DMA into rows padded by 16 B, V transposed through registers into
-// V^T rows, exactly as fa_fwd_mfma16.hpp lays them out): three K buffers, two V^T
-// buffers and two V register slots.  K_t and V_t are issued in the softmax phase of
-// tile t-2 (group 0: phase 2t-5, group 1: phase 2t-4), and a group waits for its
-// loads at the end of its following MFMA phase (phases 2t-4 and 2t-3).  V^T_t is
-// written at the end of the MFMA phases of tile t-1 (group 0 dims 0-63 in phase
-// 2t-2, group 1 dims 64-127 in phase 2t-1).  The first reader of K_t (group 0,
-// phase 2t-2) and of V^T_t (group 0, phase 2t) comes after both groups' waits and
-// writes, and no buffer or register slot is rewritten before its last reader's
-// phase has ended.
+// Staging, K and V both by DMA (buffer_load ... lds), three buffers each.  K rows
+// are padded to 272 bytes (as in fa_fwd_mfma16.hpp): the 16 rows of one
+// ds_read_b128 pass fall in distinct banks.  V stays row-major, rows padded to 320
+// bytes, and the A operand of O^T = V^T P^T (32 dims x 16 keys, a lane holding 8
+// keys of one dim) comes from two ds_read_b64_tr_b16, gfx950's transposing LDS
+// read: each group of 16 lanes reads 4 rows x 16 dims and receives them transposed,
+// lane j dim j with the 4 rows in order; with 320-byte rows the 4 rows of a
+// half-wave's read sit 16 banks apart.  The keys land in the k-slots that the
+// rounded P occupies (slot 8h + 4r + e of chunk cc holds key 16cc + 8r + 4h + e, as
+// the 32x32 accumulator layout gives it).  K_t is issued in the softmax phase of
+// tile t-2 (group 0: phase 2t-5, group 1: phase 2t-4) and V_t in that of tile t-1
+// (phases 2t-3 and 2t-2); a group waits for its loads at the end of its following
+// MFMA phase.  The first reader of K_t (group 0, phase 2t-2) and of V_t (group 0,
+// phase 2t) comes after both groups' waits, and no buffer is rewritten before its
+// last reader's phase has ended (V_t goes where V_{t-3} was, last read in phase
+// 2t-5).
 //
 // Q and O move as whole rows: the prologue stages the workgroup's 256 Q rows by DMA
 // into buffers not yet in use and each wave reads its fragments from there; the
@@ -64,21 +69,23 @@ struct TilePP {
     static constexpr int BC = 64;             // keys per K/V tile
     static constexpr int NT = 512;            // threads per workgroup
     static constexpr int KSTR = 2 * D + 16;   // K row stride in LDS
-    static constexpr int VTSTR = 2 * BC + 16; // V^T row stride in LDS
+    static constexpr int VSTR = 2 * D + 64;   // V row stride in LDS
     static constexpr int KT = BC * KSTR;      // bytes of one K tile in LDS
-    static constexpr int VT = D * VTSTR;      // bytes of one V^T tile in LDS
+    static constexpr int VT = BC * VSTR;      // bytes of one V tile in LDS
     static constexpr int KNB = KT / 1024;     // 1-KB DMA blocks per K tile
     static constexpr int KPW = (KNB + NW - 1) / NW;
+    static constexpr int VNB = VT / 1024;     // 1-KB DMA blocks per V tile
+    static constexpr int VPW = (VNB + NW - 1) / NW;
     static constexpr int DC = D / 16;
     static constexpr int DB = D / 32;
     static constexpr int NKB = 3;             // K buffers
-    static constexpr int VOFF = NKB * KT;     // first V^T buffer
-    static constexpr int LDS = NKB * KT + 2 * VT;
+    static constexpr int NVB = 3;             // V buffers
+    static constexpr int VOFF = NKB * KT;     // first V buffer
+    static constexpr int LDS = NKB * KT + NVB * VT;
     static constexpr int OSTR = 2 * D + 16;   // bytes per row of a wave's O in LDS (epilogue)
     static_assert(NW * 32 * OSTR <= LDS, "the epilogue's O rows must fit the K and V^T buffers");
     static_assert(KT + BR * KSTR <= LDS, "the prologue's Q rows must fit past K buffer 0");
-    static_assert(KT % 1024 == 0, "K tiles must be whole DMA blocks");
-    static_assert(NT == 4 * D, "V staging: one 4-key x 4-dim block per thread");
+    static_assert(KT % 1024 == 0 && VT % 1024 == 0, "tiles must be whole DMA blocks");
 };
 
 // s_waitcnt immediates (gfx9 encoding): LDS only, and all memory
@@ -94,6 +101,9 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     using vec = typename M::vec;
     constexpr int D = P::D;
     typedef T T4 __attribute__((ext_vector_type(4)));
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     __shared__ __attribute__((aligned(1024))) char smem[P::LDS];
     const char* const sm = smem;
     const int Nq = prm.Nq, Nk = prm.Nk, n_qtiles = prm.n_qtiles;
@@ -140,21 +150,19 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
         n_w = last < 0 ? 0 : min(nkt, last / P::BC + 1);
     }
 
-    // ---- staging: K blocks of this wave (DMA), V block of this thread (registers;
-    // group 0 threads cover dims 0-63, group 1 threads dims 64-127)
-    int ksrc[P::KPW];
+    // ---- staging: this wave's DMA blocks of K and V tiles
+    int ksrc[P::KPW], vsrc[P::VPW];
 #pragma unroll
     for (int i = 0; i < P::KPW; ++i)
         ksrc[i] = dma_src<D>(wave + P::NW * i, lane, P::KSTR);
+#pragma unroll
+    for (int i = 0; i < P::VPW; ++i)
+        vsrc[i] = dma_src<D>(wave + P::NW * i, lane, P::VSTR);
     auto stage_k = [&](int t, int lds_off) {
         stage_tile<D, P::KNB, P::KPW, P::NW>(Kh, t, Nks, smem + lds_off, wave, ksrc);
     };
-    const int v_dq = (tid & 3) + 4 * (tid >> 6);
-    const int v_kg = ((tid >> 2) & 3) + 4 * (((tid >> 4) & 1) + 2 * ((tid >> 5) & 1));
-    u32x2 vreg[2][4];  // V_t in vreg[t % 2] from its load to its V^T write
-    auto load_v = [&](int t, int slot) { load_v_block<D>(Vh, t, Nks, v_kg, v_dq, vreg[slot]); };
-    auto write_vt = [&](int lds_off, int slot) {
-        store_vt_block<P::VTSTR>(smem + lds_off, v_kg, v_dq, vreg[slot]);
+    auto stage_v = [&](int t, int lds_off) {
+        stage_tile<D, P::VNB, P::VPW, P::NW>(Vh, t, Nks, smem + lds_off, wave, vsrc);
     };
 
     // ---- caller mask: this lane's row of the head's mask slice, the words of one tile
@@ -172,7 +180,9 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     };
 
     const int kbase = ql * P::KSTR + hh * 16;
-    const int vbase = ql * P::VTSTR + hh * 16;
+    // transposing V reads: lane (h = lane / 32, g = (lane / 16) % 2, j = lane % 16)
+    // addresses row 4h + j / 4 (plus 8r + 16cc) at dims 16g + 4 (j % 4) .. +3 (plus 32db)
+    const int vbase = (4 * hh + ((lane >> 2) & 3)) * P::VSTR + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
     // ---- Q fragment (B operand of S^T = K Q^T): lane supplies Q[my_q][16c + 8hh .. +8],
     // read in the prologue from the workgroup's Q rows staged in LDS (rows past Nq are 0)
@@ -223,16 +233,25 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
             const vec a = *reinterpret_cast<const vec*>(sm + kb_off + kbase + 32 * c + kb * 32 * P::KSTR);
             s[kb] = M::mma(a, qf[c], s[kb]);
             const int cc = i >> 2, db = i & 3;
-            const vec b = *reinterpret_cast<const vec*>(sm + vb_off + vbase + 32 * db * P::VTSTR + 32 * cc);
-            o[db] = M::mma(b, pb[cc], o[db]);
+            const char* const vp = sm + vb_off + vbase + 16 * cc * P::VSTR + 64 * db;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * P::VSTR));
+            const s16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            o[db] = M::mma(__builtin_bit_cast(vec, w), pb[cc], o[db]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        // the reads of the first two MFMA pairs (3 each: one K, two V), then per MFMA
+        // pair the reads of the pair two ahead, so that the operands stay four MFMAs
+        // ahead (one, three or four pairs ahead time the same)
+        constexpr int ahead = 2;
+        __builtin_amdgcn_sched_group_barrier(0x100, 3 * ahead, 0);
 #pragma unroll
-        for (int i = 0; i < 28; ++i) {
+        for (int i = 0; i < 16 - ahead; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * ahead, 0);
     };
 
     // Mask of tile j (keys past the end, or after the query): only a wave's last
@@ -370,10 +389,7 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
         }
     };
     // MFMA phase of tile j (j = R mod 6): S^T of tile j+1 and P.V of tile j (K buffer
-    // of tile j+1, V^T buffer of tile j), then this group's half of V^T_{j+1} written
-    // from registers.  The write goes last: its transposing VALU work runs under the
-    // last MFMAs and its LDS stores queue behind the operand reads (placed first, or
-    // among the MFMAs, it delays the first operand reads).  On a wave's last tile the
+    // of tile j+1, V buffer of tile j).  On a wave's last tile the
     // S^T MFMAs read a K buffer that holds no tile of this wave (stale but allocated
     // LDS) and their result is never used: one code path keeps O~ in the same
     // registers throughout the loop.  The phase runs at raised wave priority, so the
@@ -388,21 +404,19 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
             rescale = false;
         }
         if (j < n_w)
-            scores_pv(((r + 1) % P::NKB) * P::KT, P::VOFF + (r & 1) * P::VT);
-        if (j + 1 < nkt)
-            write_vt(P::VOFF + ((r + 1) & 1) * P::VT, (r + 1) & 1);
+            scores_pv(((r + 1) % P::NKB) * P::KT, P::VOFF + (r % P::NVB) * P::VT);
     };
-    // staging in the softmax phase of tile u (u = R mod 6): V_{u+2} into registers and
-    // this wave's DMA blocks of K_{u+2}; the phase runs at normal priority
+    // staging in the softmax phase of tile u (u = R mod 6): this wave's DMA blocks of
+    // K_{u+2} and V_{u+1}; the phase runs at normal priority
     auto stage = [&](int u, auto R) {
         constexpr int r = decltype(R)::value;
         __builtin_amdgcn_s_setprio(0);
         if (MASK && u + 1 < n_w)
             load_mask(u + 1, (r + 1) & 1);
-        if (u + 2 < nkt) {
-            load_v(u + 2, r & 1);
+        if (u + 2 < nkt)
             stage_k(u + 2, ((r + 2) % P::NKB) * P::KT);
-        }
+        if (u + 1 < nkt)
+            stage_v(u + 1, P::VOFF + ((r + 1) % P::NVB) * P::VT);
     };    // end of a phase: this wave's LDS traffic (and, after an MFMA phase, its loads)
     // complete, then the workgroup barrier
     auto barrier = [&](bool loads) {
@@ -415,20 +429,15 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
         __asm__ volatile("" ::: "memory");
     };
 
-    // ---- prologue: K_0 and the workgroup's 256 Q rows by DMA (Q into K buffers 1-2
-    // and the V^T buffers, free until K_1 and V^T_0 arrive; whole rows per DMA block,
-    // where loading the fragments straight from memory would touch 32 rows per
-    // load); V_0 and V_1 into registers, this group's dims.  Then every wave reads
-    // its Q fragments, and a barrier frees the staging area for K_1.
+    // ---- prologue: K_0 and the workgroup's 256 Q rows by DMA (Q into the buffers past
+    // K buffer 0, free until K_1 and V_0 arrive; whole rows per DMA block, where
+    // loading the fragments straight from memory would touch 32 rows per load).  Then
+    // every wave reads its Q fragments, and a barrier frees the area for K_1 and V_0.
     if (0 < nkt)
         stage_k(0, 0);
 #pragma unroll
     for (int t = 0; t < P::BR / P::BC; ++t)
         stage_tile<D, P::KNB, P::KPW, P::NW>(Qh, q0 / P::BC + t, Nq, smem + P::KT * (1 + t), wave, ksrc);
-    if (0 < nkt)
-        load_v(0, 0);
-    if (1 < nkt)
-        load_v(1, 1);
     if (MASK && 0 < n_w)
         load_mask(0, 0);
     barrier(true);
@@ -439,6 +448,8 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
             qf[c] = *reinterpret_cast<const vec*>(qrow + 32 * c);
     }
     barrier(false);
+    if (0 < nkt)
+        stage_v(0, P::VOFF);
     if (1 < nkt && grp == 0)
         stage_k(1, P::KT);
 
@@ -447,13 +458,12 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     // the same code, one MFMA and one softmax phase per iteration; group 1 enters
     // one phase later (it issues its K_1 blocks in phase -2, while group 0 computes
     // S_0) and group 0 closes with one barrier more, so both pass the same barriers.
-    // The MFMA phase of tile j writes V^T_{j+1}, the one before tile 0 writes V^T_0.
+    // V_0 lands before the first barrier that waits for loads in each group.
     if (grp == 1) {
         if (1 < nkt)
             stage_k(1, P::KT);
         barrier(false);
     }
-    write_vt(P::VOFF, 0);
     if (0 < n_w)
         scores_only(0);
     barrier(true);
