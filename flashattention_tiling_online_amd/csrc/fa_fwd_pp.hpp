@@ -34,13 +34,15 @@
 // lane j dim j with the 4 rows in order; with 320-byte rows the 4 rows of a
 // half-wave's read sit 16 banks apart.  The keys land in the k-slots that the
 // rounded P occupies (slot 8h + 4r + e of chunk cc holds key 16cc + 8r + 4h + e, as
-// the 32x32 accumulator layout gives it).  K_t is issued in the softmax phase of
-// tile t-2 (group 0: phase 2t-5, group 1: phase 2t-4) and V_t in that of tile t-1
-// (phases 2t-3 and 2t-2); a group waits for its loads at the end of its following
-// MFMA phase.  The first reader of K_t (group 0, phase 2t-2) and of V_t (group 0,
-// phase 2t) comes after both groups' waits, and no buffer is rewritten before its
-// last reader's phase has ended (V_t goes where V_{t-3} was, last read in phase
-// 2t-5).
+// the 32x32 accumulator layout gives it).  Group 0 issues its blocks of K_t in the
+// softmax phase of tile t-2 (phase 2t-5) and of V_t in that of tile t-1 (phase
+// 2t-3); group 1 one tile earlier, K_t in phase 2t-6 and V_t in phase 2t-4.  A group
+// waits for its loads at the end of its following MFMA phase, so all of K_t has
+// landed by the end of phase 2t-4 and all of V_t by the end of phase 2t-2.  Each wave
+// reads the operands of the first MFMA pairs of its MFMA phase at the start of the
+// softmax phase before it (group 0 reads K_t first in phase 2t-3, V_t in phase
+// 2t-1), and no buffer is rewritten before its last reader's phase has ended (K_t
+// and V_t go where K_{t-3} and V_{t-3} were, last read in phases 2t-7 and 2t-5).
 //
 // Q and O move as whole rows: the prologue stages the workgroup's 256 Q rows by DMA
 // into buffers not yet in use and each wave reads its fragments from there; the
@@ -220,6 +222,25 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
                 s[kb] = M::mma(a, qf[c], s[kb]);
             }
     };
+    // The operands of the first NPRE MFMA pairs (pair i: S^T MFMA i, P.V MFMA i) of an
+    // MFMA phase, read at the start of the softmax phase before it, so that the MFMA
+    // phase starts on operands already in registers (their tiles have landed by then:
+    // see the staging schedule above).
+    constexpr int NPRE = 2;
+    vec pre_k[NPRE];
+    s16x4 pre_v[NPRE][2];
+    auto v_read = [&](const char* vp, s16x4* out) {
+        out[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
+        out[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * P::VSTR));
+    };
+    auto pre_read = [&](int kb_off, int vb_off) {
+#pragma unroll
+        for (int i = 0; i < NPRE; ++i) {
+            const int c = i >> 1, kb = i & 1, cc = i >> 2, db = i & 3;
+            pre_k[i] = *reinterpret_cast<const vec*>(sm + kb_off + kbase + 32 * c + kb * 32 * P::KSTR);
+            v_read(sm + vb_off + vbase + 16 * cc * P::VSTR + 64 * db, pre_v[i]);
+        }
+    };
     // both, interleaved: S^T of tile j+1 and P.V of tile j; the operand reads run
     // four MFMAs ahead (a fixed DS-read / MFMA order keeps the operands in flight,
     // and their registers, bounded)
@@ -230,28 +251,36 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int c = i >> 1, kb = i & 1;
-            const vec a = *reinterpret_cast<const vec*>(sm + kb_off + kbase + 32 * c + kb * 32 * P::KSTR);
+            const vec a = i < NPRE ? pre_k[i]
+                                   : *reinterpret_cast<const vec*>(sm + kb_off + kbase + 32 * c + kb * 32 * P::KSTR);
             s[kb] = M::mma(a, qf[c], s[kb]);
             const int cc = i >> 2, db = i & 3;
-            const char* const vp = sm + vb_off + vbase + 16 * cc * P::VSTR + 64 * db;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * P::VSTR));
-            const s16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            s16x4 vv[2];
+            if (i < NPRE) {
+                vv[0] = pre_v[i][0];
+                vv[1] = pre_v[i][1];
+            } else {
+                v_read(sm + vb_off + vbase + 16 * cc * P::VSTR + 64 * db, vv);
+            }
+            const s16x8 w = {vv[0][0], vv[0][1], vv[0][2], vv[0][3], vv[1][0], vv[1][1], vv[1][2], vv[1][3]};
             o[db] = M::mma(__builtin_bit_cast(vec, w), pb[cc], o[db]);
         }
-        // the reads of the first two MFMA pairs (3 each: one K, two V), then per MFMA
-        // pair the reads of the pair two ahead, so that the operands stay four MFMAs
-        // ahead (one, three or four pairs ahead time the same)
-        constexpr int ahead = 2;
-        __builtin_amdgcn_sched_group_barrier(0x100, 3 * ahead, 0);
+        // the preloaded pairs first, each followed by the reads of the pair NPRE ahead
+        // (3 each: one K, two V), then per MFMA pair the reads of the pair NPRE ahead,
+        // so that the operands stay 2 NPRE MFMAs ahead
 #pragma unroll
-        for (int i = 0; i < 16 - ahead; ++i) {
+        for (int i = 0; i < NPRE; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 16 - 2 * NPRE; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * ahead, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NPRE, 0);
     };
 
     // Mask of tile j (keys past the end, or after the query): only a wave's last
@@ -406,17 +435,29 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
         if (j < n_w)
             scores_pv(((r + 1) % P::NKB) * P::KT, P::VOFF + (r % P::NVB) * P::VT);
     };
-    // staging in the softmax phase of tile u (u = R mod 6): this wave's DMA blocks of
-    // K_{u+2} and V_{u+1}; the phase runs at normal priority
+    // staging in the softmax phase of tile u (u = R mod 6): the operands of the first
+    // MFMA pairs of MFMA(u) (ahead of the DMA: the compiler makes every transposing
+    // LDS read wait for all of the wave's DMA in flight), then this wave's DMA blocks
+    // of K_{u+2} and V_{u+1} (group 0) or K_{u+3} and V_{u+2} (group 1); the phase runs
+    // at normal priority
     auto stage = [&](int u, auto R) {
         constexpr int r = decltype(R)::value;
         __builtin_amdgcn_s_setprio(0);
+        if (u < n_w)
+            pre_read(((r + 1) % P::NKB) * P::KT, P::VOFF + (r % P::NVB) * P::VT);
         if (MASK && u + 1 < n_w)
             load_mask(u + 1, (r + 1) & 1);
-        if (u + 2 < nkt)
-            stage_k(u + 2, ((r + 2) % P::NKB) * P::KT);
-        if (u + 1 < nkt)
-            stage_v(u + 1, P::VOFF + ((r + 1) % P::NVB) * P::VT);
+        if (grp == 0) {
+            if (u + 2 < nkt)
+                stage_k(u + 2, ((r + 2) % P::NKB) * P::KT);
+            if (u + 1 < nkt)
+                stage_v(u + 1, P::VOFF + ((r + 1) % P::NVB) * P::VT);
+        } else {
+            if (u + 3 < nkt)
+                stage_k(u + 3, (r % P::NKB) * P::KT);
+            if (u + 2 < nkt)
+                stage_v(u + 2, P::VOFF + ((r + 2) % P::NVB) * P::VT);
+        }
     };    // end of a phase: this wave's LDS traffic (and, after an MFMA phase, its loads)
     // complete, then the workgroup barrier
     auto barrier = [&](bool loads) {
@@ -456,13 +497,17 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     // ---- phases: group 0 runs MFMA(j) in phase 2j and softmax(u) in phase 2u - 1,
     // group 1 softmax(u) in phase 2u and MFMA(j) in phase 2j + 1.  Both groups run
     // the same code, one MFMA and one softmax phase per iteration; group 1 enters
-    // one phase later (it issues its K_1 blocks in phase -2, while group 0 computes
-    // S_0) and group 0 closes with one barrier more, so both pass the same barriers.
-    // V_0 lands before the first barrier that waits for loads in each group.
+    // one phase later (it issues its K_1, K_2 and V_1 blocks in phase -2, while group
+    // 0 computes S_0) and group 0 closes with one barrier more, so both pass the same
+    // barriers.  V_0 and K_1 land before the first barrier that waits for loads.
     if (grp == 1) {
         if (1 < nkt)
             stage_k(1, P::KT);
-        barrier(false);
+        if (2 < nkt)
+            stage_k(2, 2 * P::KT);
+        if (1 < nkt)
+            stage_v(1, P::VOFF + P::VT);
+        barrier(true);
     }
     if (0 < n_w)
         scores_only(0);
@@ -470,8 +515,8 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     stage(0, std::integral_constant<int, 0>{});
     softmax(0, std::false_type{}, std::integral_constant<int, 0>{});
     barrier(false);
-    // unrolled by 6 = lcm(3 K buffers, 2 V^T buffers), so that every buffer offset
-    // and register slot is a constant of the code
+    // unrolled by 6 = lcm(3 buffers, the tile parity of the mask words and of the
+    // threshold update), so that every buffer offset and register slot is a constant
     auto iter = [&](int j, auto R) {  // j = R (mod 6)
         constexpr int r = decltype(R)::value;
         mfma(j, R);
