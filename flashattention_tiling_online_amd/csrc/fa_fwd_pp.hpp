@@ -226,7 +226,7 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     // MFMA phase, read at the start of the softmax phase before it, so that the MFMA
     // phase starts on operands already in registers (their tiles have landed by then:
     // see the staging schedule above).
-    constexpr int NPRE = 2;
+    constexpr int NPRE = 2;  // one, three or four pairs time 0.5-1 % slower
     vec pre_k[NPRE];
     s16x4 pre_v[NPRE][2];
     auto v_read = [&](const char* vp, s16x4* out) {
