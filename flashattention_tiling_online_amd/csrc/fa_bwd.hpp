@@ -95,47 +95,34 @@ struct DkvTile {
     static constexpr int NT = 64 * NW;
     static constexpr int KEYS = 128;             // keys per workgroup
     static constexpr int TILE = 64;              // queries per step
-    static constexpr int RSTR = 2 * D + 16;
-    static constexpr int TSTR = 2 * TILE + 16;
+    static constexpr int RSTR = 2 * D + 16;      // K and V rows (resident)
+    // Q and dO rows: with 2D + 48 bytes the 16 rows of a ds_read_b128 pass fall in
+    // distinct banks and the 4 rows of a half-wave's transposing read meet at most
+    // 2-way (no stride makes both conflict-free)
+    static constexpr int QSTR = 2 * D + 48;
     static constexpr int DC = D / 16;
     static constexpr int DB = D / 32;
-    // LDS: K and V of the workgroup's keys (resident), then per step Q and dO as
-    // row tiles and as transposed tiles, and the 64 queries' L2 and D
+    // LDS: K and V of the workgroup's keys (resident), then two staging buffers, each
+    // the Q and dO rows of one 64-query tile, the 64 queries' L2 and D and the
+    // caller-mask words [4 key words][64 queries]
     static constexpr int KS = 0;
     static constexpr int VS = KEYS * RSTR;
-    static constexpr int QR = 2 * KEYS * RSTR;
-    static constexpr int DOR = QR + TILE * RSTR;
-    static constexpr int QT = DOR + TILE * RSTR;
-    static constexpr int DOT = QT + D * TSTR;
-    static constexpr int LS = DOT + D * TSTR;
-    static constexpr int DS = LS + TILE * 4;
-    static constexpr int MS = DS + TILE * 4;     // caller-mask words: [4 key words][64 queries]
-    static constexpr int LDS = MS + 4 * TILE * 4;
-    // thread blocks of 4 rows x 4 columns per staged [64, D] tile: 16 x D/4
-    static constexpr int BLOCKS = 16 * (D / 4);
+    static constexpr int STG0 = 2 * KEYS * RSTR;
+    static constexpr int SDO = TILE * QSTR;
+    static constexpr int SL = 2 * TILE * QSTR;
+    static constexpr int SD = SL + TILE * 4;
+    static constexpr int SM = SD + TILE * 4;
+    static constexpr int STG = ((SM + 4 * TILE * 4 + 1023) / 1024) * 1024;
+    static constexpr int LDS = STG0 + 2 * STG;
+    static constexpr int QNB = TILE * QSTR / 1024;  // 1-KB DMA blocks per Q or dO tile
+    static constexpr int QPW = (QNB + NW - 1) / NW;
+    static_assert(TILE * QSTR % 1024 == 0 && STG0 % 1024 == 0, "tiles must be whole DMA blocks");
     // partial accumulators of the second query half, exchanged at the end
     static constexpr int XCH = 4 * 2 * DB * 16 * 64 * 4;
     static_assert(XCH <= LDS, "reduction buffer must fit the staging space");
     static constexpr int OSTR = 2 * 64 + 16;     // bytes per staged row of 64 dK or dV columns
     static_assert(4 * 2 * 32 * OSTR <= LDS, "the staged dK and dV rows must fit");
 };
-
-// The 4-row x 4-column block b of a [64, D] tile (rows 4kg.., columns 4dq..): the
-// block -> (kg, dq) map keeps the transposed writes of a half-wave conflict-free.
-__device__ __forceinline__ int blk_dq(int b) { return (b & 3) + 4 * (b >> 6); }
-__device__ __forceinline__ int blk_kg(int b)
-{
-    return ((b >> 2) & 3) + 4 * (((b >> 4) & 1) + 2 * ((b >> 5) & 1));
-}
-
-// Write a loaded 4x4 block as four 8-byte row segments of a padded row tile.
-template <int RSTR>
-__device__ __forceinline__ void store_row_block(char* dst, int kg, int dq, const u32x2* r)
-{
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-        *reinterpret_cast<u32x2*>(dst + (4 * kg + m) * RSTR + 8 * dq) = r[m];
-}
 
 template <typename T, int D, bool CAUSAL, bool DROP = false, bool MASK = false>
 __global__ __launch_bounds__(DkvTile<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
@@ -155,7 +142,7 @@ void fa_bwd_dkv_kernel(const BwdParams<T> prm)
     const int k0 = kt * P::KEYS;
 
     const int tid = (int)threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int kl = lane & 31;
     const int hh = lane >> 5;
@@ -201,121 +188,140 @@ void fa_bwd_dkv_kernel(const BwdParams<T> prm)
     const int nqt = (Nq + P::TILE - 1) / P::TILE;
     const int i0 = CAUSAL ? min(nqt, k0 / P::TILE) : 0;
 
-    // staging of Q and dO: each thread loads one 4x4 block of one tensor (d = 64:
-    // threads split between Q and dO) one tile ahead, and writes it both as rows and
-    // transposed
-    constexpr int PER = P::BLOCKS >= P::NT ? 2 : 1;  // tensors per thread
-    const int sb = P::BLOCKS >= P::NT ? tid : tid % P::BLOCKS;
-    const bool first_t = P::BLOCKS >= P::NT || tid < P::BLOCKS;  // Q (else dO)
-    const int s_kg = blk_kg(sb), s_dq = blk_dq(sb);
-    u32x2 sreg[PER][4];
-    auto load_tile = [&](int i) {
-        if (PER == 2) {
-            load_v_block<D>(Qh, i, Nq, s_kg, s_dq, sreg[0]);
-            load_v_block<D>(dOh, i, Nq, s_kg, s_dq, sreg[PER - 1]);
-        } else {
-            load_v_block<D>(first_t ? Qh : dOh, i, Nq, s_kg, s_dq, sreg[0]);
-        }
-    };
-    auto store_tile = [&](int i) {
+    // staging of query tile i into buffer s, issued a tile ahead: the Q and dO rows by
+    // DMA (rows past Nq read as zero), the 64 queries' L2 and D and the mask words
+    // through registers, written to LDS at the end of the tile before
+    int qsrc[P::QPW];
 #pragma unroll
-        for (int t = 0; t < PER; ++t) {
-            const bool is_q = PER == 2 ? t == 0 : first_t;
-            store_row_block<P::RSTR>(smem + (is_q ? P::QR : P::DOR), s_kg, s_dq, sreg[t]);
-            store_vt_block<P::TSTR>(smem + (is_q ? P::QT : P::DOT), s_kg, s_dq, sreg[t]);
-        }
+    for (int k = 0; k < P::QPW; ++k)
+        qsrc[k] = dma_src<D>(wave + P::NW * k, lane, P::QSTR);
+    auto stage_rows = [&](int i, int s) {
+        char* const b = smem + P::STG0 + s * P::STG;
+        stage_tile_asm<D, P::QNB, P::QPW, P::NW>(Qh, i, Nq, b, wave, qsrc);
+        stage_tile_asm<D, P::QNB, P::QPW, P::NW>(dOh, i, Nq, b + P::SDO, wave, qsrc);
+    };
+    float n_l2 = 0.f, n_d = 0.f;
+    uint32_t n_mw = 0u;
+    auto load_small = [&](int i) {
         if (tid < P::TILE) {
             const int q = i * P::TILE + tid;
             // rows past Nq: P = exp2(-inf) = 0
-            reinterpret_cast<float*>(smem + P::LS)[tid] = q < Nq ? Lh[q] * kLog2e : __builtin_inff();
-            reinterpret_cast<float*>(smem + P::DS)[tid] = q < Nq ? Dh[q] : 0.f;
+            n_l2 = q < Nq ? Lh[q] * kLog2e : __builtin_inff();
+            n_d = q < Nq ? Dh[q] : 0.f;
         }
         if (MASK && tid < 4 * P::TILE) {
             // word kw of query row q: the bits of keys k0 + 32 kw .. +31 (rows past Nq and
             // words past the row read as 0)
             const int q = i * P::TILE + (tid >> 2), kw = tid & 3;
             const int word = k0 / 32 + kw;
-            reinterpret_cast<uint32_t*>(smem + P::MS)[kw * P::TILE + (tid >> 2)] =
-                (q < Nq && word < prm.mask_w) ? mslice[(size_t)q * prm.mask_w + word] : 0u;
+            n_mw = (q < Nq && word < prm.mask_w) ? mslice[(size_t)q * prm.mask_w + word] : 0u;
         }
     };
+    auto store_small = [&](int s) {
+        char* const b = smem + P::STG0 + s * P::STG;
+        if (tid < P::TILE) {
+            reinterpret_cast<float*>(b + P::SL)[tid] = n_l2;
+            reinterpret_cast<float*>(b + P::SD)[tid] = n_d;
+        }
+        if (MASK && tid < 4 * P::TILE)
+            reinterpret_cast<uint32_t*>(b + P::SM)[(tid & 3) * P::TILE + (tid >> 2)] = n_mw;
+    };
+    // all of this wave's memory operations complete (the DMA among them), then the
+    // workgroup barrier
+    auto barrier_all = [&]() {
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+    };
 
-    const int rbase = kl * P::RSTR + hh * 16;   // row-tile operand: row kl, chunk 8hh
-    const int tbase = kl * P::TSTR + hh * 16;   // transposed-tile operand
+    const int rbase = kl * P::RSTR + hh * 16;   // K, V operand: row kl, chunk 8hh
     const int kbase = P::KS + 32 * kblk * P::RSTR + rbase;
     const int vbase = P::VS + 32 * kblk * P::RSTR + rbase;
+    const int qbase = (32 * qh + kl) * P::QSTR + hh * 16;  // Q, dO row operand of this half
+    // transposing reads of Q and dO (tr_operand): chunk 2qh + h of the tile
+    const int tbase = (4 * hh + ((lane >> 2) & 3)) * P::QSTR + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
-    if (i0 < nqt)
-        load_tile(i0);
+    if (i0 < nqt) {
+        stage_rows(i0, i0 & 1);
+        load_small(i0);
+        store_small(i0 & 1);
+    }
+    barrier_all();  // K, V and the first tile are staged
     for (int i = i0; i < nqt; ++i) {
-        wg_barrier();  // the previous tile is consumed (and K, V are staged)
-        store_tile(i);
-        wg_barrier();
-        if (i + 1 < nqt)
-            load_tile(i + 1);  // in flight while this tile is computed
-        const int qw = i * P::TILE + 32 * qh;  // first query of this wave's half
-        if (CAUSAL && qw + 31 < kw0)
-            continue;  // every query of the half precedes every key of the block
-        const bool diag = CAUSAL && (qw < kw0 + 31);
-        // S = Q K^T and dP = dO V^T for the 32 queries of this half
-        f32x16 s = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-        f32x16 dp = s;
-#pragma unroll
-        for (int c = 0; c < P::DC; ++c) {
-            const vec kf = *reinterpret_cast<const vec*>(sm + kbase + 32 * c);
-            const vec a = *reinterpret_cast<const vec*>(sm + P::QR + rbase + 32 * qh * P::RSTR + 32 * c);
-            s = M::mma(a, kf, s);
-            const vec vf = *reinterpret_cast<const vec*>(sm + vbase + 32 * c);
-            const vec b = *reinterpret_cast<const vec*>(sm + P::DOR + rbase + 32 * qh * P::RSTR + 32 * c);
-            dp = M::mma(b, vf, dp);
+        const int s = i & 1;
+        if (i + 1 < nqt) {  // in flight while this tile is computed
+            stage_rows(i + 1, s ^ 1);
+            load_small(i + 1);
         }
-        // P = 2^(s c2 - L2), dS = P (dP - D); register r holds query
-        // qw + 8(r/4) + 4hh + r%4.  With dropout Z: dV takes P o Z, dS takes dP o Z.
-        vec pp[2], ps[2];
-        uint32_t dw[4];  // group g: queries i TILE + 32qh + 8g + 4hh + 0..3
-        if (DROP)
-            drop_words_k4(prm.drop, bh, i * P::TILE + 32 * qh + 4 * hh, my_k, dw);
+        const char* const b = sm + P::STG0 + s * P::STG;
+        const int qw = i * P::TILE + 32 * qh;  // first query of this wave's half
+        // a half whose every query precedes every key of the block has nothing to add
+        if (!(CAUSAL && qw + 31 < kw0)) {
+            const bool diag = CAUSAL && (qw < kw0 + 31);
+            // S = Q K^T and dP = dO V^T for the 32 queries of this half
+            f32x16 sacc = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+            f32x16 dp = sacc;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int qo = 32 * qh + 8 * g + 4 * hh;
-            const f32x4 l2 = *reinterpret_cast<const f32x4*>(sm + P::LS + qo * 4);
-            const f32x4 dd = *reinterpret_cast<const f32x4*>(sm + P::DS + qo * 4);
-            u32x4 mw = {0u, 0u, 0u, 0u};
-            if (MASK)
-                mw = *reinterpret_cast<const u32x4*>(sm + P::MS + (kblk * P::TILE + qo) * 4);
-            uint32_t bytes = 0;
+            for (int c = 0; c < P::DC; ++c) {
+                const vec kf = *reinterpret_cast<const vec*>(sm + kbase + 32 * c);
+                const vec a = *reinterpret_cast<const vec*>(b + qbase + 32 * c);
+                sacc = M::mma(a, kf, sacc);
+                const vec vf = *reinterpret_cast<const vec*>(sm + vbase + 32 * c);
+                const vec a2 = *reinterpret_cast<const vec*>(b + P::SDO + qbase + 32 * c);
+                dp = M::mma(a2, vf, dp);
+            }
+            // P = 2^(s c2 - L2), dS = P (dP - D); register r holds query
+            // qw + 8(r/4) + 4hh + r%4.  With dropout Z: dV takes P o Z, dS takes dP o Z.
+            vec pp[2], ps[2];
+            uint32_t dw[4];  // group g: queries i TILE + 32qh + 8g + 4hh + 0..3
             if (DROP)
-                bytes = dw[g];
+                drop_words_k4(prm.drop, bh, i * P::TILE + 32 * qh + 4 * hh, my_k, dw);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * g + e;
-                float p = exp2_fast(fmaf(s[r], prm.c2, -l2[e]));
-                if (diag && my_k > i * P::TILE + qo + e)
-                    p = 0.f;  // key after the query
-                if (MASK && !((mw[e] >> kl) & 1u))
-                    p = 0.f;  // key hidden by the caller's mask (also for a row with L = -inf)
-                if (DROP) {
-                    const float z = drop_keep(bytes, e, prm.drop.t) ? prm.drop.keep_scale : 0.f;
-                    pp[r >> 3][r & 7] = (T)(p * z);
-                    ps[r >> 3][r & 7] = (T)(p * (dp[r] * z - dd[e]));
-                } else {
-                    pp[r >> 3][r & 7] = (T)p;
-                    ps[r >> 3][r & 7] = (T)(p * (dp[r] - dd[e]));
+            for (int g = 0; g < 4; ++g) {
+                const int qo = 32 * qh + 8 * g + 4 * hh;
+                const f32x4 l2 = *reinterpret_cast<const f32x4*>(b + P::SL + qo * 4);
+                const f32x4 dd = *reinterpret_cast<const f32x4*>(b + P::SD + qo * 4);
+                u32x4 mw = {0u, 0u, 0u, 0u};
+                if (MASK)
+                    mw = *reinterpret_cast<const u32x4*>(b + P::SM + (kblk * P::TILE + qo) * 4);
+                uint32_t bytes = 0;
+                if (DROP)
+                    bytes = dw[g];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g + e;
+                    float p = exp2_fast(fmaf(sacc[r], prm.c2, -l2[e]));
+                    if (diag && my_k > i * P::TILE + qo + e)
+                        p = 0.f;  // key after the query
+                    if (MASK && !((mw[e] >> kl) & 1u))
+                        p = 0.f;  // key hidden by the caller's mask (also for a row with L = -inf)
+                    if (DROP) {
+                        const float z = drop_keep(bytes, e, prm.drop.t) ? prm.drop.keep_scale : 0.f;
+                        pp[r >> 3][r & 7] = (T)(p * z);
+                        ps[r >> 3][r & 7] = (T)(p * (dp[r] * z - dd[e]));
+                    } else {
+                        pp[r >> 3][r & 7] = (T)p;
+                        ps[r >> 3][r & 7] = (T)(p * (dp[r] - dd[e]));
+                    }
+                }
+            }
+            // dV^T += dO^T P, dK^T += Q^T dS over chunks 2qh, 2qh+1 of the tile, the
+            // transposed operands read straight from the row tiles
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int cc = 2 * qh + h;
+#pragma unroll
+                for (int db = 0; db < P::DB; ++db) {
+                    const char* const tp = b + tbase + 16 * cc * P::QSTR + 64 * db;
+                    dvt[db] = M::mma(tr_operand<P::QSTR, vec>(tp + P::SDO), pp[h], dvt[db]);
+                    dkt[db] = M::mma(tr_operand<P::QSTR, vec>(tp), ps[h], dkt[db]);
                 }
             }
         }
-        // dV^T += dO^T P, dK^T += Q^T dS over chunks 2qh, 2qh+1 of the tile
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int cc = 2 * qh + h;
-#pragma unroll
-            for (int db = 0; db < P::DB; ++db) {
-                const vec a = *reinterpret_cast<const vec*>(sm + P::DOT + tbase + 32 * db * P::TSTR + 32 * cc);
-                dvt[db] = M::mma(a, pp[h], dvt[db]);
-                const vec b = *reinterpret_cast<const vec*>(sm + P::QT + tbase + 32 * db * P::TSTR + 32 * cc);
-                dkt[db] = M::mma(b, ps[h], dkt[db]);
-            }
-        }
+        if (i + 1 < nqt)
+            store_small(s ^ 1);
+        barrier_all();  // the next tile has landed; this one is consumed
     }
 
     // the second query half hands its partial sums to the first through LDS
@@ -387,26 +393,29 @@ void fa_bwd_dkv_kernel(const BwdParams<T> prm)
 template <int D>
 struct DqTile {
     // d = 128: 8 waves (256 queries) per workgroup, one per CU; d = 64: 4 waves (128
-    // queries), two per CU; either way each thread stages one 4x4 block of K
+    // queries), two per CU
     static constexpr int NW = D == 128 ? 8 : 4;
     static constexpr int NT = 64 * NW;
     static constexpr int ROWS = 32 * NW;        // queries per workgroup
     static constexpr int TILE = 64;             // keys per step
-    static constexpr int RSTR = 2 * D + 16;
-    static constexpr int TSTR = 2 * TILE + 16;
+    static constexpr int RSTR = 2 * D + 16;     // V rows
+    // K rows: read as rows (S^T = K Q^T) and transposed (dQ^T += K^T dS^T); with 2D + 48
+    // bytes the first is conflict-free and the second meets at most 2-way
+    static constexpr int KSTR = 2 * D + 48;
     static constexpr int DC = D / 16;
     static constexpr int DB = D / 32;
-    static constexpr int KR = 0;                       // K row tile
-    static constexpr int VR = TILE * RSTR;             // V row tile
-    static constexpr int KT = 2 * TILE * RSTR;         // K transposed tile
-    static constexpr int VR1 = KT + D * TSTR;          // second V row tile (DMA, double-buffered)
-    static constexpr int LDS = VR1 + TILE * RSTR;
-    static constexpr int VNB = TILE * RSTR / 1024;     // 1-KB DMA blocks per V tile
+    // LDS: two buffers each of K rows and V rows, DMA'd a tile ahead
+    static constexpr int KB = TILE * KSTR;
+    static constexpr int VB = TILE * RSTR;
+    static constexpr int VOFF = 2 * KB;
+    static constexpr int LDS = 2 * KB + 2 * VB;
+    static constexpr int KNB = KB / 1024;       // 1-KB DMA blocks per K or V tile
+    static constexpr int VNB = VB / 1024;
+    static constexpr int KPW = (KNB + NW - 1) / NW;
     static constexpr int VPW = (VNB + NW - 1) / NW;
-    static_assert(TILE * RSTR % 1024 == 0, "V tiles must be whole DMA blocks");
+    static_assert(KB % 1024 == 0 && VB % 1024 == 0, "tiles must be whole DMA blocks");
     static constexpr int OSTR = 2 * 64 + 16;     // bytes per staged row of 64 dQ columns
     static_assert(NW * 32 * OSTR <= LDS, "the staged dQ rows must fit the tiles");
-    static_assert(NT == 4 * D, "one 4x4 block of K per thread");
 };
 
 template <typename T, int D, bool CAUSAL, bool DROP = false, bool MASK = false>
@@ -427,7 +436,7 @@ void fa_bwd_dq_kernel(const BwdParams<T> prm)
     const int q0 = qt * P::ROWS;
 
     const int tid = (int)threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int ql = lane & 31;
     const int hh = lane >> 5;
@@ -447,19 +456,28 @@ void fa_bwd_dq_kernel(const BwdParams<T> prm)
     if (CAUSAL && wave_active)
         n_w = min(nkt, min(qw0 + 31, Nq - 1) / P::TILE + 1);
 
-    // staging: this thread's 4x4 block of K, loaded one tile ahead and written as a row
-    // tile and transposed; V's row tile by DMA straight into LDS, a tile ahead into
-    // the other of two buffers
-    const int s_kg = blk_kg(tid), s_dq = blk_dq(tid);
-    u32x2 kreg[4];
-    int vsrc[P::VPW];
+    // staging: K and V rows of key tile j by DMA into buffer j % 2, issued a tile ahead
+    int ksrc[P::KPW], vsrc[P::VPW];
+#pragma unroll
+    for (int i = 0; i < P::KPW; ++i)
+        ksrc[i] = dma_src<D>(wave + P::NW * i, lane, P::KSTR);
 #pragma unroll
     for (int i = 0; i < P::VPW; ++i)
         vsrc[i] = dma_src<D>(wave + P::NW * i, lane, P::RSTR);
-    if (0 < nkt) {
-        load_v_block<D>(Kh, 0, Nk, s_kg, s_dq, kreg);
-        stage_tile<D, P::VNB, P::VPW, P::NW>(Vh, 0, Nk, smem + P::VR, wave, vsrc);
-    }
+    auto stage = [&](int j, int buf) {
+        stage_tile_asm<D, P::KNB, P::KPW, P::NW>(Kh, j, Nk, smem + buf * P::KB, wave, ksrc);
+        stage_tile_asm<D, P::VNB, P::VPW, P::NW>(Vh, j, Nk, smem + P::VOFF + buf * P::VB, wave, vsrc);
+    };
+    // all of this wave's memory operations complete (the DMA among them), then the
+    // workgroup barrier
+    auto barrier_all = [&]() {
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+    };
+    if (0 < nkt)
+        stage(0, 0);
 
     // Q and dO rows of this lane's query as the B operands
     vec qf[P::DC], df[P::DC];
@@ -495,84 +513,81 @@ void fa_bwd_dq_kernel(const BwdParams<T> prm)
     for (int db = 0; db < P::DB; ++db)
         dqt[db] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 
-    const int rbase = ql * P::RSTR + hh * 16;
-    const int tbase = ql * P::TSTR + hh * 16;
+    const int kbase = ql * P::KSTR + hh * 16;   // K row operand: row ql, chunk 8hh
+    const int vbase = ql * P::RSTR + hh * 16;
+    // transposing reads of K (tr_operand): chunk cc of the tile, 32 dims per block
+    const int tbase = (4 * hh + ((lane >> 2) & 3)) * P::KSTR + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
+    barrier_all();  // K_0 and V_0 have landed
     for (int j = 0; j < nkt; ++j) {
-        wg_barrier();  // the previous tile is consumed
-        store_row_block<P::RSTR>(smem + P::KR, s_kg, s_dq, kreg);
-        store_vt_block<P::TSTR>(smem + P::KT, s_kg, s_dq, kreg);
-        __builtin_amdgcn_s_waitcnt(0x0070);  // this wave's DMA blocks of V_j have landed
-        wg_barrier();
-        const int vr = (j & 1) ? P::VR1 : P::VR;
-        if (j + 1 < nkt) {  // in flight while this tile is computed
-            load_v_block<D>(Kh, j + 1, Nk, s_kg, s_dq, kreg);
-            stage_tile<D, P::VNB, P::VPW, P::NW>(Vh, j + 1, Nk, smem + ((j & 1) ? P::VR : P::VR1),
-                                                 wave, vsrc);
-        }
-        if (j >= n_w)
-            continue;
-        // S^T = K Q^T, dP^T = V dO^T: register r of block kb holds key
-        // 32kb + 8(r/4) + 4hh + r%4 of the tile
-        f32x16 st[2], dpt[2];
+        const int buf = j & 1;
+        if (j + 1 < nkt)  // in flight while this tile is computed
+            stage(j + 1, buf ^ 1);
+        if (j < n_w) {
+            const char* const kt = sm + buf * P::KB;
+            const char* const vr = sm + P::VOFF + buf * P::VB;
+            // S^T = K Q^T, dP^T = V dO^T: register r of block kb holds key
+            // 32kb + 8(r/4) + 4hh + r%4 of the tile
+            f32x16 st[2], dpt[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            st[kb] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-            dpt[kb] = st[kb];
+            for (int kb = 0; kb < 2; ++kb) {
+                st[kb] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+                dpt[kb] = st[kb];
 #pragma unroll
-            for (int c = 0; c < P::DC; ++c) {
-                const vec a = *reinterpret_cast<const vec*>(sm + P::KR + rbase + 32 * kb * P::RSTR + 32 * c);
-                st[kb] = M::mma(a, qf[c], st[kb]);
-                const vec b = *reinterpret_cast<const vec*>(sm + vr + rbase + 32 * kb * P::RSTR + 32 * c);
-                dpt[kb] = M::mma(b, df[c], dpt[kb]);
+                for (int c = 0; c < P::DC; ++c) {
+                    const vec a = *reinterpret_cast<const vec*>(kt + kbase + 32 * kb * P::KSTR + 32 * c);
+                    st[kb] = M::mma(a, qf[c], st[kb]);
+                    const vec b = *reinterpret_cast<const vec*>(vr + vbase + 32 * kb * P::RSTR + 32 * c);
+                    dpt[kb] = M::mma(b, df[c], dpt[kb]);
+                }
             }
-        }
-        const int key0 = j * P::TILE;
-        const bool mask = (key0 + P::TILE > Nk) || (CAUSAL && key0 + P::TILE - 1 > qw0);
-        const int last = CAUSAL ? min(Nk - 1, my_q) : Nk - 1;
-        // this lane's caller-mask bits of the tile, shifted so that register r of block kb
-        // finds its key at bit 8 (r / 4) + r % 4 of cm[kb]; then the next tile's words
-        uint32_t cm[2] = {~0u, ~0u};
-        if (MASK) {
-            cm[0] = mw[0] >> (4 * hh);
-            cm[1] = mw[1] >> (4 * hh);
-            if (j + 1 < n_w)
-                load_mask(j + 1);
-        }
-        vec ps[4];
-        uint32_t dw[8];  // group 2cc + g: keys key0 + 16cc + 8g + 4hh + 0..3
-        if (DROP)
-            drop_words_q8(prm.drop, bh, my_q, key0 + 4 * hh, dw);
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-            // chunk cc holds keys 16cc + 4hh + 0..3 (e < 4) and 16cc + 8 + 4hh + 0..3
-            uint32_t bytes[2] = {0u, 0u};
-            if (DROP) {
-                bytes[0] = dw[2 * cc];
-                bytes[1] = dw[2 * cc + 1];
+            const int key0 = j * P::TILE;
+            const bool mask = (key0 + P::TILE > Nk) || (CAUSAL && key0 + P::TILE - 1 > qw0);
+            const int last = CAUSAL ? min(Nk - 1, my_q) : Nk - 1;
+            // this lane's caller-mask bits of the tile, shifted so that register r of block
+            // kb finds its key at bit 8 (r / 4) + r % 4 of cm[kb]; then the next tile's words
+            uint32_t cm[2] = {~0u, ~0u};
+            if (MASK) {
+                cm[0] = mw[0] >> (4 * hh);
+                cm[1] = mw[1] >> (4 * hh);
+                if (j + 1 < n_w)
+                    load_mask(j + 1);
             }
+            vec ps[4];
+            uint32_t dw[8];  // group 2cc + g: keys key0 + 16cc + 8g + 4hh + 0..3
+            if (DROP)
+                drop_words_q8(prm.drop, bh, my_q, key0 + 4 * hh, dw);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int kb = cc >> 1, r = 8 * (cc & 1) + e;
-                float p = exp2_fast(fmaf(st[kb][r], prm.c2, -l2));
-                if (mask && key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3) > last)
-                    p = 0.f;
-                if (MASK && !((cm[kb] >> (8 * (r >> 2) + (r & 3))) & 1u))
-                    p = 0.f;  // key hidden by the caller's mask (also for a row with L = -inf)
-                float dpz = dpt[kb][r];
-                if (DROP)
-                    dpz *= drop_keep(bytes[e >> 2], e & 3, prm.drop.t) ? prm.drop.keep_scale : 0.f;
-                ps[cc][e] = (T)(p * (dpz - dd));
+            for (int cc = 0; cc < 4; ++cc) {
+                // chunk cc holds keys 16cc + 4hh + 0..3 (e < 4) and 16cc + 8 + 4hh + 0..3
+                uint32_t bytes[2] = {0u, 0u};
+                if (DROP) {
+                    bytes[0] = dw[2 * cc];
+                    bytes[1] = dw[2 * cc + 1];
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int kb = cc >> 1, r = 8 * (cc & 1) + e;
+                    float p = exp2_fast(fmaf(st[kb][r], prm.c2, -l2));
+                    if (mask && key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3) > last)
+                        p = 0.f;
+                    if (MASK && !((cm[kb] >> (8 * (r >> 2) + (r & 3))) & 1u))
+                        p = 0.f;  // key hidden by the caller's mask (also for a row with L = -inf)
+                    float dpz = dpt[kb][r];
+                    if (DROP)
+                        dpz *= drop_keep(bytes[e >> 2], e & 3, prm.drop.t) ? prm.drop.keep_scale : 0.f;
+                    ps[cc][e] = (T)(p * (dpz - dd));
+                }
             }
+            // dQ^T += K^T dS^T, K^T read transposed from the K rows
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+                for (int db = 0; db < P::DB; ++db)
+                    dqt[db] = M::mma(tr_operand<P::KSTR, vec>(kt + tbase + 16 * cc * P::KSTR + 64 * db),
+                                     ps[cc], dqt[db]);
         }
-        // dQ^T += K^T dS^T
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-            for (int db = 0; db < P::DB; ++db) {
-                const vec a = *reinterpret_cast<const vec*>(sm + P::KT + tbase + 32 * db * P::TSTR + 32 * cc);
-                dqt[db] = M::mma(a, ps[cc], dqt[db]);
-            }
+        barrier_all();  // the next tile has landed; this one is consumed
     }
 
     // dQ rows through this wave's LDS rows, 64 columns at a time (the K and V tiles

@@ -109,6 +109,50 @@ __device__ __forceinline__ void stage_tile(const T* head, int tile, int nrows, c
     }
 }
 
+// As stage_tile, with each DMA issued from inline assembly.  The compiler then does
+// not see these writes into LDS, and so does not make the transposing LDS reads
+// (ds_read_b64_tr_b16) that follow wait for every DMA the wave has in flight, which
+// it does for DMA it can see.  The caller orders every read of a tile staged this way
+// after a wait for its DMA (s_waitcnt vmcnt in every issuing wave, then a workgroup
+// barrier), as the other waves' blocks require anyway.  M0 holds the LDS address of
+// the block for the instruction that follows.
+template <int D, int NB, int PW, int NW, typename T>
+__device__ __forceinline__ void stage_tile_asm(const T* head, int tile, int nrows, char* dst,
+                                               int wave, const int* src)
+{
+    const __amdgpu_buffer_rsrc_t r = rows_rsrc<D>(head, tile * 64, nrows);
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+        const int blk = wave + NW * i;
+        if (blk < NB) {
+            const uint32_t lds = (uint32_t)(uintptr_t)(lds_char*)(dst + blk * 1024);
+            __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                             :
+                             : "s"(lds), "v"(src[i]), "s"(r)
+                             : "memory");
+        }
+    }
+}
+
+// Transposing read of a 16-bit A operand (32 rows of the operand x 16 k-slots) from a
+// row-major LDS tile whose rows are the k dimension: two ds_read_b64_tr_b16 at `p` and
+// 8 rows further.  Lane (h = lane / 32, g = (lane / 16) % 2, j = lane % 16) passes
+// p = tile + (4h + j / 4) * stride + 2 (16g + 4 (j % 4)) (+ 16 rows per 16-slot chunk,
+// + 64 bytes per 32 columns); it receives column 16g + j (+ 32 per 64 bytes) with
+// k-slots 8h + 4r + e holding rows 8r + 4h + e of the chunk (r = 0, 1; e = 0..3), the
+// order in which a 32x32 accumulator rounded to T holds them.
+template <int STR, typename V>
+__device__ __forceinline__ V tr_operand(const char* p)
+{
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * STR));
+    const s16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(V, w);
+}
+
 // V staging of one thread: the 4-key x 4-dim block (keys 4kg..4kg+3, dims
 // 4dq..4dq+3) of 64-key tile `tile`, loaded as four 8-byte rows (rows past nrows
 // read 0).
