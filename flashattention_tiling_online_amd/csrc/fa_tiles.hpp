@@ -120,12 +120,21 @@ template <int D, int NB, int PW, int NW, typename T>
 __device__ __forceinline__ void stage_tile_asm(const T* head, int tile, int nrows, char* dst,
                                                int wave, const int* src)
 {
-    const __amdgpu_buffer_rsrc_t r = rows_rsrc<D>(head, tile * 64, nrows);
+    // the resource of rows_rsrc as four words (base, stride 0, records, word 3), each
+    // read from the first lane so that it sits in SGPRs however the code is optimised
+    const int row0 = tile * 64;
+    const int64_t n = nrows > row0 ? nrows - row0 : 0;
+    const int64_t bytes = n * D * (int64_t)sizeof(T);
+    const uint64_t base = (uint64_t)(uintptr_t)(head + (size_t)row0 * D);
+    const u32x4 r = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base),
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(base >> 32) & 0xffffu)),
+                     (uint32_t)__builtin_amdgcn_readfirstlane(bytes < kRsrcCap ? (int)bytes : kRsrcCap),
+                     (uint32_t)kRsrcWord3};
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
         const int blk = wave + NW * i;
         if (blk < NB) {
-            const uint32_t lds = (uint32_t)(uintptr_t)(lds_char*)(dst + blk * 1024);
+            const int lds = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_char*)(dst + blk * 1024));
             __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                              :
                              : "s"(lds), "v"(src[i]), "s"(r)

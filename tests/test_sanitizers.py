@@ -50,8 +50,9 @@ def test_abi_host_checks_under_asan_ubsan(tmp_path):
     obj = str(tmp_path / "fa_abi.o")
     exe = str(tmp_path / "abi_san")
     inc = ["-I", os.path.join(ROOT, "include")]
-    # device code at -O0: it is compiled for the link but never launched
-    subprocess.run([HIPCC, "--offload-arch=gfx950", "-O1", "-Xarch_device", "-O0",
+    # device code at -O1 (the least that keeps the DMA's inline-assembly operands in
+    # scalar registers): it is compiled for the link but never launched
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-O1", "-Xarch_device", "-O1",
                     "-Xarch_device", "-g0", "-g", "-std=c++17", "-fPIC", *HOST_SAN,
                     "-fno-omit-frame-pointer", "-Xclang", "-target-feature", "-Xclang",
                     "-packed-fp32-ops", *inc, "-c",
