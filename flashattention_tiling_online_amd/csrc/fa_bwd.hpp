@@ -18,10 +18,11 @@
 //     queries, lane = query, the forward's orientation; 128 queries for d = 64),
 //     looping over 64-key tiles: S^T = K Q^T and dP^T = V dO^T with Q and dO in
 //     registers, then dQ^T += K^T dS^T.
-// Both main kernels stage row tiles and transposed tiles through LDS in the layouts
-// of fa_tiles.hpp, each thread loading one 4x4 block per tensor one tile ahead and
-// writing it in both layouts; exp is exp2 with scale * log2(e) folded into one FMA
-// and L taken in base 2.  With a caller mask (the blog page's Algorithm 4 recomputes P
+// Both main kernels stage the streamed tiles (Q and dO; K and V) as rows by DMA into
+// two LDS buffers, a tile ahead, and read the operands that contract over the tile's
+// rows (Q^T, dO^T; K^T) straight from those rows with the transposing LDS read
+// (tr_operand, fa_tiles.hpp), so one barrier per tile covers the staging; exp is exp2
+// with scale * log2(e) folded into one FMA and L taken in base 2.  With a caller mask (the blog page's Algorithm 4 recomputes P
 // from mask(S)) a hidden (query, key) gets P = 0, which also covers the rows with no
 // visible key (L = -inf, no gradient).
 #pragma once
