@@ -1,16 +1,19 @@
 // fa_tiles.hpp — operand tiles shared by the gfx950 attention kernels.
 //
 // The kernels contract 32x32 blocks on v_mfma_f32_32x32x16_{bf16,f16}.  An A operand
-// comes from LDS in one of two layouts, B from registers:
-//   * row tiles: a [64, D] block of a [rows, D] matrix (K, V, Q or dO) with rows
-//     padded to 2D + 16 bytes; lane (row = lane % 32, half h) reads elements
-//     16c + 8h .. +8 of its row with one ds_read_b128 — the A operand of a product
-//     that contracts over D (S = Q K^T, dP = dO V^T and their transposes);
-//   * transposed tiles: D rows of 64 entries (144-byte stride), entries stored in
-//     the order a 32x32 accumulator holds them in registers (slots 16c + 8h + 0..3
-//     hold entries 16c + 4h + 0..3, slots 16c + 8h + 4..7 hold 16c + 8 + 4h + 0..3),
-//     so that an accumulator rounded to T is the matching B operand as it stands
-//     (O^T += V^T P^T, dV^T += dO^T P, dK^T += Q^T dS, dQ^T += K^T dS^T);
+// comes from LDS, B from registers:
+//   * row tiles: a [64, D] block of a [rows, D] matrix (K, V, Q or dO) with padded
+//     rows; lane (row = lane % 32, half h) reads elements 16c + 8h .. +8 of its row
+//     with one ds_read_b128 — the A operand of a product that contracts over D
+//     (S = Q K^T, dP = dO V^T and their transposes);
+//   * the same row tiles read transposed (tr_operand): the A operand of a product
+//     that contracts over the tile's rows (O^T += V^T P^T, dV^T += dO^T P,
+//     dK^T += Q^T dS, dQ^T += K^T dS^T), its k-slots in the order a 32x32 accumulator
+//     holds them in registers, so that the accumulator rounded to T is the matching B
+//     operand as it stands;
+//   * transposed tiles (the d = 64 forward): D rows of 64 entries (144-byte stride),
+//     written from registers in that same order (slots 16c + 8h + 0..3 hold entries
+//     16c + 4h + 0..3, slots 16c + 8h + 4..7 hold 16c + 8 + 4h + 0..3);
 //   * loads go through buffer resources bounded by the head's rows, so rows past the
 //     end read as zero.
 #pragma once
