@@ -103,9 +103,6 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     using vec = typename M::vec;
     constexpr int D = P::D;
     typedef T T4 __attribute__((ext_vector_type(4)));
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     __shared__ __attribute__((aligned(1024))) char smem[P::LDS];
     const char* const sm = smem;
     const int Nq = prm.Nq, Nk = prm.Nk, n_qtiles = prm.n_qtiles;
@@ -227,18 +224,13 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     // phase starts on operands already in registers (their tiles have landed by then:
     // see the staging schedule above).
     constexpr int NPRE = 2;  // one, three or four pairs time 0.5-1 % slower
-    vec pre_k[NPRE];
-    s16x4 pre_v[NPRE][2];
-    auto v_read = [&](const char* vp, s16x4* out) {
-        out[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
-        out[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * P::VSTR));
-    };
+    vec pre_k[NPRE], pre_v[NPRE];
     auto pre_read = [&](int kb_off, int vb_off) {
 #pragma unroll
         for (int i = 0; i < NPRE; ++i) {
             const int c = i >> 1, kb = i & 1, cc = i >> 2, db = i & 3;
             pre_k[i] = *reinterpret_cast<const vec*>(sm + kb_off + kbase + 32 * c + kb * 32 * P::KSTR);
-            v_read(sm + vb_off + vbase + 16 * cc * P::VSTR + 64 * db, pre_v[i]);
+            pre_v[i] = tr_operand<P::VSTR, vec>(sm + vb_off + vbase + 16 * cc * P::VSTR + 64 * db);
         }
     };
     // both, interleaved: S^T of tile j+1 and P.V of tile j; the operand reads run
@@ -255,15 +247,9 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
                                    : *reinterpret_cast<const vec*>(sm + kb_off + kbase + 32 * c + kb * 32 * P::KSTR);
             s[kb] = M::mma(a, qf[c], s[kb]);
             const int cc = i >> 2, db = i & 3;
-            s16x4 vv[2];
-            if (i < NPRE) {
-                vv[0] = pre_v[i][0];
-                vv[1] = pre_v[i][1];
-            } else {
-                v_read(sm + vb_off + vbase + 16 * cc * P::VSTR + 64 * db, vv);
-            }
-            const s16x8 w = {vv[0][0], vv[0][1], vv[0][2], vv[0][3], vv[1][0], vv[1][1], vv[1][2], vv[1][3]};
-            o[db] = M::mma(__builtin_bit_cast(vec, w), pb[cc], o[db]);
+            const vec b = i < NPRE ? pre_v[i]
+                                   : tr_operand<P::VSTR, vec>(sm + vb_off + vbase + 16 * cc * P::VSTR + 64 * db);
+            o[db] = M::mma(b, pb[cc], o[db]);
         }
         // the preloaded pairs first, each followed by the reads of the pair NPRE ahead
         // (3 each: one K, two V), then per MFMA pair the reads of the pair NPRE ahead,
