@@ -186,16 +186,18 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
     // ds_write_b64 conflict-free.
     const int v_dq = (gtid & 3) + 4 * (gtid >> 6);
     const int v_kg = ((gtid >> 2) & 3) + 4 * (((gtid >> 4) & 1) + 2 * ((gtid >> 5) & 1));
-    u32x2 vreg[P::VPT][4];
-    auto load_v = [&](int tile) {
+    // V of the group's local tile t sits in register slot t % 2 from its load (two
+    // steps before its V^T write) to that write
+    u32x2 vreg[2][P::VPT][4];
+    auto load_v = [&](int tile, int slot) {
 #pragma unroll
         for (int b = 0; b < P::VPT; ++b)
-            load_v_block<D>(Vh, tile, Nks, v_kg, v_dq + 4 * P::NQW * b, vreg[b]);
+            load_v_block<D>(Vh, tile, Nks, v_kg, v_dq + 4 * P::NQW * b, vreg[slot][b]);
     };
-    auto store_vt = [&](int lds_off) {
+    auto store_vt = [&](int lds_off, int slot) {
 #pragma unroll
         for (int b = 0; b < P::VPT; ++b)
-            store_vt_block<P::VTSTR>(smem + gbase + lds_off, v_kg, v_dq + 4 * P::NQW * b, vreg[b]);
+            store_vt_block<P::VTSTR>(smem + gbase + lds_off, v_kg, v_dq + 4 * P::NQW * b, vreg[slot][b]);
     };
 
     // ---- operand addresses inside a K / V^T tile: one base each, the rest immediates
@@ -227,14 +229,16 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
         load_mask(tile_of(1), 1);
     if (0 < ni_g) {
         stage_k(tile_of(0), P::K0);
-        load_v(tile_of(0));
+        load_v(tile_of(0), 0);
     }
-    if (1 < ni_g)
+    if (1 < ni_g) {
         stage_k(tile_of(1), P::K1);
+        load_v(tile_of(1), 1);  // written to LDS at the end of step 0
+    }
     if (0 < ni_g)
-        store_vt(P::V0);
-    if (1 < ni_g)
-        load_v(tile_of(1));  // written to LDS during step 0
+        store_vt(P::V0, 0);
+    if (2 < ni_g)
+        load_v(tile_of(2), 0);  // written to LDS at the end of step 1
     // Q (B operand of S^T = K Q^T): lane supplies Q[my_q][16c + 8hh .. +8]
     vec qf[P::DC];
 #pragma unroll
@@ -427,10 +431,10 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
     // as one branch-free block, the S MFMAs of the group's next tile (K buffer kn, into
     // s_nxt) and their max, together with the softmax and P.V MFMAs of tile t (V^T
     // buffer vc); a wave's last tile is masked if it needs it and has no next tile.
-    // Then the next tile's V (in registers since the last step) is written to the
+    // Then the next tile's V (in registers since two steps ago) is written to the
     // other V^T buffer vn, the barrier publishes it together with the K of local tile
     // j + 2 (DMA issued one step ago), and the next loads go out: V of local tile
-    // j + 2 into registers, K of local tile j + 3 into kn.
+    // j + 3 into the register slot just written, K of local tile j + 3 into kn.
     auto step = [&](int j, f32x16* s_cur, f32x16* s_nxt, float& m_cur, float& m_nxt, int kn,
                     int vc, int vn, auto SL) {
         constexpr int sl = decltype(SL)::value;  // mask-word slot of local tile j + 1
@@ -454,12 +458,12 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
             pv(pb, gbase + vc);
         }
         if (j + 1 < ni_g)
-            store_vt(vn);
+            store_vt(vn, sl);  // local tile j + 1 has the slot parity of sl
         wg_barrier();
         if (MASK && j + 2 < ni_w)
             load_mask(tile_of(j + 2), sl ^ 1);  // local tile j + 2 has the parity of j
-        if (j + 2 < ni_g)
-            load_v(tile_of(j + 2));
+        if (j + 3 < ni_g)
+            load_v(tile_of(j + 3), sl);  // into the slot just written
         if (j + 3 < ni_g)
             stage_k(tile_of(j + 3), kn);
     };
