@@ -34,12 +34,11 @@
 //     rows hit 64 distinct banks and every operand address is one base register
 //     plus an immediate; a DMA block is 1 KB of consecutive LDS and lanes that land
 //     on padding are masked off;
-//   * V is transposed on its way to LDS: each thread loads a 4-key x 4-dim block
-//     into registers (one tile ahead), transposes it with 8 perms and writes V^T
-//     rows with ds_write_b64, keys already in the order P has in registers; the
-//     P.V operand is then a plain ds_read_b128 (LDS transpose reads deliver a
-//     third of the bytes per cycle on gfx950); thread -> block mapping and the
-//     144-byte V^T row stride make both the writes and the reads conflict-free;
+//   * V goes to LDS by DMA as well, rows as stored (padded to 2D + 32 bytes), and
+//     the A operand of O^T = V^T P^T comes from gfx950's transposing LDS read
+//     (tr_operand in fa_tiles.hpp), its keys in the order P has in registers; the
+//     DMA is issued from inline assembly so that the compiler does not make those
+//     reads wait for every DMA in flight, and each step's barrier waits for it;
 //   * every buffer access goes through a buffer resource bounded by the head's
 //     remaining rows, so rows past Nk read as zero without a branch;
 //   * software pipeline: while the softmax of tile j and the P.V MFMAs of tile j
@@ -75,16 +74,19 @@ struct Tile16 {
     static constexpr int GT = 64 * NQW;          // threads of one key group
     static constexpr int ROWB = D * 2;           // bytes per K/V row in memory
     static constexpr int KSTR = ROWB + 16;       // K row stride in LDS
-    static constexpr int VTSTR = 2 * BC + 16;    // V^T row stride in LDS (one row per dim)
+    // V rows, read only transposed: with 2D + 32 bytes the 4 rows of a half-wave's
+    // transposing read meet at most 2-way in the banks (2D + 64 would avoid that and
+    // not fit the four key groups' buffers)
+    static constexpr int VSTR = ROWB + 32;
     static constexpr int KT = BC * KSTR;         // bytes of one K tile in LDS
-    static constexpr int VT = D * VTSTR;         // bytes of one V^T tile in LDS
+    static constexpr int VT = BC * VSTR;         // bytes of one V tile in LDS
     static constexpr int KNB = KT / 1024;        // 1-KB DMA blocks per K tile
     static constexpr int KPW = (KNB + NQW - 1) / NQW;  // K blocks per wave (at most)
-    static constexpr int VPT = 4 * D / GT;       // 4-key x 4-dim V blocks per thread and tile
-    static_assert(VPT >= 1 && VPT * GT == 4 * D, "V staging: whole 4 x 4 blocks per thread");
+    static constexpr int VNB = VT / 1024;        // 1-KB DMA blocks per V tile
+    static constexpr int VPW = (VNB + NQW - 1) / NQW;
     static constexpr int DC = D / 16;            // 16-wide d chunks of the S contraction
     static constexpr int DB = D / 32;            // 32-wide d blocks of O
-    static constexpr int GR = 2 * KT + 2 * VT;   // one key group's K[2], V^T[2]
+    static constexpr int GR = 2 * KT + 2 * VT;   // one key group's K[2], V[2]
     static constexpr int SUMS = KG * GR;         // per thread: completed row-sum blocks
     static constexpr int LDS = SUMS + 8 * NT;    // the groups' buffers, sums
     static constexpr int K0 = 0, K1 = KT, V0 = 2 * KT, V1 = 2 * KT + VT;  // in a group's
@@ -92,7 +94,7 @@ struct Tile16 {
     // (256 bytes), staged in LDS with 16 bytes of padding
     static constexpr int OSTR = (2 * D > 256 ? 2 * D : 256) + 16;
     static_assert(NQW * 32 * OSTR <= SUMS, "the epilogue's rows must fit the tile buffers");
-    static_assert(KT % 1024 == 0, "K tiles must be whole DMA blocks");
+    static_assert(KT % 1024 == 0 && VT % 1024 == 0, "tiles must be whole DMA blocks");
     // KG > 1: the state one wave of group g > 0 hands to group 0 (per lane: O^T
     // registers, this half's two row sums, the reference), past the epilogue's rows
     static constexpr int XSTR = 4 * (16 * DB + 4);   // bytes per lane
@@ -177,36 +179,31 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
 #pragma unroll
     for (int i = 0; i < P::KPW; ++i)
         ksrc[i] = dma_src<D>(qw + P::NQW * i, lane, P::KSTR);
+    int vsrc[P::VPW];
+#pragma unroll
+    for (int i = 0; i < P::VPW; ++i)
+        vsrc[i] = dma_src<D>(qw + P::NQW * i, lane, P::VSTR);
     auto stage_k = [&](int tile, int lds_off) {
-        stage_tile<D, P::KNB, P::KPW, P::NQW>(Kh, tile, Nks, smem + gbase + lds_off, qw, ksrc);
+        stage_tile_asm<D, P::KNB, P::KPW, P::NQW>(Kh, tile, Nks, smem + gbase + lds_off, qw, ksrc);
     };
-    // ---- V staging through registers: this thread's 4-key x 4-dim blocks (VPT of
-    // them; block b covers dims 4 (v_dq + 4 NQW b) ..).  Within a 32-lane half-wave the
-    // blocks cover 4 consecutive dim-quads x 8 key groups, which makes the transposed
-    // ds_write_b64 conflict-free.
-    const int v_dq = (gtid & 3) + 4 * (gtid >> 6);
-    const int v_kg = ((gtid >> 2) & 3) + 4 * (((gtid >> 4) & 1) + 2 * ((gtid >> 5) & 1));
-    // V of the group's local tile t sits in register slot t % 2 from its load (two
-    // steps before its V^T write) to that write
-    u32x2 vreg[2][P::VPT][4];
-    auto load_v = [&](int tile, int slot) {
-#pragma unroll
-        for (int b = 0; b < P::VPT; ++b)
-            load_v_block<D>(Vh, tile, Nks, v_kg, v_dq + 4 * P::NQW * b, vreg[slot][b]);
+    auto stage_v = [&](int tile, int lds_off) {
+        stage_tile_asm<D, P::VNB, P::VPW, P::NQW>(Vh, tile, Nks, smem + gbase + lds_off, qw, vsrc);
     };
-    auto store_vt = [&](int lds_off, int slot) {
-#pragma unroll
-        for (int b = 0; b < P::VPT; ++b)
-            store_vt_block<P::VTSTR>(smem + gbase + lds_off, v_kg, v_dq + 4 * P::NQW * b, vreg[slot][b]);
+    // the step's barrier: this wave's DMA has landed (and its LDS reads are done),
+    // then the workgroup barrier publishes the group's tiles
+    auto dma_barrier = [&]() {
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+        wg_barrier();
     };
 
-    // ---- operand addresses inside a K / V^T tile: one base each, the rest immediates
+    // ---- operand addresses inside a K / V tile: one base each, the rest immediates
     // K (A operand of S^T): lane reads K[32kb + ql][16c + 8hh .. +8] at
     // kbase + 32c + 32kb*KSTR.
     const int kbase = ql * P::KSTR + hh * 16;
-    // V^T (A operand of O^T): lane reads V^T[32db + ql][slots 16cc + 8hh .. +8] at
-    // vbase + 32db*VTSTR + 32cc.
-    const int vbase = ql * P::VTSTR + hh * 16;
+    // V^T (A operand of O^T, read transposed from the V rows, tr_operand): lane
+    // (h = lane / 32, g = (lane / 16) % 2, j = lane % 16) addresses row 4h + j / 4 at
+    // dims 16g + 4 (j % 4), plus 16cc rows and 32db dims.
+    const int tbase = (4 * hh + ((lane >> 2) & 3)) * P::VSTR + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
     // ---- caller mask: this lane's row of the head's mask slice; the words of tile t
     // sit in slot t % 2, loaded two tiles ahead of the S MFMAs that need them
@@ -229,16 +226,12 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
         load_mask(tile_of(1), 1);
     if (0 < ni_g) {
         stage_k(tile_of(0), P::K0);
-        load_v(tile_of(0), 0);
+        stage_v(tile_of(0), P::V0);
     }
     if (1 < ni_g) {
         stage_k(tile_of(1), P::K1);
-        load_v(tile_of(1), 1);  // written to LDS at the end of step 0
+        stage_v(tile_of(1), P::V1);
     }
-    if (0 < ni_g)
-        store_vt(P::V0, 0);
-    if (2 < ni_g)
-        load_v(tile_of(2), 0);  // written to LDS at the end of step 1
     // Q (B operand of S^T = K Q^T): lane supplies Q[my_q][16c + 8hh .. +8]
     vec qf[P::DC];
 #pragma unroll
@@ -402,18 +395,17 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
         }
     };
 
-    // O^T += V^T P^T from the V^T buffer at vb_off
+    // O^T += V^T P^T from the V buffer at vb_off
     auto pv = [&](const vec* pb, int vb_off) {
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
-            for (int db = 0; db < P::DB; ++db) {
-                const vec a = *reinterpret_cast<const vec*>(sm + vb_off + vbase + 32 * db * P::VTSTR + 32 * cc);
-                o[db] = M::mma(a, pb[cc], o[db]);
-            }
+            for (int db = 0; db < P::DB; ++db)
+                o[db] = M::mma(tr_operand<P::VSTR, vec>(sm + vb_off + tbase + 16 * cc * P::VSTR + 64 * db),
+                               pb[cc], o[db]);
     };
 
-    wg_barrier();  // waits for this wave's DMA (vmcnt), publishes K_0, K_1 and V_0
+    dma_barrier();  // publishes K_0, K_1, V_0 and V_1
     f32x16 sa[2], sb[2];
     float ma = 0.f, mb = 0.f;  // half-row maxima of the scores in sa / sb
     if (0 < ni_w) {
@@ -431,12 +423,11 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
     // as one branch-free block, the S MFMAs of the group's next tile (K buffer kn, into
     // s_nxt) and their max, together with the softmax and P.V MFMAs of tile t (V^T
     // buffer vc); a wave's last tile is masked if it needs it and has no next tile.
-    // Then the next tile's V (in registers since two steps ago) is written to the
-    // other V^T buffer vn, the barrier publishes it together with the K of local tile
-    // j + 2 (DMA issued one step ago), and the next loads go out: V of local tile
-    // j + 3 into the register slot just written, K of local tile j + 3 into kn.
+    // Then the barrier publishes the K of local tile j + 2 and the V of local tile
+    // j + 1 (DMA issued one step ago), and the next loads go out: V of local tile
+    // j + 2 into vc, K of local tile j + 3 into kn.
     auto step = [&](int j, f32x16* s_cur, f32x16* s_nxt, float& m_cur, float& m_nxt, int kn,
-                    int vc, int vn, auto SL) {
+                    int vc, auto SL) {
         constexpr int sl = decltype(SL)::value;  // mask-word slot of local tile j + 1
         if (j + 1 < ni_w) {
             update_max(m_cur);
@@ -457,20 +448,18 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
             exp_sum_pack(j, s_cur, pb);
             pv(pb, gbase + vc);
         }
-        if (j + 1 < ni_g)
-            store_vt(vn, sl);  // local tile j + 1 has the slot parity of sl
-        wg_barrier();
+        dma_barrier();
         if (MASK && j + 2 < ni_w)
             load_mask(tile_of(j + 2), sl ^ 1);  // local tile j + 2 has the parity of j
-        if (j + 3 < ni_g)
-            load_v(tile_of(j + 3), sl);  // into the slot just written
+        if (j + 2 < ni_g)
+            stage_v(tile_of(j + 2), vc);
         if (j + 3 < ni_g)
             stage_k(tile_of(j + 3), kn);
     };
     for (int j = 0; j < ni; j += 2) {
-        step(j, sa, sb, ma, mb, P::K1, P::V0, P::V1, std::integral_constant<int, 1>{});
+        step(j, sa, sb, ma, mb, P::K1, P::V0, std::integral_constant<int, 1>{});
         if (j + 1 < ni)
-            step(j + 1, sb, sa, mb, ma, P::K0, P::V1, P::V0, std::integral_constant<int, 0>{});
+            step(j + 1, sb, sa, mb, ma, P::K0, P::V1, std::integral_constant<int, 0>{});
     }
 
     // ---- key groups: the waves of groups 1 .. KG-1 hand their state to the group-0
