@@ -133,7 +133,6 @@ void fa_fwd_mfma16_kernel(const FwdParams<T> prm)
     const int qw = KG == 1 ? wave : wave % P::NQW;  // query wave: rows 32 qw .. of the tile
     const int grp = KG == 1 ? 0 : wave / P::NQW;    // key group: tiles grp, grp + KG, ...
     const int gbase = grp * P::GR;  // the group's K / V^T buffers
-    const int gtid = tid - grp * P::GT;  // thread index within the group
     const int lane = tid & 63;
     const int ql = lane & 31;  // query column of this lane in the accumulators
     const int hh = lane >> 5;  // wave half
