@@ -387,13 +387,14 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
                 uint32_t words[8];  // group 2cc + g: keys 16cc + 8g + 4hh + 0..3 of the tile
                 drop_words_q8(dp, bh, my_q, kbeg + u * P::BC + 4 * hh, words);
 #pragma unroll
-                for (int cc = 0; cc < 4; ++cc)
+                for (int cc = 0; cc < 4; ++cc) {
+                    u32x4 w = __builtin_bit_cast(u32x4, pb[cc]);  // values 2i, 2i + 1 in word i
+                    uint32_t pw[4] = {w[0], w[1], w[2], w[3]};
 #pragma unroll
                     for (int g = 0; g < 2; ++g)
-#pragma unroll
-                        for (int m = 0; m < 4; ++m)
-                            if (!drop_keep(words[2 * cc + g], m, dp.t))
-                                pb[cc][4 * g + m] = (T)0.f;
+                        drop_zero_pairs(words[2 * cc + g], pw + 2 * g, dp.t);
+                    pb[cc] = __builtin_bit_cast(vec, u32x4{pw[0], pw[1], pw[2], pw[3]});
+                }
             }
             if ((u & (kSumBlock - 1)) == kSumBlock - 1) {
                 l_done += ls0 + ls1;

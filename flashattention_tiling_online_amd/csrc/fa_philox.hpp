@@ -27,6 +27,13 @@ struct DropParams {
     float keep_scale;     // 256 / (256 - t)
 };
 
+// a ^ b ^ c in one instruction (gfx950's three-input bitwise op; 0x96 is the truth
+// table of the three-way exclusive or)
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c)
+{
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1)
 {
     constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
@@ -40,8 +47,8 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
         // both halves of each 32 x 32 -> 64-bit product from one multiply
         const uint64_t p0 = (uint64_t)M0 * c[0];
         const uint64_t p1 = (uint64_t)M1 * c[2];
-        c = u32x4{(uint32_t)(p1 >> 32) ^ c[1] ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c[3] ^ k1,
-                  (uint32_t)p0};
+        c = u32x4{xor3((uint32_t)(p1 >> 32), c[1], k0), (uint32_t)p1,
+                  xor3((uint32_t)(p0 >> 32), c[3], k1), (uint32_t)p0};
     }
     return c;
 }
@@ -151,6 +158,25 @@ __device__ __forceinline__ void drop_words_k4(const DropParams& dp, int bh, int 
 __device__ __forceinline__ bool drop_keep(uint32_t bytes, int m, uint32_t t)
 {
     return ((bytes >> (8 * m)) & 0xFFu) >= t;
+}
+
+// Dropout on four 16-bit values packed in two words (pairs[0] holds values 0, 1 in its
+// low and high halves, pairs[1] values 2, 3), value m decided by byte m of `bytes`:
+// zeroed iff the byte is below t (0 <= t <= 256).  Works on the packed words: each
+// byte pair is spread into two 16-bit lanes, byte - t is negative exactly for the
+// dropped values, and its sign, replicated over the lane, clears them.
+__device__ __forceinline__ void drop_zero_pairs(uint32_t bytes, uint32_t* pairs, uint32_t t)
+{
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    const s16x2 tt = {(short)t, (short)t};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        // bytes 2h, 2h + 1 into the low bytes of the two 16-bit lanes (selector 0x0C: zero)
+        const uint32_t x = __builtin_amdgcn_perm(0u, bytes, h ? 0x0C030C02u : 0x0C010C00u);
+        const s16x2 d = __builtin_bit_cast(s16x2, x) - tt;
+        const s16x2 drop = d >> (short)15;  // 0xFFFF where the byte is below t
+        pairs[h] &= ~__builtin_bit_cast(uint32_t, drop);
+    }
 }
 
 }  // namespace fa
