@@ -48,23 +48,30 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-# the sources the forward kernels are built from (the profiles in profiles/ that
-# bench.py reads belong to the forward kernel)
-FWD_SOURCES = ("fa_common.hpp", "fa_tiles.hpp", "fa_fwd_mfma16.hpp", "fa_fwd_pp.hpp",
-               "fa_fwd_f32.hpp")
+# the sources each forward kernel family is built from (the HBM-traffic summaries in
+# profiles/ that bench.py reads are tied to the family that runs the workload)
+KERNEL_SOURCES = {
+    "pp": ("fa_common.hpp", "fa_tiles.hpp", "fa_philox.hpp", "fa_fwd_pp.hpp"),        # d = 128
+    "mfma16": ("fa_common.hpp", "fa_tiles.hpp", "fa_philox.hpp", "fa_fwd_mfma16.hpp"),  # d = 64
+    "f32": ("fa_common.hpp", "fa_fwd_f32.hpp"),                                         # fp32
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_family(w) -> str:
+    return "f32" if w.dtype == "f32" else ("pp" if w.d == 128 else "mfma16")
+
+
+def kernel_source_hash(family: str) -> str:
     h = hashlib.sha256()
-    for f in FWD_SOURCES:
+    for f in KERNEL_SOURCES[family]:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
-def committed_traffic(workload: str):
+def committed_traffic(w):
     """HBM bytes per launch from profiles/hbm_traffic_<workload>.txt, if still current."""
-    path = os.path.join(PROFILES, f"hbm_traffic_{workload}.txt")
+    path = os.path.join(PROFILES, f"hbm_traffic_{w.name}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -72,7 +79,7 @@ def committed_traffic(workload: str):
         if "=" in line and not line.lstrip().startswith("#"):
             a, b = line.split("=", 1)
             kv[a.strip()] = b.strip()
-    if kv.get("kernel_sources_sha256_16") != kernel_source_hash():
+    if kv.get("kernel_sources_sha256_16") != kernel_source_hash(kernel_family(w)):
         log(f"[bench] {path} was taken on other kernel sources: traffic reported as null")
         return None
     try:
@@ -329,7 +336,7 @@ def main() -> int:
 
     peak = PEAK_TFLOPS[w.dtype]
     traffic = (None if (args.bwd or splits is not None or p_drop is not None)
-               else committed_traffic(w.name))
+               else committed_traffic(w))
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic}
     if not args.no_clocks:
@@ -378,7 +385,7 @@ def main() -> int:
                              f"N(0,{w.sigma_v:g}^2) V, seeded"},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "fwd_kernel_sources_sha256_16": kernel_source_hash(),
+        "fwd_kernel_sources_sha256_16": kernel_source_hash(kernel_family(w)),
     }
     print(json.dumps(line), flush=True)
     return 0
