@@ -54,6 +54,8 @@ KERNEL_SOURCES = {
     "pp": ("fa_common.hpp", "fa_tiles.hpp", "fa_philox.hpp", "fa_fwd_pp.hpp"),        # d = 128
     "mfma16": ("fa_common.hpp", "fa_tiles.hpp", "fa_philox.hpp", "fa_fwd_mfma16.hpp"),  # d = 64
     "f32": ("fa_common.hpp", "fa_fwd_f32.hpp"),                                         # fp32
+    "bwd": ("fa_common.hpp", "fa_tiles.hpp", "fa_philox.hpp", "fa_bwd.hpp"),            # backward
+    "merge": ("fa_common.hpp", "fa_merge.hpp"),                                         # key-split merge
 }
 
 
