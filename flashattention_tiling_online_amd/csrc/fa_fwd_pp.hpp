@@ -21,9 +21,13 @@
 // both waves contending for the same slots in the same phase:
 //     phase 2j:    group 0 MFMA(j),     group 1 softmax(j)
 //     phase 2j+1:  group 0 softmax(j+1), group 1 MFMA(j)
-// Query rows are assigned so that the two waves of a SIMD own adjacent 32-row
-// blocks (wave w: rows 32 (2 (w % 4) + w / 4) of the tile), which keeps their
-// causal tile counts within one of each other.
+// Query rows: the two waves of SIMD s own the tile's 32-row blocks s (wave s, group 0)
+// and 7 - s (wave s + 4, group 1).  Under a causal mask block b's last row sees key
+// tile q0 / 64 + b / 2 (b / 2 rounded down) last, so the blocks' tile counts run from
+// nkt - 3 (blocks 0, 1) to nkt (blocks 6, 7); pairing the short and long blocks leaves one
+// active wave per SIMD in the workgroup's last two tile steps, whose phases then run
+// without the other wave's interference, instead of leaving whole SIMDs idle while the
+// SIMD that holds blocks 6 and 7 runs both at the full phase length.
 //
 // Staging, K and V both by DMA (buffer_load ... lds), three buffers each.  K rows
 // are padded to 272 bytes (as in fa_fwd_mfma16.hpp): the 16 rows of one
@@ -123,7 +127,7 @@ void fa_fwd_pp_kernel(const FwdParams<T> prm)
     const int lane = tid & 63;
     const int ql = lane & 31;
     const int hh = lane >> 5;
-    const int qw0 = q0 + 32 * (2 * (wave & 3) + grp);
+    const int qw0 = q0 + 32 * (grp == 0 ? (wave & 3) : 7 - (wave & 3));
     const int my_q = qw0 + ql;
 
     // ---- key range: keys [kbeg, kbeg + Nks) of the head (all of them unless split);
