@@ -95,30 +95,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const T* base, int r
 }
 
 // DMA one K or V tile (rows [tile*BC, tile*BC + BC) of a head) into the LDS tile at
-// `dst`: this wave's blocks wave, wave+NW, ... (< NB); src[i] is the lane's source
+// `dst`: the blocks slot, slot+NW, ... (< NB) of the wave whose place in the dealing
+// order is `slot` (the wave index, or a rotation of it); src[i] is the lane's source
 // offset for its i-th block (kDmaSkip: padding).  A device function (not a lambda)
 // so that the host pass never sees the builtin.
 //
-// The LDS address of a block (M0 of the DMA) is the tile's offset plus the wave's
-// block offset, formed here by a scalar add.  The wave's offset passes through an
+// The LDS address of a block (M0 of the DMA) is the tile's offset plus the slot's
+// block offset, formed here by a scalar add.  The slot's offset passes through an
 // empty asm statement first: in an unrolled loop over several buffers the compiler
 // would otherwise keep every (buffer, block) address live across the loop, run out
 // of SGPRs and park them in VGPR lanes, so that each DMA costs a v_readlane (VALU
 // issue time in the softmax phase) instead of an s_add.
 template <int D, int NB, int PW, int NW, typename T>
 __device__ __forceinline__ void stage_tile(const T* head, int tile, int nrows, char* dst,
-                                           int wave, const int* src)
+                                           int slot, const int* src)
 {
     const __amdgpu_buffer_rsrc_t r = rows_rsrc<D>(head, tile * 64, nrows);
-    uint32_t wave_off = (uint32_t)__builtin_amdgcn_readfirstlane(wave * 1024);
-    __asm__ volatile("" : "+s"(wave_off));
+    uint32_t slot_off = (uint32_t)__builtin_amdgcn_readfirstlane(slot * 1024);
+    __asm__ volatile("" : "+s"(slot_off));
     const uint32_t tile_lds = (uint32_t)(uintptr_t)(lds_char*)dst;
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
-        const int blk = wave + NW * i;
+        const int blk = slot + NW * i;
         if (blk < NB)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (lds_void*)(uintptr_t)(tile_lds + wave_off + NW * 1024 * i), 16, src[i], 0, 0, 0);
+                r, (lds_void*)(uintptr_t)(tile_lds + slot_off + NW * 1024 * i), 16, src[i], 0, 0, 0);
     }
 }
 
