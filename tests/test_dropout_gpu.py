@@ -109,11 +109,16 @@ def test_dropout_fwd_workloads_sampled(name):
     compare_fwd(w, p, to_host(o, w.dtype), lse.cpu().numpy(), sel_bh, sel_row, o64, l64)
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("seed,p", [(1, 0.25), (0xFFFFFFFF00000001, 0.5), (987654321, 0.04)])
-def test_dropout_keep_mask_is_bit_exact(seed, p, causal):
-    """Q = 0 and V = I: O[q, k] > 0 exactly where the oracle keeps (q, k) (and k <= q)."""
-    B, H, Nq, Nk, d = 2, 3, 300, 128, 128
+@pytest.mark.parametrize("seed,p", [(1, 0.25), (0xFFFFFFFF00000001, 0.5), (987654321, 0.04),
+                                    (77, 1 / 256), (78, 255 / 256)])
+def test_dropout_keep_mask_is_bit_exact(seed, p, causal, d):
+    """Q = 0 and V = I: O[q, k] > 0 exactly where the oracle keeps (q, k) (and k <= q).
+    Thresholds t = 1 and t = 255 are the extremes the kernels' packed keep test (byte - t
+    per 16-bit lane, dropped where negative) must get right; d = 64 runs the other
+    forward kernel."""
+    B, H, Nq, Nk = 2, 3, 300, d
     q = torch.zeros((B, H, Nq, d), dtype=torch.bfloat16, device=DEV)
     eye = torch.eye(Nk, d, dtype=torch.bfloat16, device=DEV)
     v = eye.expand(B, H, Nk, d).contiguous()
