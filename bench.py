@@ -195,8 +195,13 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         flops += float((4.0 * w.d * vis).sum())
         done = sel.stop
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "seconds": round(dt, 2), "threads_used": cores, "os_cpu_count": os.cpu_count(),
+    rate = flops / dt
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(dt, 2),
+            # the whole workload at the sample's rate: an extrapolation, flop-scaled
+            "extrapolated_full_workload_seconds": round(w.flops / rate, 1),
+            "sample_fraction_of_flops": round(flops / w.flops, 4),
+            "threads_used": cores, "os_cpu_count": os.cpu_count(),
             "affinity_cores": (len(os.sched_getaffinity(0))
                                if hasattr(os, "sched_getaffinity") else None),
             "sample": (f"{done} of the {bh.size} rows of {w.name} (all heads), taken in a "
