@@ -82,6 +82,9 @@ WORKLOADS = {
     # unsplit kernel under-fills (32 workgroups), measured with the key-split path
     "short_q_long_kv": Workload("short_q_long_kv", 4, 8, 256, 16384, 128, "bf16", False,
                                 seed=606),
+    # the forward shape the article on hncyxsy.com times in its section 6.4 (B=8, H=16,
+    # N=4096, d=64, non-causal): a large d = 64 grid, measured as context
+    "pages_d64": Workload("pages_d64", 8, 16, 4096, 4096, 64, "bf16", False, seed=707),
 }
 
 # seed of the row sample drawn for the largest workloads

@@ -78,7 +78,7 @@ def test_workload_all_rows(name):
 
 
 @pytest.mark.parametrize("name", ["self_8k_causal", "cross_1k_8k", "ctx_32k_causal",
-                                  "short_q_long_kv"])
+                                  "short_q_long_kv", "pages_d64"])
 def test_workload_sampled_rows(name):
     w = inputs.WORKLOADS[name]
     _, _, v, o, lse = check_workload(w, n_heads=4, n_rows=256)
