@@ -60,8 +60,10 @@
 // partial states, as fa_fwd_mfma16.hpp does; with dropout the softmax phase zeroes
 // the dropped entries of the rounded P (the Philox words of fa_philox.hpp); with a
 // caller mask (the blog page "Flash Attention", Algorithm 2: S_masked = mask(S)) the
-// softmax phase sets the hidden scores to -inf from the mask words, loaded one tile
-// ahead, and a row that sees no key ends with O = 0 and L = -inf.
+// hidden scores are set to -inf from the mask words, loaded one tile ahead, just
+// before the running max is taken (at the end of the MFMA phase before the tile's
+// softmax phase; for tile 0 at the start of the first softmax phase), and a row that
+// sees no key ends with O = 0 and L = -inf.
 #pragma once
 
 #include <type_traits>
