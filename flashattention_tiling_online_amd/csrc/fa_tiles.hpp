@@ -176,43 +176,4 @@ __device__ __forceinline__ V tr_operand(const char* p)
     return __builtin_bit_cast(V, w);
 }
 
-// V staging of one thread: the 4-key x 4-dim block (keys 4kg..4kg+3, dims
-// 4dq..4dq+3) of 64-key tile `tile`, loaded as four 8-byte rows (rows past nrows
-// read 0).
-template <int D, typename T>
-__device__ __forceinline__ void load_v_block(const T* head, int tile, int nrows, int kg, int dq,
-                                             u32x2* r)
-{
-    const __amdgpu_buffer_rsrc_t rs = rows_rsrc<D>(head, tile * 64, nrows);
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-        r[m] = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, ((4 * kg + m) * D + 4 * dq) * 2, 0, 0));
-}
-
-// Transpose the block and write it as four V^T row segments (dim 4dq+e, 4 keys each)
-// at LDS byte `dst` + (4dq+e)*VTSTR + 2*slot, where the keys of 16-key chunk cc are
-// stored in the order the P registers hold them: slots 16cc + 8h + 0..3 hold keys
-// 16cc + 4h + 0..3 and slots 16cc + 8h + 4..7 hold keys 16cc + 8 + 4h + 0..3.
-template <int VTSTR>
-__device__ __forceinline__ void store_vt_block(char* dst, int kg, int dq, const u32x2* r)
-{
-    const int cc = kg >> 2, x = kg & 3;
-    const int slot = 16 * cc + 4 * (((x & 1) << 1) | (x >> 1));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const uint32_t a0 = (e < 2) ? r[0].x : r[0].y, a1 = (e < 2) ? r[1].x : r[1].y;
-        const uint32_t a2 = (e < 2) ? r[2].x : r[2].y, a3 = (e < 2) ? r[3].x : r[3].y;
-        u32x2 w;
-        if (e & 1) {
-            w.x = (a0 >> 16) | (a1 & 0xffff0000u);
-            w.y = (a2 >> 16) | (a3 & 0xffff0000u);
-        } else {
-            w.x = (a0 & 0xffffu) | (a1 << 16);
-            w.y = (a2 & 0xffffu) | (a3 << 16);
-        }
-        *reinterpret_cast<u32x2*>(dst + (4 * dq + e) * VTSTR + 2 * slot) = w;
-    }
-}
-
 }  // namespace fa
